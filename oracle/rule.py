@@ -1,0 +1,56 @@
+"""Rule score, IntentKV Sec. 3.2 Eqs. (3)-(4) (test infrastructure only).
+
+For every layer l and query head h, a softmax over the candidate positions H
+of M_t[l,h] . K[l,g(h),j] / sqrt(D) (Eq. 4), summed over all (l, h) into
+rule_j (Eq. 3).  The candidate set is H = [0, N) minus the forced set
+F = [0, pi) U [q_s, q_e) of Sec. 3.1.
+
+Readings: GQA expands KV head g to the G = H_q / H_kv consecutive query heads
+g*G .. g*G+G-1, i.e. g(h) = h // G; forced positions get score 0 (selection
+never looks at them).
+"""
+
+import math
+
+import numpy as np
+
+from .bf16 import as_f64
+
+
+def forced_mask(N, pi, q_s, q_e):
+    """Boolean [N]: the forced set F = [0, pi) U [q_s, q_e), clipped to [0, N)."""
+    F = np.zeros(N, dtype=bool)
+    F[: max(0, min(pi, N))] = True
+    lo, hi = max(0, q_s), min(N, q_e)
+    if hi > lo:
+        F[lo:hi] = True
+    return F
+
+
+def rule_score(K, M, pi, q_s, q_e):
+    """rule_j for j in [0, N); 0 on the forced set.
+
+    K: [L, H_kv, N, D] post-RoPE keys (float or bf16 bits).
+    M: [L, H_q, D] QueryMemory.
+    """
+    K = np.asarray(K)
+    M = np.asarray(M, dtype=np.float64)
+    L, H_kv, N, D = K.shape
+    H_q = M.shape[1]
+    if M.shape != (L, H_q, D) or H_q % H_kv != 0:
+        raise ValueError("shape mismatch between K and M")
+    G = H_q // H_kv
+    cand = ~forced_mask(N, pi, q_s, q_e)
+    rule = np.zeros(N, dtype=np.float64)
+    if not cand.any():
+        return rule
+    scale = 1.0 / math.sqrt(D)
+    for l in range(L):
+        for g in range(H_kv):
+            Kc = as_f64(K[l, g])[cand]               # [|H|, D]
+            for h in range(g * G, (g + 1) * G):
+                s = (Kc @ M[l, h]) * scale            # Eq. (4) logits over H
+                a = np.exp(s - s.max())
+                a /= a.sum()
+                rule[cand] += a                        # Eq. (3)
+    return rule
