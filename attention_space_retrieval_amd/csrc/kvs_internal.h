@@ -1,0 +1,83 @@
+// Internal declarations shared by the HIP kernels and the C-ABI host layer.
+// gfx950 (CDNA4) only: 64-lane wavefronts, bf16 MFMA, 160 KB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvs {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// bf16 is the top half of a binary32: widening is a shift.
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Merge two (max, sum-of-exp2(x - max)) pairs.  Empty pairs are (-inf, 0).
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  s = s * exp2f(m - mn) + s2 * exp2f(m2 - mn);
+  m = mn;
+}
+
+inline unsigned ceil_div(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
+
+}  // namespace kvs
+
+// Launchers (host side).  Each returns the launch status; arguments are
+// already validated by the C-ABI layer.
+hipError_t kvs_launch_qmem(const void* q, int dtype, int L, int H_q, int S, int D, float decay,
+                           int first_turn, float* M, hipStream_t st);
+
+hipError_t kvs_launch_rule(const void* K, int dtype, const float* M, int L, int H_q, int H_kv,
+                           int D, int64_t N, int64_t pi, int64_t q_s, int64_t q_e, float* rule,
+                           void* ws, hipStream_t st);
+size_t kvs_rule_ws_bytes(int L, int H_q, int64_t N);
+
+hipError_t kvs_launch_topk(const float* score, int64_t n, int64_t f0b, int64_t f0e, int64_t f1b,
+                           int64_t f1e, int64_t n_forced, int64_t c_star, uint8_t* keep_mask,
+                           int32_t* keep_idx, int64_t* n_kept, void* ws, hipStream_t st);
+size_t kvs_topk_ws_bytes(int64_t n);
+
+hipError_t kvs_launch_slotmap(const int64_t* in, const uint8_t* mask, int64_t N, int64_t dead,
+                              int64_t* out, hipStream_t st);
+
+hipError_t kvs_launch_meank_build(const void* K, int L, int H_kv, int D, int64_t N, int k_is_rope,
+                                  int64_t pos0, double theta, void* raw_out, void* index,
+                                  hipStream_t st);
+
+hipError_t kvs_launch_meank_score(const void* Q, const void* index, int L, int H_q, int H_kv,
+                                  int64_t Mq, int64_t nB, int64_t c0, int64_t c1, float* R,
+                                  void* ws, hipStream_t st);
+size_t kvs_meank_ws_bytes(int L, int H_q, int H_kv, int64_t Mq, int64_t nB);
+
+hipError_t kvs_launch_rerope(const void* k_src, const void* v_src, int64_t src_tokens,
+                             const int32_t* src_block, const int32_t* page_table, int64_t n_sel,
+                             int L, int H_kv, int D, int64_t pos_base, double theta, void* k_pool,
+                             void* v_pool, int64_t pool_pages, int32_t* err_flag, hipStream_t st);

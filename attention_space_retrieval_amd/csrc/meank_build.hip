@@ -1,0 +1,140 @@
+// Mean-K index build (KVMEM, section "Design and trade-offs: step-level
+// attention trigger and Mean-K model-native retrieval"): one mean of
+// position-free K per 32-token block, per layer and KV head.
+//
+// HBM-bound stream of K (read once) plus a 1/32-size write.  A wavefront
+// reduces one block at a time: D/8 lanes cover a 2*D-byte row with 16-byte
+// loads, so one load instruction covers 64/(D/8) rows and 32 rows take 8
+// (D=128) coalesced loads.  Sums are float32 in a fixed order (per lane over
+// its rows, then a butterfly over the row groups), the mean is rounded to bf16
+// nearest-even.
+//
+// De-RoPE mode: the keys carry RoPE at positions pos0 + i.  A workgroup owns
+// one token block for every (layer, KV head); it builds that block's 32 x D/2
+// rotation table once in LDS (float64 angles) and reuses it for all L*H_kv
+// heads, optionally writing the RoPE-free keys back out.
+#include "rope_table.h"
+
+using namespace kvs;
+
+namespace {
+
+constexpr int kBlk = 32;
+constexpr int kBlocksPerWave = 8;
+
+template <int D>
+__global__ __launch_bounds__(256) void meank_build_raw(const uint16_t* __restrict__ K, int64_t N,
+                                                       int64_t nB, int64_t total_blocks,
+                                                       uint16_t* __restrict__ index) {
+  constexpr int LPR = D / 8, RPL = 64 / LPR, LOADS = kBlk / RPL;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int cl = lane % LPR, rr = lane / LPR;
+  const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
+  for (int it = 0; it < kBlocksPerWave; ++it) {
+    const int64_t gb = gw * kBlocksPerWave + it;
+    if (gb >= total_blocks) return;
+    const int64_t lg = gb / nB, b = gb - lg * nB;
+    const int64_t t0 = b * kBlk;
+    const int nb = (int)min<int64_t>(kBlk, N - t0);
+    const uint16_t* src = K + ((size_t)lg * N + t0) * D + cl * 8;
+    u32x4 w[LOADS];
+#pragma unroll
+    for (int ld = 0; ld < LOADS; ++ld) {
+      const int t = ld * RPL + rr;
+      w[ld] = t < nb ? *reinterpret_cast<const u32x4*>(src + (size_t)t * D) : u32x4{0u, 0u, 0u, 0u};
+    }
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ld = 0; ld < LOADS; ++ld) {
+      float x[8];
+      unpack8(w[ld], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += x[e];
+    }
+#pragma unroll
+    for (int o = LPR; o < 64; o <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o, kWave);
+    if (rr == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = nb == kBlk ? acc[e] * (1.f / kBlk) : acc[e] / (float)nb;
+      *reinterpret_cast<u32x4*>(index + (size_t)gb * D + cl * 8) = pack8(acc);
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void meank_build_derope(const uint16_t* __restrict__ K, int64_t N,
+                                                          int64_t nB, int LG, int64_t pos0,
+                                                          double log2_theta,
+                                                          uint16_t* __restrict__ raw_out,
+                                                          uint16_t* __restrict__ index) {
+  constexpr int LPR = D / 8, RPL = 64 / LPR, LOADS = kBlk / RPL;
+  __shared__ float2 tab[kBlk][D / 2];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int cl = lane % LPR, rr = lane / LPR;
+  const int64_t b = blockIdx.x;
+  const int64_t t0 = b * kBlk;
+  const int nb = (int)min<int64_t>(kBlk, N - t0);
+  build_rope_table<D>(tab, pos0 + t0, log2_theta);
+  __syncthreads();
+  for (int lg = wave; lg < LG; lg += 4) {
+    const size_t row0 = (size_t)lg * N + t0;
+    const uint16_t* src = K + row0 * D + cl * 8;
+    u32x4 w[LOADS];
+#pragma unroll
+    for (int ld = 0; ld < LOADS; ++ld) {
+      const int t = ld * RPL + rr;
+      w[ld] = t < nb ? *reinterpret_cast<const u32x4*>(src + (size_t)t * D) : u32x4{0u, 0u, 0u, 0u};
+    }
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ld = 0; ld < LOADS; ++ld) {
+      const int t = ld * RPL + rr;
+      float x[8];
+      unpack8(w[ld], x);
+      rotate8<D>(x, tab[t < nb ? t : 0], cl, -1);
+      if (t < nb) {
+        if (raw_out) *reinterpret_cast<u32x4*>(raw_out + (row0 + t) * D + cl * 8) = pack8(x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += x[e];
+      }
+    }
+#pragma unroll
+    for (int o = LPR; o < 64; o <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o, kWave);
+    if (rr == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = nb == kBlk ? acc[e] * (1.f / kBlk) : acc[e] / (float)nb;
+      *reinterpret_cast<u32x4*>(index + ((size_t)lg * nB + b) * D + cl * 8) = pack8(acc);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t kvs_launch_meank_build(const void* K, int L, int H_kv, int D, int64_t N, int k_is_rope,
+                                  int64_t pos0, double theta, void* raw_out, void* index,
+                                  hipStream_t st) {
+  if (N == 0) return hipSuccess;
+  const int64_t nB = (N + kBlk - 1) / kBlk;
+  const int LG = L * H_kv;
+  const uint16_t* Kb = static_cast<const uint16_t*>(K);
+  uint16_t* idx = static_cast<uint16_t*>(index);
+  if (!k_is_rope) {
+    const int64_t total = (int64_t)LG * nB;
+    dim3 grid(ceil_div(total, 4 * kBlocksPerWave)), block(256);
+    if (D == 128) hipLaunchKernelGGL(meank_build_raw<128>, grid, block, 0, st, Kb, N, nB, total, idx);
+    else hipLaunchKernelGGL(meank_build_raw<64>, grid, block, 0, st, Kb, N, nB, total, idx);
+  } else {
+    const double l2t = __builtin_log2(theta);
+    uint16_t* raw = static_cast<uint16_t*>(raw_out);
+    dim3 grid((unsigned)nB), block(256);
+    if (D == 128)
+      hipLaunchKernelGGL(meank_build_derope<128>, grid, block, 0, st, Kb, N, nB, LG, pos0, l2t, raw, idx);
+    else
+      hipLaunchKernelGGL(meank_build_derope<64>, grid, block, 0, st, Kb, N, nB, LG, pos0, l2t, raw, idx);
+  }
+  return hipGetLastError();
+}

@@ -1,0 +1,288 @@
+// Rule score (IntentKV, Sec. 3.2, Eqs. 3-4): for each layer l and query head
+// h, a softmax over the candidate positions H = [0,N) \ F of
+// M[l,h] . K[l,h/G,j] / sqrt(D); rule_j sums the softmaxes over (l, h).
+//
+// HBM-bound: K is streamed once.  Because every (l, h) softmax has its own
+// normaliser, the logits are spilled (fp32, [L*H_q, N]) and summed after the
+// normalisers are known:
+//   1. rule_logits_*: one workgroup per (chunk of 2048 positions, l, g).  Per
+//      16-row tile of K the bf16 MFMA 16x16x32 computes the G logits of every
+//      row; the A operand holds M * log2(e)/sqrt(D) split into a bf16 high part
+//      (rows 0..7) and a bf16 low part (rows 8..15), so hi+lo gives the logit
+//      to ~2^-16 relative at no extra MFMA cost.  Logits are written in log2
+//      units and a per-chunk (max, sum 2^(x-max)) is kept per head.
+//   2. rule_lse_merge: per (l, h), merge the chunk partials in order -> lse2.
+//   3. rule_colsum: rule_j = sum_{l,h} 2^(x[l,h,j] - lse2[l,h]), fixed order.
+// Forced positions carry -inf logits, so they drop out of every softmax and
+// their rule value is exactly 0.
+#include "kvs_internal.h"
+
+using namespace kvs;
+
+namespace {
+
+constexpr int kChunk = 2048;   // positions per workgroup in the logit pass
+constexpr int kColTile = 64;   // positions per workgroup in the column sum
+
+__device__ __forceinline__ __bf16 bf16_from_bits(uint32_t b) {
+  return __builtin_bit_cast(__bf16, (uint16_t)b);
+}
+
+__device__ __forceinline__ bool is_forced(int64_t j, int64_t pi, int64_t q_s, int64_t q_e) {
+  return j < pi || (j >= q_s && j < q_e);
+}
+
+__device__ __forceinline__ void online_add(float& m, float& s, float x) {
+  const float mn = fmaxf(m, x);
+  s = s * __builtin_amdgcn_exp2f(m - mn) + __builtin_amdgcn_exp2f(x - mn);
+  m = mn;
+}
+
+// NHG = number of 8-head groups (G <= 8*NHG).
+template <int D, int NHG>
+__global__ __launch_bounds__(256) void rule_logits_mfma(
+    const uint16_t* __restrict__ K, const float* __restrict__ M, int H_q, int H_kv, int G,
+    int64_t N, int64_t pi, int64_t q_s, int64_t q_e, float scale_log2, float* __restrict__ spill,
+    float2* __restrict__ partials, int n_chunks) {
+  constexpr int KS = D / 32;            // MFMA k-steps per row
+  constexpr int QW = D / 4;             // dims owned by one 16-lane group
+  const int chunk = blockIdx.x;
+  const int lg = blockIdx.y;
+  const int l = lg / H_kv, g = lg - l * H_kv;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, q = lane >> 4;
+
+  // A operand: row r of the 16x32 tile is head slot r&7 of group hg, high part
+  // for r < 8 and low part for r >= 8; k-slot 8q+e of k-step s is dim q*QW + 8s + e.
+  bf16x8 A[NHG][KS];
+#pragma unroll
+  for (int hg = 0; hg < NHG; ++hg) {
+    const int hl = hg * 8 + (r & 7);
+    const float* mrow = M + ((size_t)l * H_q + (size_t)g * G + hl) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint32_t bits = 0;
+        if (hl < G) {
+          const float x = mrow[q * QW + 8 * s + e] * scale_log2;
+          const uint32_t hb = f32_to_bf16_bits(x);
+          bits = r < 8 ? hb : f32_to_bf16_bits(x - __uint_as_float(hb << 16));
+        }
+        A[hg][s][e] = bf16_from_bits(bits);
+      }
+    }
+  }
+
+  float mx[NHG][4], sm[NHG][4];
+#pragma unroll
+  for (int hg = 0; hg < NHG; ++hg)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) { mx[hg][v] = -INFINITY; sm[hg][v] = 0.f; }
+
+  const int64_t row0 = (int64_t)chunk * kChunk;
+  const int64_t row1 = min(N, row0 + (int64_t)kChunk);
+  const uint16_t* Kb = K + (size_t)lg * (size_t)N * D;
+  const size_t head0 = (size_t)l * H_q + (size_t)g * G;
+
+  auto load_tile = [&](int64_t t0, bf16x8* B) {
+    const int64_t j = t0 + r;
+    const bool ok = j < row1;
+    const u32x4* p = reinterpret_cast<const u32x4*>(Kb + (size_t)(ok ? j : row0) * D + q * QW);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      u32x4 w = ok ? p[s] : u32x4{0u, 0u, 0u, 0u};
+      B[s] = __builtin_bit_cast(bf16x8, w);
+    }
+  };
+
+  bf16x8 B[KS], Bn[KS];
+  int64_t t0 = row0 + wave * 16;
+  if (t0 < row1) load_tile(t0, B);
+  for (; t0 < row1; t0 += 64) {
+    const int64_t tn = t0 + 64;
+    if (tn < row1) load_tile(tn, Bn);
+    const int64_t j = t0 + r;
+    const bool vj = j < row1;
+    const bool forced = is_forced(j, pi, q_s, q_e);
+#pragma unroll
+    for (int hg = 0; hg < NHG; ++hg) {
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[hg][s], B[s], c, 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        // C row 4*(lane>>4)+v: lanes 0..31 hold the high rows, lanes 32..63 the low rows.
+        const float t = c[v] + __shfl_xor(c[v], 32, kWave);
+        const int hl = hg * 8 + 4 * (q & 1) + v;
+        if (lane < 32 && vj && hl < G) {
+          spill[(head0 + hl) * (size_t)N + j] = forced ? -INFINITY : t;
+          if (!forced) online_add(mx[hg][v], sm[hg][v], t);
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) B[s] = Bn[s];
+  }
+
+  // Reduce over the 16 lanes that hold the same head, then over the 4 waves.
+  __shared__ float2 red[4][NHG * 8];
+#pragma unroll
+  for (int hg = 0; hg < NHG; ++hg)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const float m2 = __shfl_xor(mx[hg][v], o, kWave);
+        const float s2 = __shfl_xor(sm[hg][v], o, kWave);
+        lse_merge(mx[hg][v], sm[hg][v], m2, s2);
+      }
+      if (lane == 0 || lane == 16) red[wave][hg * 8 + 4 * (lane >> 4) + v] = make_float2(mx[hg][v], sm[hg][v]);
+    }
+  __syncthreads();
+  if (threadIdx.x < NHG * 8 && (int)threadIdx.x < G) {
+    const int hl = threadIdx.x;
+    float m = -INFINITY, s = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) lse_merge(m, s, red[w][hl].x, red[w][hl].y);
+    partials[(head0 + hl) * n_chunks + chunk] = make_float2(m, s);
+  }
+}
+
+// fp32 keys: plain VALU dot products, one row per thread, same outputs.
+template <int D>
+__global__ __launch_bounds__(256) void rule_logits_f32(
+    const float* __restrict__ K, const float* __restrict__ M, int H_q, int H_kv, int G, int64_t N,
+    int64_t pi, int64_t q_s, int64_t q_e, float scale_log2, float* __restrict__ spill,
+    float2* __restrict__ partials, int n_chunks) {
+  constexpr int GMAX = 16;
+  __shared__ float Ms[GMAX][D];
+  __shared__ float2 red[4][GMAX];
+  const int chunk = blockIdx.x;
+  const int lg = blockIdx.y;
+  const int l = lg / H_kv, g = lg - l * H_kv;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const size_t head0 = (size_t)l * H_q + (size_t)g * G;
+  for (int i = threadIdx.x; i < G * D; i += 256) Ms[i / D][i % D] = M[head0 * D + i];
+  __syncthreads();
+  float mx[GMAX], sm[GMAX];
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h) { mx[h] = -INFINITY; sm[h] = 0.f; }
+  const int64_t row0 = (int64_t)chunk * kChunk;
+  const int64_t row1 = min(N, row0 + (int64_t)kChunk);
+  const float* Kb = K + (size_t)lg * (size_t)N * D;
+  for (int64_t j = row0 + threadIdx.x; j < row1; j += 256) {
+    const float* krow = Kb + (size_t)j * D;
+    const bool forced = is_forced(j, pi, q_s, q_e);
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h) {
+      if (h < G) {
+        float dot = 0.f;
+        for (int d = 0; d < D; ++d) dot = fmaf(Ms[h][d], krow[d], dot);
+        const float t = dot * scale_log2;
+        spill[(head0 + h) * (size_t)N + j] = forced ? -INFINITY : t;
+        if (!forced) online_add(mx[h], sm[h], t);
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h) {
+    if (h < G) {
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float m2 = __shfl_xor(mx[h], o, kWave);
+        const float s2 = __shfl_xor(sm[h], o, kWave);
+        lse_merge(mx[h], sm[h], m2, s2);
+      }
+      if (lane == 0) red[wave][h] = make_float2(mx[h], sm[h]);
+    }
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < G) {
+    float m = -INFINITY, s = 0.f;
+    for (int w = 0; w < 4; ++w) lse_merge(m, s, red[w][threadIdx.x].x, red[w][threadIdx.x].y);
+    partials[(head0 + threadIdx.x) * n_chunks + chunk] = make_float2(m, s);
+  }
+}
+
+__global__ __launch_bounds__(256) void rule_lse_merge(const float2* __restrict__ partials, int LH,
+                                                      int n_chunks, float* __restrict__ lse2) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= LH) return;
+  float m = -INFINITY, s = 0.f;
+  for (int c = 0; c < n_chunks; ++c) {
+    const float2 p = partials[(size_t)i * n_chunks + c];
+    lse_merge(m, s, p.x, p.y);
+  }
+  lse2[i] = s > 0.f ? m + log2f(s) : INFINITY;
+}
+
+__global__ __launch_bounds__(256) void rule_colsum(const float* __restrict__ spill,
+                                                   const float* __restrict__ lse2, int LH, int64_t N,
+                                                   float* __restrict__ rule) {
+  __shared__ float part[4][kColTile];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t j = (int64_t)blockIdx.x * kColTile + lane;
+  float acc = 0.f;
+  if (j < N) {
+    const float* col = spill + j;
+#pragma unroll 8
+    for (int lh = wave; lh < LH; lh += 4)
+      acc += __builtin_amdgcn_exp2f(col[(size_t)lh * N] - lse2[lh]);
+  }
+  part[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0 && j < N) rule[j] = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+size_t kvs_rule_ws_bytes(int L, int H_q, int64_t N) {
+  const size_t LH = (size_t)L * H_q;
+  const size_t n_chunks = (size_t)ceil_div(N, kChunk);
+  return align256(LH * (size_t)N * 4) + align256(LH * n_chunks * 8) + align256(LH * 4);
+}
+
+hipError_t kvs_launch_rule(const void* K, int dtype, const float* M, int L, int H_q, int H_kv,
+                           int D, int64_t N, int64_t pi, int64_t q_s, int64_t q_e, float* rule,
+                           void* ws, hipStream_t st) {
+  const int LH = L * H_q;
+  const int G = H_q / H_kv;
+  const int n_chunks = (int)ceil_div(N, kChunk);
+  char* w = static_cast<char*>(ws);
+  float* spill = reinterpret_cast<float*>(w);
+  w += align256((size_t)LH * (size_t)N * 4);
+  float2* partials = reinterpret_cast<float2*>(w);
+  w += align256((size_t)LH * n_chunks * 8);
+  float* lse2 = reinterpret_cast<float*>(w);
+  const float scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)D));
+  dim3 grid(n_chunks, L * H_kv), block(256);
+  if (dtype == 1) {
+    const uint16_t* Kb = static_cast<const uint16_t*>(K);
+#define RULE_LAUNCH(DD, NH)                                                                    \
+  hipLaunchKernelGGL((rule_logits_mfma<DD, NH>), grid, block, 0, st, Kb, M, H_q, H_kv, G, N, pi, \
+                     q_s, q_e, scale_log2, spill, partials, n_chunks)
+    if (D == 128) { if (G <= 8) RULE_LAUNCH(128, 1); else RULE_LAUNCH(128, 2); }
+    else { if (G <= 8) RULE_LAUNCH(64, 1); else RULE_LAUNCH(64, 2); }
+#undef RULE_LAUNCH
+  } else {
+    const float* Kf = static_cast<const float*>(K);
+    if (D == 128)
+      hipLaunchKernelGGL((rule_logits_f32<128>), grid, block, 0, st, Kf, M, H_q, H_kv, G, N, pi, q_s,
+                         q_e, scale_log2, spill, partials, n_chunks);
+    else
+      hipLaunchKernelGGL((rule_logits_f32<64>), grid, block, 0, st, Kf, M, H_q, H_kv, G, N, pi, q_s,
+                         q_e, scale_log2, spill, partials, n_chunks);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(rule_lse_merge, dim3(ceil_div(LH, 256)), dim3(256), 0, st, partials, LH,
+                     n_chunks, lse2);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(rule_colsum, dim3(ceil_div(N, kColTile)), dim3(256), 0, st, spill, lse2, LH, N,
+                     rule);
+  return hipGetLastError();
+}

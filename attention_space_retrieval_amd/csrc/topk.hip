@@ -1,0 +1,197 @@
+// Budgeted top-k with a forced set (IntentKV, Sec. 3.1, Eq. 1) and the
+// slot-map redirect of the IntentKV layout layer.
+//
+// Scores map to order-preserving uint32 keys (sign-flip trick; NaN -> 0, the
+// lowest key; -0 -> +0), so the selection is integer-only and exact.  One
+// 1024-thread workgroup runs a radix select over the key range
+// [kmin, kmax] of the candidates, 8 bits per pass with one LDS histogram per
+// wave (no cross-wave atomic contention on hot bins), to find the threshold
+// key T and the number of threshold ties k to keep.  The emit pass gives each
+// wave a contiguous segment of positions; ballot/popcount ranks make the
+// output ascending and hand the k ties to the lowest indices.
+#include "kvs_internal.h"
+
+using namespace kvs;
+
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0u;
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint32_t rank_below(uint64_t mask, int lane) {
+  return (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
+}
+
+struct Forced {
+  int f0b, f0e, f1b, f1e;
+  __device__ bool operator()(int j) const { return (j >= f0b && j < f0e) || (j >= f1b && j < f1e); }
+};
+
+__global__ __launch_bounds__(kThreads) void topk_select_kernel(
+    const float* __restrict__ score, int n, Forced forced, int c_star, int n_forced,
+    uint8_t* __restrict__ keep_mask, int32_t* __restrict__ keep_idx, int64_t* __restrict__ n_kept) {
+  __shared__ uint32_t hist[kWaves][256];
+  __shared__ uint32_t wmin[kWaves], wmax[kWaves];
+  __shared__ uint32_t wcnt[kWaves][2];
+  __shared__ uint32_t state[2];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const bool none = c_star == 0;   // C <= |F|: keep the forced set only
+
+  uint32_t kT = 0xffffffffu, k_tie = 0;
+  if (!none) {
+    uint32_t mn = 0xffffffffu, mx = 0u;
+    for (int j = tid; j < n; j += kThreads)
+      if (!forced(j)) {
+        const uint32_t k = score_key(score[j]);
+        mn = min(mn, k);
+        mx = max(mx, k);
+      }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
+      mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
+    }
+    if (lane == 0) { wmin[wave] = mn; wmax[wave] = mx; }
+    __syncthreads();
+    mn = wmin[0]; mx = wmax[0];
+    for (int w = 1; w < kWaves; ++w) { mn = min(mn, wmin[w]); mx = max(mx, wmax[w]); }
+    const uint32_t range = mx - mn;
+    const int bits = range ? 32 - __clz(range) : 0;
+    const int ndig = (bits + 7) / 8;
+    uint32_t prefix = 0, k = (uint32_t)c_star;
+    for (int p = ndig - 1; p >= 0; --p) {
+      for (int i = tid; i < kWaves * 256; i += kThreads) (&hist[0][0])[i] = 0u;
+      __syncthreads();
+      const int sh = 8 * p;
+      for (int j = tid; j < n; j += kThreads) {
+        if (forced(j)) continue;
+        const uint32_t rel = score_key(score[j]) - mn;
+        const uint32_t hi = sh + 8 >= 32 ? 0u : rel >> (sh + 8);
+        if (hi == prefix) atomicAdd(&hist[wave][(rel >> sh) & 255u], 1u);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        uint32_t c[4], lsum = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t t = 0;
+          for (int w = 0; w < kWaves; ++w) t += hist[w][4 * lane + i];
+          c[i] = t;
+          lsum += t;
+        }
+        // inclusive suffix sum over lanes: elements in bins >= 4*lane
+        uint32_t incl = lsum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t t = (uint32_t)__shfl_down((int)incl, o, kWave);
+          if (lane + o < 64) incl += t;
+        }
+        const uint32_t above = incl - lsum;
+        if (above < k && k <= incl) {
+          uint32_t a = above;
+          for (int i = 3; i >= 0; --i) {
+            if (a + c[i] >= k) {
+              state[0] = (prefix << 8) | (uint32_t)(4 * lane + i);
+              state[1] = k - a;
+              break;
+            }
+            a += c[i];
+          }
+        }
+      }
+      __syncthreads();
+      prefix = state[0];
+      k = state[1];
+      __syncthreads();
+    }
+    kT = mn + prefix;
+    k_tie = k;
+  }
+
+  // Emit: wave w owns positions [w*seg, (w+1)*seg).
+  const int seg = (((n + kWaves - 1) / kWaves) + 63) / 64 * 64;
+  const int s0 = wave * seg, s1 = min(n, s0 + seg);
+  uint32_t c_def = 0, c_tie = 0;
+  for (int base = s0; base < s1; base += 64) {
+    const int j = base + lane;
+    const bool in = j < s1;
+    const bool f = in && forced(j);
+    const uint32_t key = (in && !f && !none) ? score_key(score[j]) : 0u;
+    const bool cand = in && !f && !none;
+    c_def += (uint32_t)__popcll(__ballot(f || (cand && key > kT)));
+    c_tie += (uint32_t)__popcll(__ballot(cand && key == kT));
+  }
+  if (lane == 0) { wcnt[wave][0] = c_def; wcnt[wave][1] = c_tie; }
+  __syncthreads();
+  uint32_t def_base = 0, tie_base = 0;
+  for (int w = 0; w < wave; ++w) { def_base += wcnt[w][0]; tie_base += wcnt[w][1]; }
+  uint32_t out = def_base + min(tie_base, k_tie);
+  uint32_t tie_run = tie_base;
+  for (int base = s0; base < s1; base += 64) {
+    const int j = base + lane;
+    const bool in = j < s1;
+    const bool f = in && forced(j);
+    const bool cand = in && !f && !none;
+    const uint32_t key = cand ? score_key(score[j]) : 0u;
+    const bool tie = cand && key == kT;
+    const uint64_t bt = __ballot(tie);
+    const bool keep = f || (cand && key > kT) || (tie && tie_run + rank_below(bt, lane) < k_tie);
+    const uint64_t bk = __ballot(keep);
+    if (in) keep_mask[j] = keep ? 1 : 0;
+    if (keep) keep_idx[out + rank_below(bk, lane)] = j;
+    tie_run += (uint32_t)__popcll(bt);
+    out += (uint32_t)__popcll(bk);
+  }
+  if (tid == 0) *n_kept = (int64_t)n_forced + c_star;
+}
+
+// C* >= |H|: everything is kept.
+__global__ __launch_bounds__(256) void keep_all_kernel(int n, uint8_t* __restrict__ keep_mask,
+                                                       int32_t* __restrict__ keep_idx,
+                                                       int64_t* __restrict__ n_kept) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j < n) { keep_mask[j] = 1; keep_idx[j] = j; }
+  if (j == 0) *n_kept = n;
+}
+
+__global__ __launch_bounds__(256) void slotmap_kernel(const int64_t* __restrict__ in,
+                                                      const uint8_t* __restrict__ mask, int64_t N,
+                                                      int64_t dead, int64_t* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < N; j += stride)
+    out[j] = mask[j] ? in[j] : dead;
+}
+
+}  // namespace
+
+size_t kvs_topk_ws_bytes(int64_t) { return 0; }
+
+hipError_t kvs_launch_topk(const float* score, int64_t n, int64_t f0b, int64_t f0e, int64_t f1b,
+                           int64_t f1e, int64_t n_forced, int64_t c_star, uint8_t* keep_mask,
+                           int32_t* keep_idx, int64_t* n_kept, void*, hipStream_t st) {
+  if (c_star >= n - n_forced) {   // includes n == 0: still writes n_kept
+    const unsigned blocks = n > 0 ? ceil_div(n, 256) : 1u;
+    hipLaunchKernelGGL(keep_all_kernel, dim3(blocks), dim3(256), 0, st, (int)n, keep_mask, keep_idx,
+                       n_kept);
+    return hipGetLastError();
+  }
+  Forced f{(int)f0b, (int)f0e, (int)f1b, (int)f1e};
+  hipLaunchKernelGGL(topk_select_kernel, dim3(1), dim3(kThreads), 0, st, score, (int)n, f,
+                     (int)c_star, (int)n_forced, keep_mask, keep_idx, n_kept);
+  return hipGetLastError();
+}
+
+hipError_t kvs_launch_slotmap(const int64_t* in, const uint8_t* mask, int64_t N, int64_t dead,
+                              int64_t* out, hipStream_t st) {
+  if (N == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((N + 255) / 256 < 4096 ? (N + 255) / 256 : 4096);
+  hipLaunchKernelGGL(slotmap_kernel, dim3(blocks), dim3(256), 0, st, in, mask, N, dead, out);
+  return hipGetLastError();
+}

@@ -1,0 +1,201 @@
+/*
+ * kvs.h -- attention-space KV-cache scoring and budgeted top-k on AMD MI355X
+ * (gfx950).  Plain C ABI: device pointers, sizes and a HIP stream handle.
+ *
+ * Two modes share the library:
+ *   - IntentKV ("Cross-turn intent-aware KV cache pruning for multi-turn
+ *     reasoning agents"): QueryMemory rule scoring (Sec. 3.2, Eqs. 2-4),
+ *     budgeted top-k with a forced set (Sec. 3.1, Eq. 1), and eviction by
+ *     redirecting dropped slots to a dead slot (abstract, Sec. 1, Sec. 3).
+ *   - KVMEM ("Virtualising million-token agent workspaces onto a laptop
+ *     GPU"): Mean-K block index and block relevance R_b (section "Design and
+ *     trade-offs: step-level attention trigger and Mean-K model-native
+ *     retrieval"), and the execution view rebuilt by re-applying RoPE to raw K
+ *     at compact page-table positions (section "Engineering and cost: tiered
+ *     movement, page-table aliasing and position-consistent reconstruction").
+ *
+ * Conventions for every call
+ *   - Tensors are caller-owned, contiguous, row-major device buffers in the
+ *     layout stated per argument.  The library never allocates, frees or keeps
+ *     a pointer after the call returns.  Scratch memory is a caller workspace
+ *     whose size comes from the matching *_workspace() query.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue work on it and return without synchronising.
+ *   - The return value is a kvs_status, decided on the host before any work is
+ *     enqueued (argument and shape checks).  A failed launch returns
+ *     KVS_ERR_HIP.  Nothing is thrown across the ABI.
+ *   - Results are deterministic: identical inputs give identical bits (no
+ *     floating-point atomics; fixed reduction orders).
+ *   - Layouts use the pages' notation: L layers, H_q query heads, H_kv KV
+ *     heads (G = H_q / H_kv query heads share KV head g = h / G), D head
+ *     dimension, N tokens.
+ *   - bf16 means IEEE binary32 with the low 16 bits dropped (uint16 storage).
+ *   - A data pointer may be NULL only where its tensor holds no elements.
+ */
+#ifndef KVS_H_
+#define KVS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t kvs_status;
+
+#define KVS_OK 0
+#define KVS_ERR_ARG 1          /* null pointer, negative size, bad range, non-finite scalar */
+#define KVS_ERR_SHAPE 2        /* inconsistent sizes (H_q % H_kv != 0, size overflow, ...) */
+#define KVS_ERR_DTYPE 3        /* dtype code not accepted by this call */
+#define KVS_ERR_UNSUPPORTED 4  /* valid but not built: D outside {64, 128}, block != 32 */
+#define KVS_ERR_WORKSPACE 5    /* workspace missing or smaller than the query says */
+#define KVS_ERR_HIP 6          /* the HIP runtime rejected a launch */
+
+#define KVS_F32 0
+#define KVS_BF16 1
+
+/* Human-readable name of a status code (static string). */
+const char* kvs_status_string(kvs_status s);
+
+/* Library version, as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t kvs_version(void);
+
+/*
+ * QueryMemory update -- IntentKV Sec. 3.2, Eq. (2).
+ *   M <- exp(-lambda) * M + Enc(q_t);  M[l,h,:] <- M[l,h,:] / ||M[l,h,:]||_2
+ * Enc(q_t) is the mean of the S post-RoPE query rows of the actionable span.
+ *   q_span   [L, H_q, S, D], dtype q_dtype (KVS_F32 or KVS_BF16), device.
+ *   lambda   decay rate >= 0; +INFINITY gives the page's "query" mode.
+ *   first_turn  nonzero: the previous M is taken as zero and M is not read.
+ *   M        [L, H_q, D] float32, device, read (unless first_turn) and written.
+ * A zero vector stays zero.  Errors: KVS_ERR_ARG (null, S < 1, lambda < 0 or
+ * NaN), KVS_ERR_DTYPE, KVS_ERR_UNSUPPORTED (D not 64 or 128).
+ */
+kvs_status kvs_qmem_update(const void* q_span, int32_t q_dtype, int32_t L, int32_t H_q,
+                           int32_t S, int32_t D, float lambda, int32_t first_turn, float* M,
+                           void* stream);
+
+/* Workspace bytes kvs_rule_score needs for these sizes. */
+size_t kvs_rule_score_workspace(int32_t L, int32_t H_q, int32_t H_kv, int64_t N);
+
+/*
+ * Rule score -- IntentKV Sec. 3.2, Eqs. (3)-(4), with the candidate set of
+ * Sec. 3.1.  For every layer l and query head h, a softmax over the candidate
+ * positions H = [0,N) \ F of M[l,h] . K[l,h/G,j] / sqrt(D), summed over
+ * (l, h):  rule[j] = sum_{l,h} a_{l,h,j}.  F = [0,pi) U [q_s,q_e).
+ *   K        [L, H_kv, N, D] post-RoPE keys, dtype k_dtype (KVS_F32 or KVS_BF16).
+ *   M        [L, H_q, D] float32 QueryMemory.
+ *   pi       protected prefix length (clipped to N); q_s <= q_e actionable span.
+ *   rule     [N] float32 output; exactly 0 on F.  sum(rule) = L*H_q when H is
+ *            non-empty.
+ *   ws       device workspace of >= kvs_rule_score_workspace() bytes.
+ * Errors: KVS_ERR_ARG, KVS_ERR_SHAPE (H_q % H_kv, N > 2^31-1), KVS_ERR_DTYPE,
+ * KVS_ERR_UNSUPPORTED (D not 64/128), KVS_ERR_WORKSPACE.
+ */
+kvs_status kvs_rule_score(const void* K, int32_t k_dtype, const float* M, int32_t L,
+                          int32_t H_q, int32_t H_kv, int32_t D, int64_t N, int64_t pi,
+                          int64_t q_s, int64_t q_e, float* rule, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* Workspace bytes kvs_topk_select needs for n scores. */
+size_t kvs_topk_workspace(int64_t n);
+
+/*
+ * Budgeted top-k with a forced set -- IntentKV Sec. 3.1, Eq. (1); KVMEM's
+ * "sink and recent blocks are always kept, the rest of the budget goes to the
+ * largest R_b" is the same call with the sink and recent ranges as forced.
+ *   score    [n] float32 scores.
+ *   [f0_begin, f0_end), [f1_begin, f1_end)  forced ranges (clipped, may overlap).
+ *   C        total budget including the forced positions; C* = max(0, C - |F|).
+ *   keep_mask [n] uint8 output: 1 = kept.
+ *   keep_idx  [n] int32 output: kept indices ascending in the first n_kept
+ *             entries; the rest is left untouched.
+ *   n_kept    device int64 output: |F| + min(C*, n - |F|).
+ * Order among candidates: larger score first; equal scores -> lower index
+ * first (Eq. 1's argmax is not unique under ties); NaN below every number;
+ * -0.0 equal to +0.0.  C >= n keeps everything; C < |F| keeps F only.
+ * Errors: KVS_ERR_ARG, KVS_ERR_SHAPE (n > 2^31-1), KVS_ERR_WORKSPACE.
+ */
+kvs_status kvs_topk_select(const float* score, int64_t n, int64_t f0_begin, int64_t f0_end,
+                           int64_t f1_begin, int64_t f1_end, int64_t C, uint8_t* keep_mask,
+                           int32_t* keep_idx, int64_t* n_kept, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/*
+ * Slot-map redirect -- IntentKV layout layer (abstract; Sec. 1 contributions;
+ * Sec. 3.1 slot map S_r in Z^N): a dropped position is routed to the sentinel
+ * dead slot; kept positions keep their slot, K/V rows and RoPE phase.
+ *   slot_out[j] = keep_mask[j] ? slot_in[j] : dead_slot
+ *   slot_in, slot_out [N] int64 (may alias); keep_mask [N] uint8.
+ * Errors: KVS_ERR_ARG.
+ */
+kvs_status kvs_slotmap_redirect(const int64_t* slot_in, const uint8_t* keep_mask, int64_t N,
+                                int64_t dead_slot, int64_t* slot_out, void* stream);
+
+/*
+ * Mean-K index build -- KVMEM, section "Design and trade-offs ... Mean-K":
+ * one mean of position-free K per block of `block` tokens, per layer and KV
+ * head.  index[l,g,b,:] = bf16( (1/n_b) sum_{i in block b} k~[l,g,i,:] ),
+ * summed in float32, rounded to nearest-even; a partial last block averages
+ * its n_b < block tokens.
+ *   K        [L, H_kv, N, D] bf16.  k_is_rope = 0: K is raw (pre-RoPE) and k~ = K.
+ *            k_is_rope = 1: K carries RoPE at positions pos0 + i (rotate-half
+ *            pairs (i, i+D/2), omega_i = theta^(-2i/D)) and k~ is K rotated
+ *            back; raw_k_out (nullable, [L,H_kv,N,D] bf16) then receives k~.
+ *   index    [L, H_kv, ceil(N/block), D] bf16 output.
+ * Errors: KVS_ERR_ARG (null, pos0 < 0, theta not finite/positive),
+ * KVS_ERR_UNSUPPORTED (block != 32, D not 64/128), KVS_ERR_SHAPE.
+ */
+kvs_status kvs_meank_build(const void* K, int32_t L, int32_t H_kv, int32_t D, int64_t N,
+                           int32_t block, int32_t k_is_rope, int64_t pos0, double theta,
+                           void* raw_k_out, void* index, void* stream);
+
+/* Workspace bytes kvs_meank_score needs. */
+size_t kvs_meank_score_workspace(int32_t L, int32_t H_q, int32_t H_kv, int64_t Mq, int64_t nB);
+
+/*
+ * Block relevance R_b -- KVMEM, section "Design and trade-offs ... Mean-K":
+ * per layer l, query head h and query token m, a softmax over the candidate
+ * blocks C of q[l,h,m] . kbar[l,h/G,b] / sqrt(D); summed over m and averaged
+ * over the L*H_q (layer, head) pairs.  C = [n_sink, nB - n_recent).
+ *   Q        [L, H_q, Mq, D] bf16 position-free query vectors.
+ *   index    [L, H_kv, nB, D] bf16 Mean-K index.
+ *   R        [nB] float32 output; 0 on sink and recent blocks; sum over C = Mq.
+ *   ws       device workspace of >= kvs_meank_score_workspace() bytes.
+ * Errors: KVS_ERR_ARG, KVS_ERR_SHAPE, KVS_ERR_UNSUPPORTED (D != 128),
+ * KVS_ERR_WORKSPACE.
+ */
+kvs_status kvs_meank_score(const void* Q, const void* index, int32_t L, int32_t H_q,
+                           int32_t H_kv, int32_t D, int64_t Mq, int64_t nB, int64_t n_sink,
+                           int64_t n_recent, float* R, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Re-RoPE scatter into the execution view -- KVMEM, section "Engineering and
+ * cost ...": raw K is the reconstruction authority and RoPE is re-applied at
+ * the block's new compact position; V carries no position and is copied.
+ * For r < n_sel, layer l, KV head g, offset t < block:
+ *   k_pool[l,g, block*page_table[r] + t, :] = RoPE(pos_base + block*r + t) k_src[l,g, block*src_block[r] + t, :]
+ *   v_pool[l,g, block*page_table[r] + t, :] = v_src[l,g, block*src_block[r] + t, :]
+ * RoPE: rotate-half pairs (i, i+D/2), omega_i = theta^(-2i/D), angles reduced
+ * in float64, rotation in float32, bf16 nearest-even output.
+ *   k_src, v_src [L, H_kv, src_tokens, D] bf16 (src_tokens a multiple of block).
+ *   src_block    [n_sel] int32 device, block ids into the source.
+ *   page_table   [n_sel] int32 device destination pages, or NULL for r -> r.
+ *   k_pool, v_pool [L, H_kv, pool_pages*block, D] bf16 outputs; pages not
+ *                named keep their contents.  v_src/v_pool may both be NULL.
+ *   err_flag     nullable device int32: set to 1 if a src_block or
+ *                page_table entry is out of range (that block is skipped).
+ * Errors: KVS_ERR_ARG, KVS_ERR_SHAPE, KVS_ERR_UNSUPPORTED (block != 32, D not 64/128).
+ */
+kvs_status kvs_rerope_scatter(const void* k_src, const void* v_src, int64_t src_tokens,
+                              const int32_t* src_block, const int32_t* page_table, int64_t n_sel,
+                              int32_t L, int32_t H_kv, int32_t D, int32_t block, int64_t pos_base,
+                              double theta, void* k_pool, void* v_pool, int64_t pool_pages,
+                              int32_t* err_flag, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVS_H_ */

@@ -1,0 +1,110 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header
+declares, and rejects bad arguments on the host before any HIP call."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from attention_space_retrieval_amd import kvs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvs.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvs_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return kvs.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = header_functions()
+    assert len(names) == 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(kvs.ENTRY_POINTS) == names
+
+
+def test_status_strings(lib):
+    assert lib.kvs_status_string(0) == b"ok"
+    assert lib.kvs_status_string(5) == b"workspace missing or too small"
+    assert lib.kvs_version() >= 100
+
+
+FAKE = 0x1000   # never dereferenced: every call below must be rejected on the host
+
+
+def test_qmem_rejections(lib):
+    f = lib.kvs_qmem_update
+    assert f(None, 1, 2, 4, 8, 128, 0.5, 1, FAKE, None) == 1
+    assert f(FAKE, 7, 2, 4, 8, 128, 0.5, 1, FAKE, None) == 3
+    assert f(FAKE, 1, 2, 4, 0, 128, 0.5, 1, FAKE, None) == 1
+    assert f(FAKE, 1, 2, 4, 8, 128, -1.0, 1, FAKE, None) == 1
+    assert f(FAKE, 1, 2, 4, 8, 128, math.nan, 1, FAKE, None) == 1
+    assert f(FAKE, 1, 2, 4, 8, 96, 0.5, 1, FAKE, None) == 4
+
+
+def test_rule_rejections(lib):
+    f = lib.kvs_rule_score
+    ws = lib.kvs_rule_score_workspace(2, 4, 2, 1024)
+    assert ws >= 2 * 4 * 1024 * 4
+    args = dict(K=FAKE, dt=1, M=FAKE, L=2, Hq=4, Hkv=2, D=128, N=1024, pi=16, qs=992, qe=1024,
+                rule=FAKE, ws=FAKE, wsb=ws)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["K"], a["dt"], a["M"], a["L"], a["Hq"], a["Hkv"], a["D"], a["N"], a["pi"],
+                 a["qs"], a["qe"], a["rule"], a["ws"], a["wsb"], None)
+
+    assert call(K=None) == 1
+    assert call(dt=5) == 3
+    assert call(Hq=5) == 2
+    assert call(qs=10, qe=5) == 1
+    assert call(pi=-1) == 1
+    assert call(D=80) == 4
+    assert call(Hq=34, Hkv=2) == 4          # G = 17 > 16 is not built
+    assert call(ws=None) == 5
+    assert call(wsb=ws - 1) == 5
+    assert call(N=1 << 31) == 2
+    assert call(N=0) == 0                   # empty input: nothing to do, nothing launched
+
+
+def test_topk_slot_meank_rerope_rejections(lib):
+    assert lib.kvs_topk_select(None, 10, 0, 1, 5, 6, 3, FAKE, FAKE, FAKE, None, 0, None) == 1
+    assert lib.kvs_topk_select(FAKE, 10, 3, 1, 5, 6, 3, FAKE, FAKE, FAKE, None, 0, None) == 1
+    assert lib.kvs_topk_select(FAKE, 10, 0, 1, 5, 6, -1, FAKE, FAKE, FAKE, None, 0, None) == 1
+    assert lib.kvs_topk_select(FAKE, 1 << 31, 0, 1, 5, 6, 3, FAKE, FAKE, FAKE, None, 0, None) == 2
+    assert lib.kvs_slotmap_redirect(None, FAKE, 10, -1, FAKE, None) == 1
+    assert lib.kvs_slotmap_redirect(FAKE, FAKE, -1, -1, FAKE, None) == 1
+    assert lib.kvs_meank_build(FAKE, 2, 2, 128, 64, 16, 0, 0, 1e6, None, FAKE, None) == 4
+    assert lib.kvs_meank_build(FAKE, 2, 2, 128, 64, 32, 1, 0, math.inf, None, FAKE, None) == 1
+    assert lib.kvs_meank_build(FAKE, 2, 2, 128, 64, 32, 1, -5, 1e6, None, FAKE, None) == 1
+    assert lib.kvs_meank_build(None, 2, 2, 128, 64, 32, 0, 0, 1e6, None, FAKE, None) == 1
+    ws = lib.kvs_meank_score_workspace(2, 8, 2, 50, 300)
+    assert ws > 0
+    assert lib.kvs_meank_score(FAKE, FAKE, 2, 8, 2, 64, 50, 300, 4, 7, FAKE, FAKE, ws, None) == 4
+    assert lib.kvs_meank_score(FAKE, FAKE, 2, 8, 3, 128, 50, 300, 4, 7, FAKE, FAKE, ws, None) == 2
+    assert lib.kvs_meank_score(FAKE, FAKE, 2, 8, 2, 128, 50, 300, 4, 7, FAKE, FAKE, ws - 1, None) == 5
+    assert lib.kvs_meank_score(FAKE, FAKE, 2, 8, 2, 128, 50, 300, -1, 7, FAKE, FAKE, ws, None) == 1
+    r = lib.kvs_rerope_scatter
+    assert r(FAKE, FAKE, 640, FAKE, None, 3, 2, 2, 128, 32, 0, 1e6, FAKE, None, 8, None, None) == 1
+    assert r(FAKE, FAKE, 650, FAKE, None, 3, 2, 2, 128, 32, 0, 1e6, FAKE, FAKE, 8, None, None) == 2
+    assert r(FAKE, FAKE, 640, FAKE, None, 3, 2, 2, 128, 64, 0, 1e6, FAKE, FAKE, 8, None, None) == 4
+    assert r(FAKE, FAKE, 640, FAKE, None, 3, 2, 2, 128, 32, 0, -1.0, FAKE, FAKE, 8, None, None) == 1
+    assert r(FAKE, FAKE, 640, None, None, 3, 2, 2, 128, 32, 0, 1e6, FAKE, FAKE, 8, None, None) == 1
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError, match="GPU"):
+        kvs.kvs_rule_score(torch.zeros(1, 1, 8, 64), torch.zeros(1, 1, 64), 0, 0, 0)
+    with pytest.raises(ValueError, match="GPU"):
+        kvs.kvs_topk_select(torch.zeros(8), (0, 0), (0, 0), 3)

@@ -1,0 +1,206 @@
+"""GPU parity, KVMEM Mean-K mode: index build, block relevance, selection, re-RoPE scatter.
+
+Tolerances: index within 1 bf16 ulp of the float64 mean (+1e-5 absolute for
+float32 summation of 32 bf16 keys); R_b 2e-3 relative per candidate block;
+re-RoPE'd K within max(1e-2, 1 bf16 ulp) of the float64 rotation, and within
+1 ulp + 1e-6 as the tighter check actually met; V bit-exact; selections
+bit-exact on identical float32 scores.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attention_space_retrieval_amd import kvs, workloads as W
+from tests.helpers import assert_rel, assert_within_ulp, bf16_ulp, bits, host
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+R_RTOL = 2e-3
+
+
+# ---------------------------------------------------------------- index build
+
+@pytest.mark.parametrize("L,H_kv,N,D", [(2, 3, 1000, 128), (1, 2, 64, 64), (2, 8, 4096, 128), (1, 1, 7, 128)])
+def test_meank_build_raw(L, H_kv, N, D):
+    K = W.normal((L, H_kv, N, D), 21, W.T_K, "bf16", DEV)
+    idx = kvs.kvs_meank_build(K)
+    torch.cuda.synchronize()
+    want, _ = oracle.meank_build(host(K))
+    assert_within_ulp(bits(idx), want, "index", atol=1e-5)
+
+
+@pytest.mark.parametrize("D,pos0", [(128, 0), (128, 1000000 - 640), (64, 12345)])
+def test_meank_build_derope(D, pos0):
+    L, H_kv, N, theta = 2, 2, 640 + 17, 1e6
+    raw = host(W.normal((L, H_kv, N, D), 22, W.T_K, "bf16", "cpu"))
+    post = oracle.f64_to_bf16_bits(oracle.rope_rotate(oracle.bf16_bits_to_f64(raw),
+                                                      pos0 + np.arange(N), theta))
+    Kt = torch.from_numpy(post.view(np.int16)).view(torch.bfloat16).to(DEV)
+    raw_out = torch.empty_like(Kt)
+    idx = kvs.kvs_meank_build(Kt, k_is_rope=True, pos0=pos0, theta=theta, raw_k_out=raw_out)
+    torch.cuda.synchronize()
+    want_idx, want_raw = oracle.meank_build(post, k_is_rope=True, pos0=pos0, theta=theta)
+    assert_within_ulp(bits(raw_out), want_raw, "de-RoPE'd K", atol=1e-6)
+    assert_within_ulp(bits(idx), want_idx, "index (de-RoPE mode)", atol=1e-5)
+
+
+def test_meank_build_full_size_sampled():
+    """meank-256k in the benchmark's launch shape; sampled blocks checked one by one."""
+    c = W.config("meank-256k")
+    K = W.normal((c["L"], c["H_kv"], c["N"], c["D"]), c["seed"], W.T_K, "bf16", DEV)
+    idx = kvs.kvs_meank_build(K)
+    torch.cuda.synchronize()
+    r = np.random.default_rng(5)
+    nB = c["N"] // 32
+    for _ in range(64):
+        l, g, b = int(r.integers(c["L"])), int(r.integers(c["H_kv"])), int(r.integers(nB))
+        blk = host(K[l, g, 32 * b:32 * b + 32])[None, None]
+        want, _ = oracle.meank_build(blk)
+        assert_within_ulp(bits(idx[l, g, b])[None, None, None], want, f"index block {(l, g, b)}", atol=1e-5)
+    del K
+
+
+# ---------------------------------------------------------------- block relevance
+
+def check_score(Q, index, n_sink, n_recent, what):
+    R = kvs.kvs_meank_score(Q, index, n_sink, n_recent)
+    torch.cuda.synchronize()
+    got = R.cpu().numpy()
+    want = oracle.meank_score(host(Q), host(index), n_sink, n_recent)
+    C = oracle.candidate_blocks(index.shape[2], n_sink, n_recent)
+    assert np.all(got[~C] == 0.0), f"{what}: forced blocks must score exactly 0"
+    if C.any() and Q.shape[2] > 0:
+        assert_rel(got[C], want[C], R_RTOL, what)
+        assert abs(got.sum(dtype=np.float64) - Q.shape[2]) <= 1e-4 * Q.shape[2]
+    return got, want
+
+
+@pytest.mark.parametrize("L,H_q,H_kv,Mq,nB,sink,recent", [
+    (2, 8, 2, 50, 300, 4, 7),        # ragged rows (200) and columns (289)
+    (1, 40, 8, 33, 130, 4, 64),      # G = 5, 62 candidate blocks
+    (2, 4, 4, 64, 96, 0, 0),         # G = 1, no forced blocks
+    (1, 8, 2, 1, 40, 1, 1),          # one query token
+    (1, 2, 1, 16, 70, 35, 35),       # no candidates
+])
+def test_meank_score_shapes(L, H_q, H_kv, Mq, nB, sink, recent):
+    Q = W.normal((L, H_q, Mq, 128), 31, W.T_Q, "bf16", DEV)
+    index = W.index_like(L, H_kv, nB, 128, 31, DEV)
+    check_score(Q, index, sink, recent, f"R L{L} Hq{H_q} Hkv{H_kv} Mq{Mq} nB{nB}")
+
+
+def test_meank_score_peaked_softmax():
+    # index spread 1.0 with N(0,1) queries: logits of several units, far from uniform
+    Q = W.normal((2, 8, 40, 128), 32, W.T_Q, "bf16", DEV)
+    index = W.index_like(2, 2, 200, 128, 32, DEV, scale=1.0)
+    check_score(Q, index, 4, 8, "peaked")
+
+
+def test_meank_score_layer_slice_full_extent():
+    """Two layers of meank-256k at their full per-(l,g) extent: 2560 query rows x 8124 blocks."""
+    c = W.config("meank-256k")
+    L = 2
+    Q = W.normal((L, c["H_q"], c["Mq"], c["D"]), c["seed"], W.T_Q, "bf16", DEV)
+    index = W.index_like(L, c["H_kv"], c["N"] // 32, c["D"], c["seed"], DEV)
+    check_score(Q, index, c["n_sink"], c["n_recent"], "meank-256k, 2 layers")
+
+
+def test_meank_score_full_size_properties():
+    """meank-256k in the benchmark's launch shape: mass, zeros on forced blocks, determinism."""
+    c = W.config("meank-256k")
+    nB = c["N"] // 32
+    Q = W.normal((c["L"], c["H_q"], c["Mq"], c["D"]), c["seed"], W.T_Q, "bf16", DEV)
+    index = W.index_like(c["L"], c["H_kv"], nB, c["D"], c["seed"], DEV)
+    R1 = kvs.kvs_meank_score(Q, index, c["n_sink"], c["n_recent"]).clone()
+    R2 = kvs.kvs_meank_score(Q, index, c["n_sink"], c["n_recent"])
+    torch.cuda.synchronize()
+    assert torch.equal(R1, R2)
+    r = R1.cpu().numpy().astype(np.float64)
+    C = oracle.candidate_blocks(nB, c["n_sink"], c["n_recent"])
+    assert np.all(r[~C] == 0) and np.all(r[C] > 0)
+    assert abs(r.sum() - c["Mq"]) <= 1e-4 * c["Mq"]
+
+
+# ---------------------------------------------------------------- re-RoPE scatter
+
+@pytest.mark.parametrize("D,pos_base,with_v,identity", [(128, 0, True, False), (128, 1000000, True, True),
+                                                        (64, 77, False, False)])
+def test_rerope_scatter(D, pos_base, with_v, identity):
+    L, H_kv, n_src_blocks, pool_pages, n_sel, theta = 2, 3, 20, 12, 7, 1e6
+    k_src = W.normal((L, H_kv, 32 * n_src_blocks, D), 41, W.T_K, "bf16", DEV)
+    v_src = W.normal((L, H_kv, 32 * n_src_blocks, D), 41, W.T_V, "bf16", DEV) if with_v else None
+    src_block = torch.tensor([0, 3, 4, 9, 10, 17, 19], dtype=torch.int32, device=DEV)
+    pt = None if identity else W.page_permutation(n_sel, pool_pages, 41).to(DEV)
+    k_pool = torch.full((L, H_kv, 32 * pool_pages, D), -3.0, dtype=torch.bfloat16, device=DEV)
+    v_pool = torch.full_like(k_pool, 5.0) if with_v else None      # bf16 5.0 = 0x40A0
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kvs.kvs_rerope_scatter(k_src, v_src, src_block, pt, n_sel, pos_base, theta, k_pool, v_pool, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    k0 = np.full((L, H_kv, 32 * pool_pages, D), -3.0)
+    v0 = np.full((L, H_kv, 32 * pool_pages, D), 0x40A0, dtype=np.uint16)
+    ko, vo = oracle.rerope_scatter(host(k_src), host(v_src) if with_v else host(k_src),
+                                   src_block.cpu().numpy(), None if pt is None else pt.cpu().numpy(),
+                                   pos_base, theta, k0, v0)
+    kb = bits(k_pool)
+    g = oracle.bf16_bits_to_f64(kb)
+    assert np.max(np.abs(g - ko) - np.maximum(1e-2, bf16_ulp(ko))) <= 0      # the stated bar
+    assert_within_ulp(kb, ko, "re-RoPE'd K", atol=1e-6)                       # what is met
+    if with_v:
+        np.testing.assert_array_equal(bits(v_pool), vo)
+
+
+def test_rerope_scatter_rejects_bad_indices():
+    L, H_kv, D = 1, 2, 128
+    k_src = W.normal((L, H_kv, 64, D), 42, W.T_K, "bf16", DEV)
+    k_pool = torch.zeros((L, H_kv, 64, D), dtype=torch.bfloat16, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    src = torch.tensor([1, 2], dtype=torch.int32, device=DEV)     # block 2 does not exist
+    pt = torch.tensor([0, 1], dtype=torch.int32, device=DEV)
+    kvs.kvs_rerope_scatter(k_src, None, src, pt, 2, 0, 1e6, k_pool, None, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 1
+    assert torch.all(k_pool[:, :, 32:] == 0)                     # the bad block was skipped
+    want, _ = oracle.rerope_scatter(host(k_src), host(k_src), [1], [0], 0, 1e6,
+                                    np.zeros((L, H_kv, 32, D)), np.zeros((L, H_kv, 32, D)))
+    assert_within_ulp(bits(k_pool[:, :, :32]), want, "valid block", atol=1e-6)
+
+
+# ---------------------------------------------------------------- chain
+
+def test_meank_step_planted_evidence():
+    """build -> score -> select -> scatter; blocks planted along the queries' direction are kept."""
+    L, H_q, H_kv, Mq, N, D = 2, 8, 2, 24, 32 * 96, 128
+    r = np.random.default_rng(7)
+    u = r.standard_normal(D); u /= np.linalg.norm(u)
+    K = W.normal((L, H_kv, N, D), 51, W.T_K, "bf16", "cpu").float()
+    planted = [10, 23, 40, 41, 70]
+    for b in planted:
+        K[:, :, 32 * b:32 * b + 32, :] += torch.from_numpy(3.0 * u).float()
+    K = K.to(torch.bfloat16).to(DEV)
+    Q = (W.normal((L, H_q, Mq, D), 51, W.T_Q, "bf16", "cpu").float() + torch.from_numpy(4.0 * u).float())
+    Q = Q.to(torch.bfloat16).to(DEV)
+    V = W.normal((L, H_kv, N, D), 51, W.T_V, "bf16", DEV)
+    n_sink, n_recent, budget = 4, 8, 4 + 8 + len(planted)
+    idx = kvs.kvs_meank_build(K)
+    R = kvs.kvs_meank_score(Q, idx, n_sink, n_recent)
+    nB = N // 32
+    keep, kidx, nk = kvs.kvs_topk_select(R, (0, n_sink), (nB - n_recent, nB), budget)
+    torch.cuda.synchronize()
+    nk = int(nk.item())
+    sel = kidx[:nk].cpu().numpy()
+    assert set(planted) <= set(sel.tolist())
+    # the oracle chain on the same inputs picks the same blocks
+    o_idx, _ = oracle.meank_build(host(K))
+    o_R = oracle.meank_score(host(Q), o_idx, n_sink, n_recent)
+    o_sel, dst, _ = oracle.meank_select(o_R, n_sink, n_recent, budget)
+    np.testing.assert_array_equal(sel, o_sel)
+    k_pool = torch.zeros((L, H_kv, 32 * nk, D), dtype=torch.bfloat16, device=DEV)
+    v_pool = torch.zeros_like(k_pool)
+    kvs.kvs_rerope_scatter(K, V, kidx[:nk].contiguous(), None, nk, 0, 1e6, k_pool, v_pool)
+    torch.cuda.synchronize()
+    ko, vo = oracle.rerope_scatter(host(K), host(V), o_sel, None, 0, 1e6,
+                                   np.zeros(k_pool.shape), np.zeros(k_pool.shape, dtype=np.uint16))
+    assert_within_ulp(bits(k_pool), ko, "scattered K", atol=1e-6)
+    np.testing.assert_array_equal(bits(v_pool), vo)

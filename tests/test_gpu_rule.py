@@ -1,0 +1,229 @@
+"""GPU parity, IntentKV rule mode: QueryMemory, rule score, top-k, slot redirect.
+
+Every case feeds the same seeded tensors to the HIP library (through the C ABI)
+and to the float64 oracle.  Tolerances: QueryMemory 1e-5 absolute; rule scores
+2e-3 relative per candidate (float32 accumulation against float64); top-k and
+slot maps bit-exact when both sides rank the same float32 scores; chained
+selections (GPU scores vs oracle scores) must be valid top-C* sets under the
+oracle's scores up to that score tolerance.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from attention_space_retrieval_amd import kvs, workloads as W
+from tests.helpers import assert_rel, assert_valid_selection, host
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+RULE_RTOL = 2e-3
+
+
+def gpu_rule(K, M, pi, q_s, q_e):
+    r = kvs.kvs_rule_score(K, M, pi, q_s, q_e)
+    torch.cuda.synchronize()
+    return r
+
+
+def check_rule(K, M, pi, q_s, q_e, what, M_oracle=None):
+    """M_oracle: the oracle's own QueryMemory when M came from the GPU."""
+    got = gpu_rule(K, M, pi, q_s, q_e).cpu().numpy()
+    want = oracle.rule_score(host(K), host(M) if M_oracle is None else M_oracle, pi, q_s, q_e)
+    F = oracle.forced_mask(K.shape[2], pi, q_s, q_e)
+    assert np.all(got[F] == 0.0), f"{what}: forced positions must score exactly 0"
+    if (~F).any():
+        assert_rel(got[~F], want[~F], RULE_RTOL, what)
+        L, H_q = M.shape[0], M.shape[1]
+        assert abs(got.sum(dtype=np.float64) - L * H_q) <= 1e-4 * L * H_q
+    return got, want
+
+
+# ---------------------------------------------------------------- QueryMemory
+
+@pytest.mark.parametrize("dtype,D,S", [("f32", 64, 32), ("bf16", 128, 64), ("bf16", 64, 5)])
+def test_qmem_turns(dtype, D, S):
+    L, H_q, T, lam = 3, 8, 4, 0.3
+    spans = [W.normal((L, H_q, S, D), 77, 100 + t, dtype, DEV) for t in range(T)]
+    M = torch.empty((L, H_q, D), dtype=torch.float32, device=DEV)
+    Mo = None
+    for t, q in enumerate(spans):
+        kvs.kvs_qmem_update(q, lam, M, first_turn=(t == 0))
+        Mo = oracle.qmem_update(host(q), lam, Mo)
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(M.cpu().numpy(), Mo, rtol=0, atol=1e-5)
+
+
+def test_qmem_query_mode_and_zero():
+    L, H_q, S, D = 2, 4, 8, 128
+    q0 = W.normal((L, H_q, S, D), 78, 1, "bf16", DEV)
+    q1 = W.normal((L, H_q, S, D), 78, 2, "bf16", DEV)
+    M = torch.full((L, H_q, D), float("nan"), device=DEV)     # first turn must not read M
+    kvs.kvs_qmem_update(q0, math.inf, M, True)
+    kvs.kvs_qmem_update(q1, math.inf, M, False)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(M.cpu().numpy(), oracle.qmem_update(host(q1), math.inf), atol=1e-5)
+    z = torch.zeros((1, 2, 3, 64), device=DEV)
+    Mz = torch.empty((1, 2, 64), device=DEV)
+    kvs.kvs_qmem_update(z, 0.5, Mz, True)
+    torch.cuda.synchronize()
+    assert torch.all(Mz == 0)
+
+
+# ---------------------------------------------------------------- rule score
+
+def test_rule_tiny_config():
+    c = W.config("rule-tiny")
+    inp = W.rule_inputs(c, DEV)
+    M = torch.empty((c["L"], c["H_q"], c["D"]), dtype=torch.float32, device=DEV)
+    Mo = None
+    for t, q in enumerate(inp["spans"]):
+        kvs.kvs_qmem_update(q, c["lam"], M, t == 0)
+        Mo = oracle.qmem_update(host(q), c["lam"], Mo)
+    check_rule(inp["K"], M, c["pi"], c["q_s"], c["q_e"], "rule-tiny", M_oracle=Mo)
+
+
+@pytest.mark.parametrize("L,H_q,H_kv,D,N,pi,q_s,q_e", [
+    (2, 32, 8, 128, 5000, 64, 4900, 4964),     # 3 chunks, ragged tail, G = 4
+    (3, 40, 8, 128, 4097, 1, 4097, 4097),      # G = 5, one-row tail chunk, empty span
+    (2, 8, 8, 128, 300, 0, 0, 0),              # G = 1, no forced positions
+    (1, 24, 2, 128, 2100, 10, 20, 30),         # G = 12: two 8-head groups
+    (2, 16, 4, 64, 3000, 5, 2990, 3000),       # D = 64
+    (1, 4, 2, 128, 1, 0, 0, 0),                # N = 1
+])
+def test_rule_bf16_shapes(L, H_q, H_kv, D, N, pi, q_s, q_e):
+    K = W.normal((L, H_kv, N, D), 11, W.T_K, "bf16", DEV)
+    M = W.memory_vectors(L, H_q, D, 11, DEV)
+    check_rule(K, M, pi, q_s, q_e, f"rule L{L} Hq{H_q} Hkv{H_kv} D{D} N{N}")
+
+
+def test_rule_large_logits_keep_precision():
+    # |M| ~ 10 and K spread ~ 3: logits of tens; the hi/lo split of M keeps them exact enough.
+    L, H_q, H_kv, D, N = 1, 8, 2, 128, 3000
+    K = W.normal((L, H_kv, N, D), 12, W.T_K, "bf16", DEV, scale=3.0)
+    M = W.memory_vectors(L, H_q, D, 12, DEV) * 1.0
+    check_rule(K, M, 0, 0, 0, "large logits")
+
+
+def test_rule_all_forced_and_determinism():
+    L, H_q, H_kv, D, N = 2, 8, 2, 128, 700
+    K = W.normal((L, H_kv, N, D), 13, W.T_K, "bf16", DEV)
+    M = W.memory_vectors(L, H_q, D, 13, DEV)
+    assert torch.all(gpu_rule(K, M, 400, 300, 700) == 0)
+    a = gpu_rule(K, M, 3, 600, 650).clone()
+    b = gpu_rule(K, M, 3, 600, 650)
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["rule-8b", "rule-14b"])
+def test_rule_full_size(name):
+    """Full configuration in the benchmark's launch shape, every output against the oracle."""
+    c = W.config(name)
+    print(f"[{name}] generating inputs", flush=True)
+    inp = W.rule_inputs(c, DEV)
+    M = torch.empty((c["L"], c["H_q"], c["D"]), dtype=torch.float32, device=DEV)
+    Mo = None
+    for t, q in enumerate(inp["spans"]):
+        kvs.kvs_qmem_update(q, c["lam"], M, t == 0)
+        Mo = oracle.qmem_update(host(q), c["lam"], Mo)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(M.cpu().numpy(), Mo, atol=1e-5)
+    print(f"[{name}] oracle rule score", flush=True)
+    got, want = check_rule(inp["K"], M, c["pi"], c["q_s"], c["q_e"], name, M_oracle=Mo)
+    # selection on the GPU's scores is a valid top-C* under the oracle's scores
+    keep, idx, nk = kvs.kvs_topk_select(torch.from_numpy(got).to(DEV), (0, c["pi"]),
+                                        (c["q_s"], c["q_e"]), c["C"])
+    nk = int(nk.item())
+    F = oracle.forced_mask(c["N"], c["pi"], c["q_s"], c["q_e"])
+    assert nk == c["C"]
+    assert_valid_selection(want, idx[:nk].cpu().numpy(), F, c["C"] - int(F.sum()), 2 * RULE_RTOL)
+
+
+# ---------------------------------------------------------------- top-k
+
+def check_topk(score, f0, f1, C):
+    keep, idx, nk = kvs.kvs_topk_select(score, f0, f1, C)
+    torch.cuda.synchronize()
+    ok, oidx, onk = oracle.topk_select(score.cpu().numpy(), f0, f1, C)
+    nk = int(nk.item())
+    assert nk == onk
+    np.testing.assert_array_equal(keep.cpu().numpy().astype(bool), ok)
+    np.testing.assert_array_equal(idx[:nk].cpu().numpy(), oidx)
+
+
+@pytest.mark.parametrize("n,levels,f0,f1,C", [
+    (1024, None, (0, 16), (992, 1024), 256),
+    (1024, 7, (0, 16), (992, 1024), 256),          # heavy ties at the threshold
+    (32768, 50, (0, 64), (32704, 32768), 8192),
+    (92160, None, (0, 64), (92096, 92160), 8192),
+    (92160, 3, (0, 64), (92096, 92160), 8192),
+    (8192, 1000, (0, 4), (8128, 8192), 2048),      # Mean-K shape
+    (4097, 2, (5, 3000), (2000, 4097), 3500),      # overlapping forced ranges
+    (1, None, (0, 0), (0, 0), 1),
+    (77, None, (0, 0), (0, 0), 0),                 # C = 0
+    (500, None, (0, 10), (490, 500), 5),           # C < |F|
+    (500, None, (0, 10), (490, 500), 10000),       # C >= n
+    (0, None, (0, 0), (0, 0), 5),                  # empty input
+])
+def test_topk_bit_exact(n, levels, f0, f1, C):
+    score = W.scores_with_ties(n, n + 1, levels).to(DEV)
+    check_topk(score, f0, f1, C)
+
+
+def test_topk_special_values():
+    s = torch.tensor([float("nan"), -float("inf"), 0.0, -0.0, 1.0, float("inf"), -1e-30, 1e-30,
+                      float("nan"), 0.0], device=DEV)
+    for C in range(0, 11):
+        check_topk(s, (0, 0), (0, 0), C)
+    check_topk(s, (4, 6), (0, 1), 5)
+
+
+def test_topk_all_equal():
+    s = torch.full((10000,), 0.25, device=DEV)
+    check_topk(s, (0, 3), (9990, 10000), 1000)
+
+
+# ---------------------------------------------------------------- slot map
+
+def test_slotmap_bit_exact():
+    c = W.config("rule-tiny")
+    score = W.scores_with_ties(c["N"], 5).to(DEV)
+    keep, idx, nk = kvs.kvs_topk_select(score, (0, c["pi"]), (c["q_s"], c["q_e"]), c["C"])
+    slots = W.rule_inputs(c, DEV)["slots"]
+    out = kvs.kvs_slotmap_redirect(slots, keep, c["dead_slot"])
+    torch.cuda.synchronize()
+    want = oracle.slotmap_redirect(slots.cpu().numpy(), keep.cpu().numpy().astype(bool), c["dead_slot"])
+    np.testing.assert_array_equal(out.cpu().numpy(), want)
+    assert int((out == -1).sum()) == c["N"] - c["C"]
+    kvs.kvs_slotmap_redirect(slots, keep, 123456789, slot_out=slots)      # in place
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(slots.cpu().numpy(), np.where(want == -1, 123456789, want))
+
+
+def test_rule_turn_end_to_end_tiny():
+    """qmem x 3 turns -> rule -> top-k -> slot map on rule-tiny, against the oracle chain."""
+    c = W.config("rule-tiny")
+    inp = W.rule_inputs(c, DEV)
+    M = torch.empty((c["L"], c["H_q"], c["D"]), dtype=torch.float32, device=DEV)
+    Mo = None
+    for t, q in enumerate(inp["spans"]):
+        kvs.kvs_qmem_update(q, c["lam"], M, t == 0)
+        Mo = oracle.qmem_update(host(q), c["lam"], Mo)
+    rule = kvs.kvs_rule_score(inp["K"], M, c["pi"], c["q_s"], c["q_e"])
+    keep, idx, nk = kvs.kvs_topk_select(rule, (0, c["pi"]), (c["q_s"], c["q_e"]), c["C"])
+    slots = kvs.kvs_slotmap_redirect(inp["slots"], keep, c["dead_slot"])
+    torch.cuda.synchronize()
+    o_rule = oracle.rule_score(host(inp["K"]), Mo, c["pi"], c["q_s"], c["q_e"])
+    F = oracle.forced_mask(c["N"], c["pi"], c["q_s"], c["q_e"])
+    assert_rel(rule.cpu().numpy()[~F], o_rule[~F], RULE_RTOL, "chain rule")
+    nk = int(nk.item())
+    assert nk == c["C"]
+    kidx = idx[:nk].cpu().numpy()
+    assert_valid_selection(o_rule, kidx, F, c["C"] - int(F.sum()), 2 * RULE_RTOL)
+    s = slots.cpu().numpy()
+    kept = np.zeros(c["N"], bool); kept[kidx] = True
+    np.testing.assert_array_equal(s[kept], inp["slots"].cpu().numpy()[kept])
+    assert np.all(s[~kept] == c["dead_slot"])
