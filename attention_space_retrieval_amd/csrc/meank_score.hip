@@ -5,20 +5,28 @@
 //
 // Per (l, g) this is a dense contraction S = Q_g x index_g^T with Q_g the
 // G*Mq query rows of the KV group (contiguous in [L, H_q, Mq, D]) and index_g
-// the |C| candidate block means; it runs on bf16 MFMA 32x32x16 with float32
+// the |C| candidate block means, on bf16 MFMA 32x32x16 with float32
 // accumulation.  An exact per-row softmax needs each row's normaliser before
-// any column can be summed, and S is far too large to keep, so there are two
-// passes over the tiles:
-//   1. meank_lse: a wave keeps 32 query rows as the B operand and sweeps the
-//      index (A operand).  The tile is S^T, so each lane owns one query row and
-//      the online (max, sum 2^(x-max)) stays in-lane.   -> lse2 per row
-//   2. meank_colsum: a wave keeps 32 index rows as the B operand and sweeps the
-//      query rows (A operand).  Now each lane owns one block column and
-//      sum_m 2^(x - lse2[m]) stays in-lane.             -> per-(l,g) partials
-//   3. meank_reduce: R_b = sum over (l,g) of the partials, in order, / (L*H_q).
+// any column can be summed and S is far too large to keep, so the tiles are
+// computed twice:
+//   pass 1 (lse):    persistent operand = 64 query rows per wave, streamed =
+//                    32-block index tiles.  C = index_tile x Q^T, so a lane
+//                    owns one query row and its online (max, sum 2^(x-max))
+//                    is reduced in-lane.                -> lse2[row]
+//   pass 2 (colsum): persistent operand = 64 index rows per wave, streamed =
+//                    32-row query tiles (+ their lse2).  C = Q_tile x index^T,
+//                    so a lane owns one block column and
+//                    sum_m 2^(x - lse2[m]) is in-lane.  -> per-(l,g) partials
+//   reduce:          R_b = sum of the (l,g) partials in fixed order / (L*H_q).
+// Both passes share one engine: a 256-thread workgroup keeps 256 persistent
+// rows in registers, streams 8 KB tiles global -> LDS (double buffered, rows
+// XOR-swizzled in 16-byte chunks so the MFMA operand reads are bank-conflict
+// free) and software-pipelines each wave: the MFMAs of tile t+1 are issued
+// before the exp2 epilogue of tile t, so matrix and vector units overlap.
+// Workgroups are mapped XCD-aware: the tiles of one (l, g) land on the same
+// XCD and share its L2 copy of the streamed operand.
 // Operand k-slots: lane half h = lane/32 carries k-slots 8h..8h+7 of every
-// k-step; k-step s of half h is dims [64h + 8s, +8) for both operands, so each
-// lane reads 128 contiguous bytes of its row.
+// k-step; k-step s of half h is dims [64h + 8s, +8) for both operands.
 #include "kvs_internal.h"
 
 using namespace kvs;
@@ -26,121 +34,331 @@ using namespace kvs;
 namespace {
 
 constexpr int D = 128;
-constexpr int KS = D / 16;        // k-steps of the 32x32x16 MFMA
-constexpr int kRowsPerWG = 128;   // 4 waves x 32 rows (or columns)
-
-__device__ __forceinline__ void load_operand(const uint16_t* rowp, bool ok, int h, bf16x8* op) {
-  const u32x4* p = reinterpret_cast<const u32x4*>(rowp + 64 * h);
-#pragma unroll
-  for (int s = 0; s < KS; ++s) op[s] = __builtin_bit_cast(bf16x8, ok ? p[s] : u32x4{0u, 0u, 0u, 0u});
-}
+constexpr int KS = D / 16;          // k-steps of the 32x32x16 MFMA
+constexpr int kTile = 32;           // streamed rows per tile
+constexpr int kPerWave = 64;        // persistent rows per wave (two 32-row operands)
+constexpr int kPerWG = 4 * kPerWave;
+constexpr int kRowBytes = D * 2;
+constexpr int kLdsRow = kRowBytes + 16;   // padded LDS row: conflict-free 16-byte reads
+constexpr float kRebase = 0x1p60f;        // pass 1 rebases its reference past this tile sum
 
 // C layout of the 32x32 MFMA: lane l holds column l%32 and rows
 // 8*(v/4) + 4*(l/32) + (v%4) for v = 0..15.
 __device__ __forceinline__ int c_row(int v, int h) { return 8 * (v >> 2) + 4 * h + (v & 3); }
 
-__global__ __launch_bounds__(256) void meank_lse(const uint16_t* __restrict__ Q,
-                                                 const uint16_t* __restrict__ index, int H_kv, int G,
-                                                 int64_t Mq, int64_t nB, int64_t c0, int64_t c1,
-                                                 int64_t rows_pad, float scale_log2,
-                                                 float* __restrict__ lse2) {
-  const int lg = blockIdx.y;
+// Persistent operand straight from global memory: row `row` (zero if !ok).
+__device__ __forceinline__ void load_persistent(const uint16_t* base, int64_t row, bool ok, int h, bf16x8* op) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(base + (size_t)(ok ? row : 0) * D + 64 * h);
+#pragma unroll
+  for (int s = 0; s < KS; ++s) op[s] = __builtin_bit_cast(bf16x8, ok ? p[s] : u32x4{0u, 0u, 0u, 0u});
+}
+
+struct Stage {
+  u32x4 w[2];
+  float4 lse;
+};
+
+// Global -> registers for streamed tile rows [r0, r0+32) (rows >= limit are zero).
+template <bool WITH_LSE>
+__device__ __forceinline__ void stage_load(Stage& st, const uint16_t* base, int64_t r0, int64_t limit,
+                                           const float* lse) {
+  const int t = threadIdx.x;
+  const char* tile = reinterpret_cast<const char*>(base + (size_t)r0 * D);
+  if (r0 + kTile <= limit) {            // full tile: no per-row checks
+#pragma unroll
+    for (int i = 0; i < 2; ++i) st.w[i] = *reinterpret_cast<const u32x4*>(tile + (t + 256 * i) * 16);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = t + 256 * i;
+      st.w[i] = r0 + (idx >> 4) < limit ? *reinterpret_cast<const u32x4*>(tile + idx * 16)
+                                        : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  if (WITH_LSE && t < 8) st.lse = *reinterpret_cast<const float4*>(lse + r0 + 4 * t);
+}
+
+template <bool WITH_LSE>
+__device__ __forceinline__ void stage_store(const Stage& st, char* buf, float* lbuf) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int idx = t + 256 * i, row = idx >> 4, chunk = idx & 15;
+    *reinterpret_cast<u32x4*>(buf + row * kLdsRow + chunk * 16) = st.w[i];
+  }
+  if (WITH_LSE && t < 8) *reinterpret_cast<float4*>(lbuf + 4 * t) = st.lse;
+}
+
+__device__ __forceinline__ void read_streamed(const char* buf, int lane, bf16x8* A) {
+  const char* p = buf + (lane & 31) * kLdsRow + (lane >> 5) * 128;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) A[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p + 16 * s));
+}
+
+__device__ __forceinline__ void read_lse16(const float* lbuf, int h, float* l16) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const float4 v4 = *reinterpret_cast<const float4*>(lbuf + 8 * u + 4 * h);
+    l16[4 * u] = v4.x; l16[4 * u + 1] = v4.y; l16[4 * u + 2] = v4.z; l16[4 * u + 3] = v4.w;
+  }
+}
+
+__device__ __forceinline__ void mma2(const bf16x8* A, const bf16x8* B0, const bf16x8* B1, f32x16& c0,
+                                     f32x16& c1) {
+  c0 = f32x16{};
+  c1 = f32x16{};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], B0[s], c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], B1[s], c1, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ float tile_max(const f32x16& c) {
+  float t = fmaxf(fmaxf(c[0], c[1]), c[2]);
+#pragma unroll
+  for (int v = 3; v < 15; v += 2) t = fmaxf(fmaxf(t, c[v]), c[v + 1]);
+  return fmaxf(t, c[15]);
+}
+
+// Pins a value to this point of the instruction stream (an empty asm that
+// claims to read and rewrite it), so IR passes cannot sink the epilogue slice
+// below the MFMAs it is meant to overlap.
+#define KVS_PIN2(a, b) asm volatile("" : "+v"(a), "+v"(b))
+
+// One software-pipelined step: the 16 MFMAs of the next tile (cn = A x B) are
+// issued one at a time, each followed by a slice of the current tile's
+// epilogue (2 logits of each C tile), with scheduling barriers in between so
+// the matrix unit works while the wave's vector ALU runs the exp2 epilogue.
+// ref0/ref1 are the per-lane exponent references (pass 1: the running
+// reference of the lane's query row; pass 2: unused, the row lse2 in l16).
+template <bool PASS1>
+__device__ __forceinline__ void step_mma_epi(const bf16x8* A, const bf16x8* B0, const bf16x8* B1,
+                                             f32x16& cn0, f32x16& cn1, const f32x16& cc0,
+                                             const f32x16& cc1, float scale, const float* l16,
+                                             float ref0, float ref1, float& sum0, float& sum1) {
+  cn0 = f32x16{};
+  cn1 = f32x16{};
+  float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const float r00 = PASS1 ? ref0 : l16[2 * s], r01 = PASS1 ? ref0 : l16[2 * s + 1];
+    const float r10 = PASS1 ? ref1 : l16[2 * s], r11 = PASS1 ? ref1 : l16[2 * s + 1];
+    cn0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], B0[s], cn0, 0, 0, 0);
+    a0 += __builtin_amdgcn_exp2f(fmaf(cc0[2 * s], scale, -r00));
+    a1 += __builtin_amdgcn_exp2f(fmaf(cc0[2 * s + 1], scale, -r01));
+    KVS_PIN2(a0, a1);
+    __builtin_amdgcn_sched_barrier(0);
+    cn1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], B1[s], cn1, 0, 0, 0);
+    b0 += __builtin_amdgcn_exp2f(fmaf(cc1[2 * s], scale, -r10));
+    b1 += __builtin_amdgcn_exp2f(fmaf(cc1[2 * s + 1], scale, -r11));
+    KVS_PIN2(b0, b1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  sum0 = a0 + a1;
+  sum1 = b0 + b1;
+}
+
+// Pass-1 accumulation of one C tile's sum `a` taken against reference m.  The
+// reference only moves when a tile could overflow: then the tile is redone
+// against its exact max (rare; terms below 2^-126 of the reference are
+// negligible against the terms that set it).
+template <bool TAIL>
+__device__ __forceinline__ void lse_fold(const f32x16& c, float scale, float& m, float& s, float a,
+                                         int64_t b0, int h, int64_t c1) {
+  if (TAIL || !(a <= kRebase)) {
+    float x[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) x[v] = (TAIL && b0 + c_row(v, h) >= c1) ? -INFINITY : c[v];
+    float t = fmaxf(fmaxf(x[0], x[1]), x[2]);
+#pragma unroll
+    for (int v = 3; v < 15; v += 2) t = fmaxf(fmaxf(t, x[v]), x[v + 1]);
+    t = fmaxf(t, x[15]);
+    const float mn = fmaxf(fmaxf(m, t * scale), -3.0e38f);
+    a = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) a += __builtin_amdgcn_exp2f(fmaf(x[v], scale, -mn));
+    s = fmaf(s, __builtin_amdgcn_exp2f(m - mn), a);
+    m = mn;
+  } else {
+    s += a;
+  }
+}
+
+// blockIdx.x -> (lg, tile) so that one lg's tiles share an XCD (dispatch is
+// round-robin over the 8 XCDs).  Falls back to the plain order when LG % 8 != 0.
+__device__ __forceinline__ void xcd_map(int T, int LG, int& lg, int& tile) {
+  const int w = blockIdx.x;
+  if ((LG & 7) == 0) {
+    const int x = w & 7, j = w >> 3;
+    lg = x + 8 * (j / T);
+    tile = j % T;
+  } else {
+    lg = w / T;
+    tile = w % T;
+  }
+}
+
+template <bool PASS1>
+__global__ __launch_bounds__(256, 2) void meank_pass(const uint16_t* __restrict__ Q,
+                                                     const uint16_t* __restrict__ index, int LG,
+                                                     int64_t rows, int64_t rows_pad, int64_t nB,
+                                                     int64_t c0, int64_t c1, int T, float scale,
+                                                     float* __restrict__ lse2,
+                                                     float* __restrict__ colpart) {
+  __shared__ __attribute__((aligned(16))) char tiles[2][kTile * kLdsRow];
+  __shared__ __attribute__((aligned(16))) float lses[2][kTile];
+  int lg, tile;
+  xcd_map(T, LG, lg, tile);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 31, h = lane >> 5;
-  const int64_t rows = (int64_t)G * Mq;
-  const int64_t qrow = (int64_t)blockIdx.x * kRowsPerWG + wave * 32 + n;
   const uint16_t* Qg = Q + (size_t)lg * rows * D;
   const uint16_t* Ig = index + (size_t)lg * nB * D;
+  const float* Lg = lse2 + (size_t)lg * rows_pad;
 
-  bf16x8 Bq[KS];
-  load_operand(Qg + (size_t)(qrow < rows ? qrow : 0) * D, qrow < rows, h, Bq);
+  // persistent operand: pass 1 = query rows, pass 2 = index rows (block columns)
+  const int64_t p0 = (int64_t)tile * kPerWG + wave * kPerWave;
+  bf16x8 B0[KS], B1[KS];
+  if (PASS1) {
+    load_persistent(Qg, p0 + n, p0 + n < rows, h, B0);
+    load_persistent(Qg, p0 + 32 + n, p0 + 32 + n < rows, h, B1);
+  } else {
+    load_persistent(Ig, c0 + p0 + n, c0 + p0 + n < c1, h, B0);
+    load_persistent(Ig, c0 + p0 + 32 + n, c0 + p0 + 32 + n < c1, h, B1);
+  }
+  // streamed operand: pass 1 = index tiles over [c0, c1), pass 2 = query tiles over [0, rows)
+  const uint16_t* sbase = PASS1 ? Ig : Qg;
+  const int64_t s_begin = PASS1 ? c0 : 0, s_end = PASS1 ? c1 : rows;
+  const int nt = (int)((s_end - s_begin + kTile - 1) / kTile);
 
-  float m = -INFINITY, ssum = 0.f;
-  bf16x8 A[KS], An[KS];
-  load_operand(Ig + (size_t)min(c0 + n, c1 - 1) * D, c0 + n < c1, h, A);
-  for (int64_t cb = c0; cb < c1; cb += 32) {
-    const int64_t nb = cb + 32 + n;
-    if (cb + 32 < c1) load_operand(Ig + (size_t)min(nb, c1 - 1) * D, nb < c1, h, An);
-    f32x16 c = {};
+  Stage st;
+  stage_load<!PASS1>(st, sbase, s_begin, s_end, Lg);
+  stage_store<!PASS1>(st, tiles[0], lses[0]);
+  if (nt > 1) {
+    stage_load<!PASS1>(st, sbase, s_begin + kTile, s_end, Lg);
+    stage_store<!PASS1>(st, tiles[1], lses[1]);
+  }
+  __syncthreads();
+
+  bf16x8 A[KS];
+  f32x16 cA0, cA1, cB0, cB1;          // ping-pong accumulators (tile t and t+1)
+  float lA[16], lB[16];               // pass 2: lse2 of the rows of tile t and t+1
+  read_streamed(tiles[0], lane, A);
+  if (!PASS1) read_lse16(lses[0], h, lA);
+  mma2(A, B0, B1, cA0, cA1);
+  __syncthreads();
+
+  // pass 1: running reference and sum per persistent row; pass 2: column sums
+  float m0, m1, s0 = 0.f, s1 = 0.f;
+  if (PASS1) {
+    // the first tile may also be the partial last one: mask its padding columns
+    f32x16 x0 = cA0, x1 = cA1;
+    if (nt == 1) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], Bq[s], c, 0, 0, 0);
-    float x[16];
-    float tmax = -INFINITY;
+      for (int v = 0; v < 16; ++v)
+        if (s_begin + c_row(v, h) >= c1) { x0[v] = -INFINITY; x1[v] = -INFINITY; }
+    }
+    m0 = fmaxf(tile_max(x0) * scale, -3.0e38f);
+    m1 = fmaxf(tile_max(x1) * scale, -3.0e38f);
+    m0 = fmaxf(m0, __shfl_xor(m0, 32, kWave));        // both halves share the row's reference
+    m1 = fmaxf(m1, __shfl_xor(m1, 32, kWave));
+  }
+
+  // Process tile t (accumulators cc, lse lc) while issuing tile t+1 into cn.
+  auto body = [&](int t, f32x16& cc0, f32x16& cc1, float* lc, f32x16& cn0, f32x16& cn1, float* ln) {
+    const bool pre = t + 2 < nt;
+    if (pre) stage_load<!PASS1>(st, sbase, s_begin + (int64_t)(t + 2) * kTile, s_end, Lg);
+    read_streamed(tiles[(t + 1) & 1], lane, A);
+    if (!PASS1) read_lse16(lses[(t + 1) & 1], h, ln);
+    float a0, a1;
+    step_mma_epi<PASS1>(A, B0, B1, cn0, cn1, cc0, cc1, scale, lc, m0, m1, a0, a1);
+    if (PASS1) {
+      // rebase only when some lane's tile sum could overflow (wave-uniform, rare)
+      if (__builtin_expect(__ballot(!(a0 <= kRebase) || !(a1 <= kRebase)) != 0, 0)) {
+        lse_fold<false>(cc0, scale, m0, s0, a0, 0, h, c1);
+        lse_fold<false>(cc1, scale, m1, s1, a1, 0, h, c1);
+      } else {
+        s0 += a0;
+        s1 += a1;
+      }
+    } else {
+      s0 += a0;
+      s1 += a1;
+    }
+    if (pre) stage_store<!PASS1>(st, tiles[t & 1], lses[t & 1]);
+    __syncthreads();
+  };
+
+  int t = 0;
+  for (; t + 2 < nt; t += 2) {
+    body(t, cA0, cA1, lA, cB0, cB1, lB);
+    body(t + 1, cB0, cB1, lB, cA0, cA1, lA);
+  }
+  f32x16* last0 = &cA0;
+  f32x16* last1 = &cA1;
+  float* llast = lA;
+  if (t + 1 < nt) {
+    body(t, cA0, cA1, lA, cB0, cB1, lB);
+    last0 = &cB0;
+    last1 = &cB1;
+    llast = lB;
+  }
+  // last tile (the only one that can be partial)
+  if (PASS1) {
+    const int64_t b0 = s_begin + (int64_t)(nt - 1) * kTile;
+    lse_fold<true>(*last0, scale, m0, s0, 0.f, b0, h, c1);
+    lse_fold<true>(*last1, scale, m1, s1, 0.f, b0, h, c1);
+  } else {
+    float a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      x[v] = cb + c_row(v, h) < c1 ? c[v] * scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, x[v]);
+      a0 += __builtin_amdgcn_exp2f(fmaf((*last0)[v], scale, -llast[v]));
+      a1 += __builtin_amdgcn_exp2f(fmaf((*last1)[v], scale, -llast[v]));
     }
-    if (tmax != -INFINITY) {
-      const float mn = fmaxf(m, tmax);
-      float add = 0.f;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) add += __builtin_amdgcn_exp2f(x[v] - mn);
-      ssum = ssum * __builtin_amdgcn_exp2f(m - mn) + add;
-      m = mn;
-    }
-#pragma unroll
-    for (int s = 0; s < KS; ++s) A[s] = An[s];
+    s0 += a0;
+    s1 += a1;
   }
-  const float m2 = __shfl_xor(m, 32, kWave);
-  const float s2 = __shfl_xor(ssum, 32, kWave);
-  lse_merge(m, ssum, m2, s2);
-  if (h == 0 && qrow < rows_pad)
-    lse2[(size_t)lg * rows_pad + qrow] = (qrow < rows && ssum > 0.f) ? m + log2f(ssum) : INFINITY;
+
+  if (PASS1) {
+    float mm = __shfl_xor(m0, 32, kWave), ss = __shfl_xor(s0, 32, kWave);
+    lse_merge(m0, s0, mm, ss);
+    mm = __shfl_xor(m1, 32, kWave);
+    ss = __shfl_xor(s1, 32, kWave);
+    lse_merge(m1, s1, mm, ss);
+    if (h == 0) {
+      const int64_t r0 = p0 + n, r1 = p0 + 32 + n;
+      if (r0 < rows_pad) lse2[(size_t)lg * rows_pad + r0] = (r0 < rows && s0 > 0.f) ? m0 + log2f(s0) : INFINITY;
+      if (r1 < rows_pad) lse2[(size_t)lg * rows_pad + r1] = (r1 < rows && s1 > 0.f) ? m1 + log2f(s1) : INFINITY;
+    }
+  } else {
+    s0 += __shfl_xor(s0, 32, kWave);
+    s1 += __shfl_xor(s1, 32, kWave);
+    if (h == 0) {
+      const int64_t b0 = c0 + p0 + n, b1 = c0 + p0 + 32 + n;
+      if (b0 < c1) colpart[(size_t)lg * nB + b0] = s0;
+      if (b1 < c1) colpart[(size_t)lg * nB + b1] = s1;
+    }
+  }
 }
 
-__global__ __launch_bounds__(256) void meank_colsum(const uint16_t* __restrict__ Q,
-                                                    const uint16_t* __restrict__ index, int G,
-                                                    int64_t Mq, int64_t nB, int64_t c0, int64_t c1,
-                                                    int64_t rows_pad, float scale_log2,
-                                                    const float* __restrict__ lse2,
-                                                    float* __restrict__ colpart) {
-  const int lg = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n = lane & 31, h = lane >> 5;
-  const int64_t rows = (int64_t)G * Mq;
-  const int64_t col = c0 + (int64_t)blockIdx.x * kRowsPerWG + wave * 32 + n;
-  const uint16_t* Qg = Q + (size_t)lg * rows * D;
-  const uint16_t* Ig = index + (size_t)lg * nB * D;
-  const float* L2 = lse2 + (size_t)lg * rows_pad;
-
-  bf16x8 Bi[KS];
-  load_operand(Ig + (size_t)(col < c1 ? col : c0) * D, col < c1, h, Bi);
-
-  float acc = 0.f;
-  bf16x8 A[KS], An[KS];
-  load_operand(Qg + (size_t)min<int64_t>(n, rows - 1) * D, n < rows, h, A);
-  for (int64_t r0 = 0; r0 < rows; r0 += 32) {
-    const int64_t nr = r0 + 32 + n;
-    if (r0 + 32 < rows) load_operand(Qg + (size_t)min(nr, rows - 1) * D, nr < rows, h, An);
-    f32x16 c = {};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], Bi[s], c, 0, 0, 0);
-    // rows r0 + 8u + 4h + 0..3 for u = 0..3 (padding rows hold +inf)
-    const float4* lp = reinterpret_cast<const float4*>(L2 + r0 + 4 * h);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float4 ls = lp[2 * u];
-      acc += __builtin_amdgcn_exp2f(fmaf(c[4 * u + 0], scale_log2, -ls.x));
-      acc += __builtin_amdgcn_exp2f(fmaf(c[4 * u + 1], scale_log2, -ls.y));
-      acc += __builtin_amdgcn_exp2f(fmaf(c[4 * u + 2], scale_log2, -ls.z));
-      acc += __builtin_amdgcn_exp2f(fmaf(c[4 * u + 3], scale_log2, -ls.w));
-    }
-#pragma unroll
-    for (int s = 0; s < KS; ++s) A[s] = An[s];
-  }
-  acc += __shfl_xor(acc, 32, kWave);
-  if (h == 0 && col < c1) colpart[(size_t)lg * nB + col] = acc;
-}
-
+// R_b = sum over (l, g) of the partials, fixed order, / (L * H_q).  A workgroup
+// owns 64 blocks; wave w sums lg = w, w+4, ... and the 4 waves combine in order.
 __global__ __launch_bounds__(256) void meank_reduce(const float* __restrict__ colpart, int LG,
-                                                    int64_t nB, int64_t c0, int64_t c1, float LH, float* __restrict__ R) {
-  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (b >= nB) return;
-  if (b < c0 || b >= c1) { R[b] = 0.f; return; }
+                                                    int64_t nB, int64_t c0, int64_t c1, float LH,
+                                                    float* __restrict__ R) {
+  __shared__ float part[4][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t b = (int64_t)blockIdx.x * 64 + lane;
+  const bool cand = b >= c0 && b < c1;
   float s = 0.f;
-  for (int lg = 0; lg < LG; ++lg) s += colpart[(size_t)lg * nB + b];
-  R[b] = s / LH;
+  if (cand) {
+#pragma unroll 8
+    for (int lg = wave; lg < LG; lg += 4) s += colpart[(size_t)lg * nB + b];
+  }
+  part[wave][lane] = s;
+  __syncthreads();
+  if (wave == 0 && b < nB)
+    R[b] = cand ? (((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane]) / LH : 0.f;
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -164,22 +382,24 @@ hipError_t kvs_launch_meank_score(const void* Q, const void* index, int L, int H
   char* w = static_cast<char*>(ws);
   float* lse2 = reinterpret_cast<float*>(w);
   float* colpart = reinterpret_cast<float*>(w + align256((size_t)LG * rows_pad * 4));
-  const float scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)D));
+  const float scale = (float)(1.4426950408889634 / __builtin_sqrt((double)D));
   const uint16_t* Qb = static_cast<const uint16_t*>(Q);
   const uint16_t* Ib = static_cast<const uint16_t*>(index);
   if (c1 > c0 && rows > 0) {
-    hipLaunchKernelGGL(meank_lse, dim3(ceil_div(rows_pad, kRowsPerWG), LG), dim3(256), 0, st, Qb, Ib,
-                       H_kv, G, Mq, nB, c0, c1, rows_pad, scale_log2, lse2);
+    const int T1 = (int)ceil_div(rows_pad, kPerWG);
+    hipLaunchKernelGGL((meank_pass<true>), dim3((unsigned)T1 * LG), dim3(256), 0, st, Qb, Ib, LG, rows,
+                       rows_pad, nB, c0, c1, T1, scale, lse2, colpart);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(meank_colsum, dim3(ceil_div(c1 - c0, kRowsPerWG), LG), dim3(256), 0, st, Qb,
-                       Ib, G, Mq, nB, c0, c1, rows_pad, scale_log2, lse2, colpart);
+    const int T2 = (int)ceil_div(c1 - c0, kPerWG);
+    hipLaunchKernelGGL((meank_pass<false>), dim3((unsigned)T2 * LG), dim3(256), 0, st, Qb, Ib, LG, rows,
+                       rows_pad, nB, c0, c1, T2, scale, lse2, colpart);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   } else {
     c1 = c0;   // no candidates (or no queries): every R_b is 0
   }
-  hipLaunchKernelGGL(meank_reduce, dim3(ceil_div(nB, 256)), dim3(256), 0, st, colpart, LG, nB, c0, c1,
+  hipLaunchKernelGGL(meank_reduce, dim3(ceil_div(nB, 64)), dim3(256), 0, st, colpart, LG, nB, c0, c1,
                      (float)(L * H_q), R);
   return hipGetLastError();
 }

@@ -1,0 +1,316 @@
+"""Benchmark: one step = the whole hot path on one GPU, inputs resident in HBM.
+
+A step is an IntentKV turn on the rule-mode cache (QueryMemory update, rule
+score, top-k with the forced set, slot redirect) followed by a KVMEM agent step
+on the Mean-K workspace (index build from raw K, block scoring, sink/recent +
+budget selection, re-RoPE scatter of the selected K/V blocks into the pool).
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload rule-8b+meank-256k]
+
+Prints one JSON line.  `value` counts K-cache tokens scored per second over the
+whole step (the rule cache's N plus the Mean-K workspace's N).  Per-call times
+come from HIP events on the stream the library launches on; `roofline` is the
+call with the largest share of the step, priced against MI355X's published
+peaks; `cpu_baseline` times the float64 oracle on a bounded sample of the same
+workload and scales it linearly to a whole step.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from attention_space_retrieval_amd import kvs, workloads as W  # noqa: E402
+
+METRIC = "K-cache tokens scored/s + HBM GB/s (rule+top-k); Mean-K scoring TFLOP/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+WORKLOADS = {"rule-8b+meank-256k": ("rule-8b", "meank-256k"),
+             "rule-14b+meank-1m": ("rule-14b", "meank-1m")}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Setup:
+    """Device-resident inputs, outputs and workspaces for one step."""
+
+    def __init__(self, rule_name, meank_name, dev):
+        self.dev = dev
+        c = self.rc = W.config(rule_name)
+        inp = W.rule_inputs(c, dev)
+        self.K = inp["K"]
+        self.spans = inp["spans"]
+        self.slots = inp["slots"]
+        self.M = torch.empty((c["L"], c["H_q"], c["D"]), dtype=torch.float32, device=dev)
+        for t, q in enumerate(self.spans[:-1]):          # earlier turns build the session state
+            kvs.kvs_qmem_update(q, c["lam"], self.M, t == 0)
+        self.rule = torch.empty(c["N"], dtype=torch.float32, device=dev)
+        self.ws_rule = torch.empty(kvs.kvs_rule_score_workspace(c["L"], c["H_q"], c["H_kv"], c["N"]),
+                                   dtype=torch.uint8, device=dev)
+        self.keep_r = torch.empty(c["N"], dtype=torch.uint8, device=dev)
+        self.idx_r = torch.empty(c["N"], dtype=torch.int32, device=dev)
+        self.nk_r = torch.empty(1, dtype=torch.int64, device=dev)
+        self.slots_out = torch.empty_like(self.slots)
+
+        m = self.mc = W.config(meank_name)
+        self.nB = m["N"] // 32
+        mi = W.meank_inputs(m, dev, with_k=True, with_v=not m.get("staging"))
+        self.Kraw, self.Q = mi["K"], mi["Q"]
+        self.n_sel = min(m["budget"], self.nB)
+        if m.get("staging"):
+            # packed staging buffers stand in for the host->device batch of selected blocks
+            shp = (m["L"], m["H_kv"], 32 * self.n_sel, m["D"])
+            self.k_src = W.normal(shp, m["seed"], W.T_K + 10, "bf16", dev)
+            self.v_src = W.normal(shp, m["seed"], W.T_V + 10, "bf16", dev)
+            self.src_block = torch.arange(self.n_sel, dtype=torch.int32, device=dev)
+            self.page_table = W.page_permutation(self.n_sel, self.n_sel, m["seed"]).to(dev)
+        else:
+            self.k_src, self.v_src = self.Kraw, mi["V"]
+            self.src_block = None                        # the selection itself
+            self.page_table = None
+        self.index = torch.empty((m["L"], m["H_kv"], self.nB, m["D"]), dtype=torch.bfloat16, device=dev)
+        self.R = torch.empty(self.nB, dtype=torch.float32, device=dev)
+        self.ws_mk = torch.empty(kvs.kvs_meank_score_workspace(m["L"], m["H_q"], m["H_kv"], m["Mq"], self.nB),
+                                 dtype=torch.uint8, device=dev)
+        self.keep_m = torch.empty(self.nB, dtype=torch.uint8, device=dev)
+        self.idx_m = torch.empty(self.nB, dtype=torch.int32, device=dev)
+        self.nk_m = torch.empty(1, dtype=torch.int64, device=dev)
+        pool = (m["L"], m["H_kv"], 32 * self.n_sel, m["D"])
+        self.k_pool = torch.empty(pool, dtype=torch.bfloat16, device=dev)
+        self.v_pool = torch.empty(pool, dtype=torch.bfloat16, device=dev)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+
+    # (name, callable) in step order
+    def calls(self):
+        c, m = self.rc, self.mc
+        nB = self.nB
+        src = self.src_block if self.src_block is not None else self.idx_m[: self.n_sel]
+        return [
+            ("kvs_qmem_update", lambda: kvs.kvs_qmem_update(self.spans[-1], c["lam"], self.M, False)),
+            ("kvs_rule_score", lambda: kvs.kvs_rule_score(self.K, self.M, c["pi"], c["q_s"], c["q_e"],
+                                                          rule=self.rule, ws=self.ws_rule)),
+            ("kvs_topk_select[rule]", lambda: kvs.kvs_topk_select(
+                self.rule, (0, c["pi"]), (c["q_s"], c["q_e"]), c["C"], self.keep_r, self.idx_r, self.nk_r)),
+            ("kvs_slotmap_redirect", lambda: kvs.kvs_slotmap_redirect(self.slots, self.keep_r, c["dead_slot"],
+                                                                      self.slots_out)),
+            ("kvs_meank_build", lambda: kvs.kvs_meank_build(self.Kraw, index=self.index)),
+            ("kvs_meank_score", lambda: kvs.kvs_meank_score(self.Q, self.index, m["n_sink"], m["n_recent"],
+                                                            R=self.R, ws=self.ws_mk)),
+            ("kvs_topk_select[meank]", lambda: kvs.kvs_topk_select(
+                self.R, (0, m["n_sink"]), (nB - m["n_recent"], nB), m["budget"], self.keep_m, self.idx_m,
+                self.nk_m)),
+            ("kvs_rerope_scatter", lambda: kvs.kvs_rerope_scatter(
+                self.k_src, self.v_src, src, self.page_table, self.n_sel, m["pos_base"], m["theta"],
+                self.k_pool, self.v_pool, self.err)),
+        ]
+
+    def work(self):
+        """Algorithmic bytes or flops of each call (what the method must move or compute)."""
+        c, m = self.rc, self.mc
+        N, nB = c["N"], self.nB
+        LG_r = c["L"] * c["H_kv"]
+        blk = m["L"] * m["H_kv"] * 32 * m["D"] * 2           # bytes of one 32-token block over all heads
+        cand = nB - m["n_sink"] - m["n_recent"]
+        return {
+            "kvs_qmem_update": ("hbm", c["L"] * c["H_q"] * c["span"] * c["D"] * 2 + 2 * c["L"] * c["H_q"] * c["D"] * 4),
+            "kvs_rule_score": ("hbm", LG_r * N * c["D"] * 2 + c["L"] * c["H_q"] * c["D"] * 4 + 4 * N),
+            "kvs_topk_select[rule]": ("hbm", 4 * N + N + 4 * c["C"]),
+            "kvs_slotmap_redirect": ("hbm", 17 * N),
+            "kvs_meank_build": ("hbm", m["L"] * m["H_kv"] * m["N"] * m["D"] * 2 + m["L"] * m["H_kv"] * nB * m["D"] * 2),
+            "kvs_meank_score": ("mfma", 2.0 * m["Mq"] * m["H_q"] * m["L"] * cand * m["D"]),
+            "kvs_topk_select[meank]": ("hbm", 4 * nB + nB + 4 * m["budget"]),
+            "kvs_rerope_scatter": ("hbm", 4 * self.n_sel * blk),
+        }
+
+
+def run_gpu(s, steps, warmup, only=None):
+    calls = s.calls()
+    if only:
+        calls = [c for c in calls if c[0] in only]
+    for _ in range(warmup):
+        for _, f in calls:
+            f()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        ev[k][0].record(stream)
+        for i, (_, f) in enumerate(calls):
+            f()
+            ev[k][i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    times = {name: [ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(steps)]
+             for i, (name, _) in enumerate(calls)}
+    per_call = {name: float(np.mean(v)) for name, v in times.items()}
+    spread = {name: (float(np.min(v)), float(np.max(v))) for name, v in times.items()}
+    assert int(s.err.item()) == 0, "scatter reported an out-of-range block"
+    return wall, per_call, spread
+
+
+def cpu_baseline(s):
+    """The float64 oracle on a bounded sample of the same inputs, scaled to one step."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"), default=1)
+    except Exception:                                    # pragma: no cover
+        blas = 1
+
+    def bits(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    c, m = s.rc, s.mc
+    L_r = min(4, c["L"])
+    lg_m = 16
+    blocks = 64
+    t = {}
+    K = bits(s.K[:L_r])
+    Mo = None
+    for q in s.spans[:-1]:                               # the oracle's own session state
+        Mo = oracle.qmem_update(bits(q), c["lam"], Mo)
+    t0 = time.perf_counter()
+    Mo = oracle.qmem_update(bits(s.spans[-1]), c["lam"], Mo)
+    t["qmem"] = time.perf_counter() - t0
+    M = Mo[:L_r]
+    t0 = time.perf_counter()
+    rule = oracle.rule_score(K, M, c["pi"], c["q_s"], c["q_e"])
+    t["rule"] = (time.perf_counter() - t0) * c["L"] / L_r
+    t0 = time.perf_counter()
+    keep, _, _ = oracle.topk_select(rule, (0, c["pi"]), (c["q_s"], c["q_e"]), c["C"])
+    oracle.slotmap_redirect(s.slots.cpu().numpy(), keep, c["dead_slot"])
+    t["topk_slot"] = time.perf_counter() - t0
+    # Mean-K on lg_m (layer, KV head) pairs of layer 0 and 1
+    G = m["H_q"] // m["H_kv"]
+    LG = m["L"] * m["H_kv"]
+    pairs = [(p // m["H_kv"], p % m["H_kv"]) for p in range(lg_m)]
+    t0 = time.perf_counter()
+    idx = [oracle.meank_build(bits(s.Kraw[l, g])[None, None])[0] for l, g in pairs]
+    t["build"] = (time.perf_counter() - t0) * LG / lg_m
+    t0 = time.perf_counter()
+    R = np.zeros(s.nB)
+    for (l, g), ix in zip(pairs, idx):
+        R += oracle.meank_score(bits(s.Q[l, g * G:(g + 1) * G])[None], ix, m["n_sink"], m["n_recent"])
+    t["score"] = (time.perf_counter() - t0) * LG / lg_m
+    t0 = time.perf_counter()
+    sel, _, _ = oracle.meank_select(R, m["n_sink"], m["n_recent"], m["budget"])
+    t["select"] = time.perf_counter() - t0
+    l, g = pairs[0]
+    ks = bits(s.k_src[l, g])[None, None]
+    vs = bits(s.v_src[l, g])[None, None]
+    src = sel[:blocks] if s.src_block is None else np.arange(blocks)
+    t0 = time.perf_counter()
+    for _ in range(lg_m):
+        oracle.rerope_scatter(ks, vs, src, None, m["pos_base"], m["theta"],
+                              np.zeros((1, 1, 32 * blocks, m["D"])), np.zeros((1, 1, 32 * blocks, m["D"]), np.uint16))
+    t["scatter"] = (time.perf_counter() - t0) * (LG / lg_m) * (s.n_sel / blocks)
+    step = sum(t.values())
+    tokens = c["N"] + m["N"]
+    return {
+        "value": tokens / step, "unit": "K-cache tokens/s", "cores": blas, "kind": "oracle",
+        "sample": (f"float64 oracle on the same input bits: rule score over {L_r} of {c['L']} layers, "
+                   f"Mean-K build and score over {lg_m} of {LG} (layer, KV head) pairs, re-RoPE scatter of "
+                   f"{blocks} of {s.n_sel} blocks on {lg_m} pairs; each part scaled linearly to the full step "
+                   f"({step:.1f} s extrapolated). BLAS threads = cores; elementwise numpy is single-threaded."),
+        "seconds_per_step_extrapolated": step,
+        "parts_s": {k: round(v, 3) for k, v in t.items()},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="rule-8b+meank-256k", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None,
+                    help="comma-separated call names to time alone (profiling; not a headline figure)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run one 4 GiB device copy (for HBM counter scaling)")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the scoring path has no multi-GPU mode in this build "
+              "(sharding by (layer, KV head) is a design note). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    dev = "cuda:0"
+    rule_name, meank_name = WORKLOADS[a.workload]
+    log(f"[bench] setting up {a.workload}")
+    s = Setup(rule_name, meank_name, dev)
+    log(f"[bench] warmup {a.warmup}, timing {a.steps} steps")
+    only = set(a.only.split(",")) if a.only else None
+    wall, per_call, spread = run_gpu(s, a.steps, a.warmup, only)
+    if only:
+        print(json.dumps({"only": sorted(only), "ms_per_step": 1000.0 * wall / a.steps, "calls_ms": per_call,
+                          "calls_ms_min_max": spread}))
+        return
+    ms_per_step = 1000.0 * wall / a.steps
+    if a.copy_calibration:
+        x = torch.empty(1 << 31, dtype=torch.int16, device=dev)
+        y = torch.empty_like(x)
+        y.copy_(x)
+        torch.cuda.synchronize()
+        del x, y
+    c, m = s.rc, s.mc
+    tokens = c["N"] + m["N"]
+    work = s.work()
+    rows = {}
+    for name, ms in per_call.items():
+        bound, amount = work[name]
+        if bound == "hbm":
+            ach, peak, unit = amount / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
+        else:
+            ach, peak, unit = amount / (ms * 1e-3) / 1e12, BF16_PEAK_TFLOPS, "TFLOP/s"
+        rows[name] = {"ms": round(ms, 4), "ms_min": round(spread[name][0], 4), "ms_max": round(spread[name][1], 4),
+                      "bound": bound, "achieved": round(ach, 2), "peak": peak,
+                      "unit": unit, "frac": round(ach / peak, 4),
+                      "per_launch": amount}
+    dom = max(rows, key=lambda k: rows[k]["ms"])
+    d = rows[dom]
+    kernels = {"kvs_rule_score": "rule_logits_mfma + rule_lse_merge + rule_colsum",
+               "kvs_meank_score": "meank_lse + meank_colsum + meank_reduce",
+               "kvs_meank_build": "meank_build_raw", "kvs_rerope_scatter": "rerope_scatter_kernel"}
+    rule_ms = sum(per_call[k] for k in ("kvs_qmem_update", "kvs_rule_score", "kvs_topk_select[rule]",
+                                         "kvs_slotmap_redirect"))
+    rule_bytes = sum(work[k][1] for k in ("kvs_qmem_update", "kvs_rule_score", "kvs_topk_select[rule]",
+                                          "kvs_slotmap_redirect"))
+    out = {
+        "metric": METRIC,
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "K-cache tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": a.workload, "rule": {k: c[k] for k in ("L", "H_q", "H_kv", "D", "N", "pi", "q_s", "q_e", "C", "lam")},
+                   "meank": {k: m[k] for k in ("L", "H_q", "H_kv", "D", "N", "Mq", "n_sink", "n_recent", "budget", "theta")},
+                   "tokens_per_step": tokens},
+        "roofline": {"call": dom, "kernels": kernels.get(dom, dom), "bound": d["bound"],
+                     "achieved": d["achieved"], "peak": d["peak"], "unit": d["unit"], "frac": d["frac"],
+                     "traffic": None},
+        "rule_turn": {"ms": round(rule_ms, 4), "tokens_per_s": c["N"] / (rule_ms * 1e-3),
+                      "hbm_gbps": rule_bytes / (rule_ms * 1e-3) / 1e9,
+                      "frac_hbm_peak": rule_bytes / (rule_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "meank_score_tflops": rows["kvs_meank_score"]["achieved"],
+        "calls": rows,
+    }
+    if not a.no_cpu_baseline:
+        log("[bench] timing the oracle on a bounded CPU sample")
+        out["cpu_baseline"] = cpu_baseline(s)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
