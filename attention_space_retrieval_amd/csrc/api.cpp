@@ -56,7 +56,7 @@ int32_t kvs_version(void) { return 100; }
 
 kvs_status kvs_qmem_update(const void* q_span, int32_t q_dtype, int32_t L, int32_t H_q, int32_t S,
                            int32_t D, float lambda, int32_t first_turn, float* M, void* stream) {
-  if (!q_span || !M) return KVS_ERR_ARG;
+  if (!q_span || !M || !a16(q_span)) return KVS_ERR_ARG;
   if (q_dtype != KVS_F32 && q_dtype != KVS_BF16) return KVS_ERR_DTYPE;
   if (L < 1 || H_q < 1 || S < 1 || std::isnan(lambda) || lambda < 0.f) return KVS_ERR_ARG;
   if (!head_dim_ok(D)) return KVS_ERR_UNSUPPORTED;
@@ -68,7 +68,7 @@ kvs_status kvs_qmem_update(const void* q_span, int32_t q_dtype, int32_t L, int32
 
 size_t kvs_rule_score_workspace(int32_t L, int32_t H_q, int32_t H_kv, int64_t N) {
   if (L < 1 || H_q < 1 || H_kv < 1 || N < 0 || N > kMaxIndex) return 0;
-  return kvs_rule_ws_bytes(L, H_q, N);
+  return kvs_rule_ws_bytes(L, H_q, H_kv, N);
 }
 
 kvs_status kvs_rule_score(const void* K, int32_t k_dtype, const float* M, int32_t L, int32_t H_q,
@@ -82,7 +82,7 @@ kvs_status kvs_rule_score(const void* K, int32_t k_dtype, const float* M, int32_
     return KVS_ERR_SHAPE;
   if (!head_dim_ok(D) || H_q / H_kv > 16) return KVS_ERR_UNSUPPORTED;
   if (N == 0) return KVS_OK;
-  const size_t need = kvs_rule_ws_bytes(L, H_q, N);
+  const size_t need = kvs_rule_ws_bytes(L, H_q, H_kv, N);
   if (!ws || ws_bytes < need || !a16(ws)) return KVS_ERR_WORKSPACE;
   pi = pi > N ? N : pi;
   int64_t s = q_s, e = q_e;

@@ -2,12 +2,8 @@
 // attention trigger and Mean-K model-native retrieval"): one mean of
 // position-free K per 32-token block, per layer and KV head.
 //
-// HBM-bound stream of K (read once) plus a 1/32-size write.  A wavefront
-// reduces one block at a time: D/8 lanes cover a 2*D-byte row with 16-byte
-// loads, so one load instruction covers 64/(D/8) rows and 32 rows take 8
-// (D=128) coalesced loads.  Sums are float32 in a fixed order (per lane over
-// its rows, then a butterfly over the row groups), the mean is rounded to bf16
-// nearest-even.
+// HBM-bound stream of K (read once) plus a 1/32-size write.  Sums are float32
+// in a fixed order and the mean is rounded to bf16 nearest-even.
 //
 // De-RoPE mode: the keys carry RoPE at positions pos0 + i.  A workgroup owns
 // one token block for every (layer, KV head); it builds that block's 32 x D/2
@@ -20,44 +16,68 @@ using namespace kvs;
 namespace {
 
 constexpr int kBlk = 32;
-constexpr int kBlocksPerWave = 8;
 
-template <int D>
+// Raw mode.  A wavefront reduces 64*8/D blocks at once: lane (j, c) owns
+// 16-byte column chunk c of block j and sums all 32 rows of it in-lane, so the
+// mean needs no cross-lane traffic; every load instruction still moves whole
+// 256-byte rows.  Waves take their block groups in grid-stride order (the
+// resident waves read one contiguous stretch of K at a time) and keep the next
+// 8 rows' loads in flight while adding the current ones.  K is read once, in
+// whole 256-byte rows, with non-temporal loads (streaming reads of whole rows
+// run closest to the HBM peak).  When N is a multiple
+// of 32 the blocks of all (layer, head) slices are contiguous and addressed
+// linearly; otherwise the block's slice and row count are derived per lane.
+template <int D, bool LINEAR>
 __global__ __launch_bounds__(256) void meank_build_raw(const uint16_t* __restrict__ K, int64_t N,
                                                        int64_t nB, int64_t total_blocks,
                                                        uint16_t* __restrict__ index) {
-  constexpr int LPR = D / 8, RPL = 64 / LPR, LOADS = kBlk / RPL;
+  constexpr int LPR = D / 8, BPW = 64 / LPR;   // lanes per row, blocks per wave
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int cl = lane % LPR, rr = lane / LPR;
-  const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
-  for (int it = 0; it < kBlocksPerWave; ++it) {
-    const int64_t gb = gw * kBlocksPerWave + it;
-    if (gb >= total_blocks) return;
-    const int64_t lg = gb / nB, b = gb - lg * nB;
-    const int64_t t0 = b * kBlk;
-    const int nb = (int)min<int64_t>(kBlk, N - t0);
-    const uint16_t* src = K + ((size_t)lg * N + t0) * D + cl * 8;
-    u32x4 w[LOADS];
-#pragma unroll
-    for (int ld = 0; ld < LOADS; ++ld) {
-      const int t = ld * RPL + rr;
-      w[ld] = t < nb ? *reinterpret_cast<const u32x4*>(src + (size_t)t * D) : u32x4{0u, 0u, 0u, 0u};
+  const int cl = lane % LPR, j = lane / LPR;
+  const int64_t stride = (int64_t)gridDim.x * 4 * BPW;
+  for (int64_t g0 = ((int64_t)blockIdx.x * 4 + wave) * BPW; g0 < total_blocks; g0 += stride) {
+    const int64_t gb = g0 + j;
+    const bool ok = gb < total_blocks;
+    int nb = kBlk;
+    const uint16_t* src;
+    if (LINEAR) {
+      src = K + (size_t)(ok ? gb : 0) * kBlk * D + cl * 8;
+    } else {
+      const int64_t g = ok ? gb : 0, lg = g / nB, b = g - lg * nB;
+      nb = (int)min<int64_t>(kBlk, N - b * kBlk);
+      src = K + ((size_t)lg * N + (size_t)b * kBlk) * D + cl * 8;
     }
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    u32x4 w[8];
 #pragma unroll
-    for (int ld = 0; ld < LOADS; ++ld) {
-      float x[8];
-      unpack8(w[ld], x);
+    for (int r = 0; r < 8; ++r)
+      w[r] = (LINEAR || r < nb) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t)r * D))
+                                : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += x[e];
+    for (int r0 = 8; r0 <= kBlk; r0 += 8) {
+      u32x4 wn[8];
+      if (r0 < kBlk) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+          wn[r] = (LINEAR || r0 + r < nb)
+                      ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t)(r0 + r) * D))
+                      : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        float x[8];
+        unpack8(w[r], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += x[e];
+      }
+      if (r0 < kBlk) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) w[r] = wn[r];
+      }
     }
+    if (ok) {
 #pragma unroll
-    for (int o = LPR; o < 64; o <<= 1)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o, kWave);
-    if (rr == 0) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = nb == kBlk ? acc[e] * (1.f / kBlk) : acc[e] / (float)nb;
+      for (int e = 0; e < 8; ++e) acc[e] = (LINEAR || nb == kBlk) ? acc[e] * (1.f / kBlk) : acc[e] / (float)nb;
       *reinterpret_cast<u32x4*>(index + (size_t)gb * D + cl * 8) = pack8(acc);
     }
   }
@@ -124,9 +144,15 @@ hipError_t kvs_launch_meank_build(const void* K, int L, int H_kv, int D, int64_t
   uint16_t* idx = static_cast<uint16_t*>(index);
   if (!k_is_rope) {
     const int64_t total = (int64_t)LG * nB;
-    dim3 grid(ceil_div(total, 4 * kBlocksPerWave)), block(256);
-    if (D == 128) hipLaunchKernelGGL(meank_build_raw<128>, grid, block, 0, st, Kb, N, nB, total, idx);
-    else hipLaunchKernelGGL(meank_build_raw<64>, grid, block, 0, st, Kb, N, nB, total, idx);
+    const int bpw = 64 / (D / 8);
+    // three resident workgroups per CU, each wave with its block group's rows in flight
+    const int64_t want = 256 * 3, need = (total + 4 * bpw - 1) / (4 * bpw);
+    dim3 grid((unsigned)(need < want ? need : want)), block(256);
+    const bool linear = N % kBlk == 0;
+#define BUILD_LAUNCH(DD, LIN) hipLaunchKernelGGL((meank_build_raw<DD, LIN>), grid, block, 0, st, Kb, N, nB, total, idx)
+    if (D == 128) { if (linear) BUILD_LAUNCH(128, true); else BUILD_LAUNCH(128, false); }
+    else { if (linear) BUILD_LAUNCH(64, true); else BUILD_LAUNCH(64, false); }
+#undef BUILD_LAUNCH
   } else {
     const double l2t = __builtin_log2(theta);
     uint16_t* raw = static_cast<uint16_t*>(raw_out);

@@ -5,9 +5,10 @@
 // HBM-bound: K is streamed once.  Because every (l, h) softmax has its own
 // normaliser, the logits are spilled (fp32, [L*H_q, N]) and summed after the
 // normalisers are known:
-//   1. rule_logits_*: one workgroup per (chunk of 2048 positions, l, g).  Per
-//      16-row tile of K the bf16 MFMA 16x16x32 computes the G logits of every
-//      row; the A operand holds M * log2(e)/sqrt(D) split into a bf16 high part
+//   1. rule_logits_*: one workgroup per (chunk of 2048 positions, l, g).  K is
+//      streamed in whole rows with non-temporal loads and each 16-row tile is
+//      transposed through LDS into the operand of a bf16 MFMA 16x16x32 that
+//      computes the G logits of every row; the A operand holds M * log2(e)/sqrt(D) split into a bf16 high part
 //      (rows 0..7) and a bf16 low part (rows 8..15), so hi+lo gives the logit
 //      to ~2^-16 relative at no extra MFMA cost.  Logits are written in log2
 //      units and a per-chunk (max, sum 2^(x-max)) is kept per head.
@@ -85,23 +86,41 @@ __global__ __launch_bounds__(256) void rule_logits_mfma(
   const uint16_t* Kb = K + (size_t)lg * (size_t)N * D;
   const size_t head0 = (size_t)l * H_q + (size_t)g * G;
 
-  auto load_tile = [&](int64_t t0, bf16x8* B) {
-    const int64_t j = t0 + r;
-    const bool ok = j < row1;
-    const u32x4* p = reinterpret_cast<const u32x4*>(Kb + (size_t)(ok ? j : row0) * D + q * QW);
+  // K rows are read whole (16 lanes x 16 B = one 256-byte row, 4 rows per
+  // instruction) with non-temporal loads: K is touched once, and full-row
+  // streaming reads run far closer to the HBM peak than the 64-byte row pieces
+  // the MFMA operand layout would need.  Each wave then transposes its 16-row
+  // tile through its own padded LDS slot into that layout.
+  __shared__ __attribute__((aligned(16))) char stage[4][16 * (D * 2 + 16)];
+  constexpr int kRow = D * 2 + 16;
+  constexpr int RPI = 64 / (D / 8);                 // rows per load instruction
+  constexpr int NLD = 16 / RPI;                     // load instructions per 16-row tile
+  char* slot = stage[wave];
+  const int lr = lane / (D / 8), lc = lane % (D / 8);
+  auto load_tile = [&](int64_t t0, u32x4* w) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      u32x4 w = ok ? p[s] : u32x4{0u, 0u, 0u, 0u};
-      B[s] = __builtin_bit_cast(bf16x8, w);
+    for (int i = 0; i < NLD; ++i) {
+      const int64_t j = t0 + i * RPI + lr;
+      w[i] = j < row1 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Kb + (size_t)j * D) + lc)
+                      : u32x4{0u, 0u, 0u, 0u};
     }
   };
+  auto to_operand = [&](const u32x4* w, bf16x8* B) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) *reinterpret_cast<u32x4*>(slot + (i * RPI + lr) * kRow + lc * 16) = w[i];
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      B[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(slot + r * kRow + (q * QW + 8 * s) * 2));
+  };
 
-  bf16x8 B[KS], Bn[KS];
+  u32x4 W[NLD], Wn[NLD];
+  bf16x8 B[KS];
   int64_t t0 = row0 + wave * 16;
-  if (t0 < row1) load_tile(t0, B);
+  if (t0 < row1) load_tile(t0, W);
   for (; t0 < row1; t0 += 64) {
     const int64_t tn = t0 + 64;
-    if (tn < row1) load_tile(tn, Bn);
+    if (tn < row1) load_tile(tn, Wn);
+    to_operand(W, B);
     const int64_t j = t0 + r;
     const bool vj = j < row1;
     const bool forced = is_forced(j, pi, q_s, q_e);
@@ -122,7 +141,7 @@ __global__ __launch_bounds__(256) void rule_logits_mfma(
       }
     }
 #pragma unroll
-    for (int s = 0; s < KS; ++s) B[s] = Bn[s];
+    for (int i = 0; i < NLD; ++i) W[i] = Wn[i];
   }
 
   // Reduce over the 16 lanes that hold the same head, then over the 4 waves.
@@ -239,7 +258,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
-size_t kvs_rule_ws_bytes(int L, int H_q, int64_t N) {
+size_t kvs_rule_ws_bytes(int L, int H_q, int /*H_kv*/, int64_t N) {
   const size_t LH = (size_t)L * H_q;
   const size_t n_chunks = (size_t)ceil_div(N, kChunk);
   return align256(LH * (size_t)N * 4) + align256(LH * n_chunks * 8) + align256(LH * 4);

@@ -3,7 +3,8 @@
 //
 // Scores map to order-preserving uint32 keys (sign-flip trick; NaN -> 0, the
 // lowest key; -0 -> +0), so the selection is integer-only and exact.  One
-// 1024-thread workgroup runs a radix select over the key range
+// 1024-thread workgroup (keys staged in LDS when they fit) runs a radix select
+// over the key range
 // [kmin, kmax] of the candidates, 8 bits per pass with one LDS histogram per
 // wave (no cross-wave atomic contention on hot bins), to find the threshold
 // key T and the number of threshold ties k to keep.  The emit pass gives each
@@ -34,9 +35,17 @@ struct Forced {
   __device__ bool operator()(int j) const { return (j >= f0b && j < f0e) || (j >= f1b && j < f1e); }
 };
 
+// Keys for n <= kCacheKeys are staged once in LDS (gfx950 gives a workgroup up
+// to 160 KB) so every pass after the first reads LDS; larger inputs re-read the
+// scores from global memory (L2-resident) with 4 loads in flight per thread.
+constexpr int kCacheKeys = 32768;
+constexpr int kUnroll = 4;
+
+template <bool CACHED>
 __global__ __launch_bounds__(kThreads) void topk_select_kernel(
     const float* __restrict__ score, int n, Forced forced, int c_star, int n_forced,
     uint8_t* __restrict__ keep_mask, int32_t* __restrict__ keep_idx, int64_t* __restrict__ n_kept) {
+  __shared__ uint32_t keys[CACHED ? kCacheKeys : 1];
   __shared__ uint32_t hist[kWaves][256];
   __shared__ uint32_t wmin[kWaves], wmax[kWaves];
   __shared__ uint32_t wcnt[kWaves][2];
@@ -44,15 +53,41 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const bool none = c_star == 0;   // C <= |F|: keep the forced set only
 
+  auto key_at = [&](int j) -> uint32_t { return CACHED ? keys[j] : score_key(score[j]); };
+
+  if (CACHED) {
+    for (int j0 = tid; j0 < n; j0 += kThreads * kUnroll) {
+      float v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int j = j0 + u * kThreads;
+        v[u] = j < n ? score[j] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int j = j0 + u * kThreads;
+        if (j < n) keys[j] = score_key(v[u]);
+      }
+    }
+    __syncthreads();
+  }
+
   uint32_t kT = 0xffffffffu, k_tie = 0;
   if (!none) {
     uint32_t mn = 0xffffffffu, mx = 0u;
-    for (int j = tid; j < n; j += kThreads)
-      if (!forced(j)) {
-        const uint32_t k = score_key(score[j]);
-        mn = min(mn, k);
-        mx = max(mx, k);
+    for (int j0 = tid; j0 < n; j0 += kThreads * kUnroll) {
+      uint32_t k[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int j = j0 + u * kThreads;
+        k[u] = j < n ? key_at(j) : 0u;
       }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int j = j0 + u * kThreads;
+        if (j < n && !forced(j)) { mn = min(mn, k[u]); mx = max(mx, k[u]); }
+      }
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
@@ -70,11 +105,21 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
       for (int i = tid; i < kWaves * 256; i += kThreads) (&hist[0][0])[i] = 0u;
       __syncthreads();
       const int sh = 8 * p;
-      for (int j = tid; j < n; j += kThreads) {
-        if (forced(j)) continue;
-        const uint32_t rel = score_key(score[j]) - mn;
-        const uint32_t hi = sh + 8 >= 32 ? 0u : rel >> (sh + 8);
-        if (hi == prefix) atomicAdd(&hist[wave][(rel >> sh) & 255u], 1u);
+      for (int j0 = tid; j0 < n; j0 += kThreads * kUnroll) {
+        uint32_t kk[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const int j = j0 + u * kThreads;
+          kk[u] = j < n ? key_at(j) : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const int j = j0 + u * kThreads;
+          if (j >= n || forced(j)) continue;
+          const uint32_t rel = kk[u] - mn;
+          const uint32_t hi = sh + 8 >= 32 ? 0u : rel >> (sh + 8);
+          if (hi == prefix) atomicAdd(&hist[wave][(rel >> sh) & 255u], 1u);
+        }
       }
       __syncthreads();
       if (wave == 0) {
@@ -123,8 +168,8 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
     const int j = base + lane;
     const bool in = j < s1;
     const bool f = in && forced(j);
-    const uint32_t key = (in && !f && !none) ? score_key(score[j]) : 0u;
     const bool cand = in && !f && !none;
+    const uint32_t key = cand ? key_at(j) : 0u;
     c_def += (uint32_t)__popcll(__ballot(f || (cand && key > kT)));
     c_tie += (uint32_t)__popcll(__ballot(cand && key == kT));
   }
@@ -139,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
     const bool in = j < s1;
     const bool f = in && forced(j);
     const bool cand = in && !f && !none;
-    const uint32_t key = cand ? score_key(score[j]) : 0u;
+    const uint32_t key = cand ? key_at(j) : 0u;
     const bool tie = cand && key == kT;
     const uint64_t bt = __ballot(tie);
     const bool keep = f || (cand && key > kT) || (tie && tie_run + rank_below(bt, lane) < k_tie);
@@ -183,8 +228,12 @@ hipError_t kvs_launch_topk(const float* score, int64_t n, int64_t f0b, int64_t f
     return hipGetLastError();
   }
   Forced f{(int)f0b, (int)f0e, (int)f1b, (int)f1e};
-  hipLaunchKernelGGL(topk_select_kernel, dim3(1), dim3(kThreads), 0, st, score, (int)n, f,
-                     (int)c_star, (int)n_forced, keep_mask, keep_idx, n_kept);
+  if (n <= kCacheKeys)
+    hipLaunchKernelGGL(topk_select_kernel<true>, dim3(1), dim3(kThreads), 0, st, score, (int)n, f,
+                       (int)c_star, (int)n_forced, keep_mask, keep_idx, n_kept);
+  else
+    hipLaunchKernelGGL(topk_select_kernel<false>, dim3(1), dim3(kThreads), 0, st, score, (int)n, f,
+                       (int)c_star, (int)n_forced, keep_mask, keep_idx, n_kept);
   return hipGetLastError();
 }
 
