@@ -17,67 +17,45 @@ namespace {
 
 constexpr int kBlk = 32;
 
-// Raw mode.  A wavefront reduces 64*8/D blocks at once: lane (j, c) owns
-// 16-byte column chunk c of block j and sums all 32 rows of it in-lane, so the
-// mean needs no cross-lane traffic; every load instruction still moves whole
-// 256-byte rows.  Waves take their block groups in grid-stride order (the
-// resident waves read one contiguous stretch of K at a time) and keep the next
-// 8 rows' loads in flight while adding the current ones.  K is read once, in
-// whole 256-byte rows, with non-temporal loads (streaming reads of whole rows
-// run closest to the HBM peak).  When N is a multiple
-// of 32 the blocks of all (layer, head) slices are contiguous and addressed
-// linearly; otherwise the block's slice and row count are derived per lane.
-template <int D, bool LINEAR>
+// Raw mode.  One wavefront per block: each load instruction moves 64*8/D
+// whole contiguous rows (16-byte non-temporal loads, since K is read once), a
+// lane adds the rows it loaded for its 16-byte column chunk, and the row groups
+// are folded with a fixed xor butterfly.  The grid has one wavefront per block
+// (up to 2^24 blocks; beyond that waves stride over the rest): with many
+// short-lived workgroups in flight the HBM stream runs faster than with a
+// persistent grid.
+template <int D>
 __global__ __launch_bounds__(256) void meank_build_raw(const uint16_t* __restrict__ K, int64_t N,
                                                        int64_t nB, int64_t total_blocks,
                                                        uint16_t* __restrict__ index) {
-  constexpr int LPR = D / 8, BPW = 64 / LPR;   // lanes per row, blocks per wave
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int cl = lane % LPR, j = lane / LPR;
-  const int64_t stride = (int64_t)gridDim.x * 4 * BPW;
-  for (int64_t g0 = ((int64_t)blockIdx.x * 4 + wave) * BPW; g0 < total_blocks; g0 += stride) {
-    const int64_t gb = g0 + j;
-    const bool ok = gb < total_blocks;
-    int nb = kBlk;
-    const uint16_t* src;
-    if (LINEAR) {
-      src = K + (size_t)(ok ? gb : 0) * kBlk * D + cl * 8;
-    } else {
-      const int64_t g = ok ? gb : 0, lg = g / nB, b = g - lg * nB;
-      nb = (int)min<int64_t>(kBlk, N - b * kBlk);
-      src = K + ((size_t)lg * N + (size_t)b * kBlk) * D + cl * 8;
-    }
+  constexpr int LPR = D / 8, RPL = 64 / LPR, LOADS = kBlk / RPL;
+  const int lane = threadIdx.x & 63;
+  const int cl = lane % LPR, rr = lane / LPR;
+  for (int64_t gb = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); gb < total_blocks;
+       gb += (int64_t)gridDim.x * 4) {
+    const int64_t lg = gb / nB, b = gb - lg * nB;
+    const int nb = (int)min<int64_t>(kBlk, N - b * kBlk);
+    const uint16_t* src = K + ((size_t)lg * N + (size_t)b * kBlk + rr) * D + cl * 8;
+    u32x4 w[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      w[i] = i * RPL + rr < nb ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t)i * RPL * D))
+                               : u32x4{0u, 0u, 0u, 0u};
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    u32x4 w[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
-      w[r] = (LINEAR || r < nb) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t)r * D))
-                                : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < LOADS; ++i) {
+      float x[8];
+      unpack8(w[i], x);
 #pragma unroll
-    for (int r0 = 8; r0 <= kBlk; r0 += 8) {
-      u32x4 wn[8];
-      if (r0 < kBlk) {
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-          wn[r] = (LINEAR || r0 + r < nb)
-                      ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t)(r0 + r) * D))
-                      : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        float x[8];
-        unpack8(w[r], x);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += x[e];
-      }
-      if (r0 < kBlk) {
-#pragma unroll
-        for (int r = 0; r < 8; ++r) w[r] = wn[r];
-      }
+      for (int e = 0; e < 8; ++e) acc[e] += x[e];
     }
-    if (ok) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = (LINEAR || nb == kBlk) ? acc[e] * (1.f / kBlk) : acc[e] / (float)nb;
+    for (int o = LPR; o < 64; o <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o, kWave);
+    if (rr == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = nb == kBlk ? acc[e] * (1.f / kBlk) : acc[e] / (float)nb;
       *reinterpret_cast<u32x4*>(index + (size_t)gb * D + cl * 8) = pack8(acc);
     }
   }
@@ -144,15 +122,12 @@ hipError_t kvs_launch_meank_build(const void* K, int L, int H_kv, int D, int64_t
   uint16_t* idx = static_cast<uint16_t*>(index);
   if (!k_is_rope) {
     const int64_t total = (int64_t)LG * nB;
-    const int bpw = 64 / (D / 8);
-    // three resident workgroups per CU, each wave with its block group's rows in flight
-    const int64_t want = 256 * 3, need = (total + 4 * bpw - 1) / (4 * bpw);
-    dim3 grid((unsigned)(need < want ? need : want)), block(256);
-    const bool linear = N % kBlk == 0;
-#define BUILD_LAUNCH(DD, LIN) hipLaunchKernelGGL((meank_build_raw<DD, LIN>), grid, block, 0, st, Kb, N, nB, total, idx)
-    if (D == 128) { if (linear) BUILD_LAUNCH(128, true); else BUILD_LAUNCH(128, false); }
-    else { if (linear) BUILD_LAUNCH(64, true); else BUILD_LAUNCH(64, false); }
-#undef BUILD_LAUNCH
+    const int64_t wgs = (total + 3) / 4;
+    dim3 grid((unsigned)(wgs < (int64_t(1) << 22) ? wgs : (int64_t(1) << 22))), block(256);
+    if (D == 128)
+      hipLaunchKernelGGL(meank_build_raw<128>, grid, block, 0, st, Kb, N, nB, total, idx);
+    else
+      hipLaunchKernelGGL(meank_build_raw<64>, grid, block, 0, st, Kb, N, nB, total, idx);
   } else {
     const double l2t = __builtin_log2(theta);
     uint16_t* raw = static_cast<uint16_t*>(raw_out);
