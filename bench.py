@@ -11,8 +11,12 @@ Prints one JSON line.  `value` counts K-cache tokens scored per second over the
 whole step (the rule cache's N plus the Mean-K workspace's N).  Per-call times
 come from HIP events on the stream the library launches on; `roofline` is the
 call with the largest share of the step, priced against MI355X's published
-peaks; `cpu_baseline` times the float64 oracle on a bounded sample of the same
-workload and scales it linearly to a whole step.
+peaks; its `traffic` (and each call's) is the HBM bytes per launch that
+rocprofv3's FETCH_SIZE/WRITE_SIZE counters measured, read from the committed
+summary under profiles/ and scaled by the counters' reading of a device copy of
+known size, or null when the kernel source has changed since.  `cpu_baseline`
+times the float64 oracle on a bounded sample of the same workload and scales
+it linearly to a whole step.
 """
 
 import argparse
@@ -34,6 +38,15 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 WORKLOADS = {"rule-8b+meank-256k": ("rule-8b", "meank-256k"),
              "rule-14b+meank-1m": ("rule-14b", "meank-1m")}
+# kernels each call launches (rocprofv3 short names); the two top-k calls share one kernel
+CALL_KERNELS = {
+    "kvs_qmem_update": ["qmem_kernel<128, true>"],
+    "kvs_rule_score": ["rule_logits_mfma<128, 1>", "rule_lse_merge", "rule_colsum"],
+    "kvs_slotmap_redirect": ["slotmap_kernel"],
+    "kvs_meank_build": ["meank_build_raw<128>"],
+    "kvs_meank_score": ["meank_pass<true>", "meank_pass<false>", "meank_reduce"],
+    "kvs_rerope_scatter": ["rerope_scatter_kernel<128>"],
+}
 
 
 def log(*a):
@@ -133,6 +146,30 @@ class Setup:
         }
 
 
+def measured_traffic(workload):
+    """HBM bytes per call from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary.
+
+    A call's figure is null when the summary is missing or when the source of
+    any of its kernels has changed since the counters were taken."""
+    from attention_space_retrieval_amd import rocprof_summary as rs
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_all-kernels_{workload}.json")
+    if not os.path.exists(path):
+        return {}
+    with open(path) as f:
+        summ = json.load(f)["kernels"]
+    out = {}
+    for call, kernels in CALL_KERNELS.items():
+        total = 0.0
+        for k in kernels:
+            e = summ.get(k)
+            if e is None or e["source_sha256"] != rs.source_hash(rs.base_name(k)):
+                total = None
+                break
+            total += e["read_bytes_mean"] + e["write_bytes_mean"]
+        out[call] = total
+    return out
+
+
 def run_gpu(s, steps, warmup, only=None):
     calls = s.calls()
     if only:
@@ -173,9 +210,9 @@ def cpu_baseline(s):
         return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
     c, m = s.rc, s.mc
-    L_r = min(4, c["L"])
-    lg_m = 16
-    blocks = 64
+    L_r = min(8, c["L"])
+    lg_m = 48
+    blocks = 256
     t = {}
     K = bits(s.K[:L_r])
     Mo = None
@@ -237,7 +274,9 @@ def main():
     ap.add_argument("--workload", default="rule-8b+meank-256k", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    help="comma-separated call names to time alone (profiling; not a headline figure)")
+                    help="comma-separated call names to time alone (profiling; not a headline figure). "
+                         "Calls left out are not run, so a call that consumes another's output "
+                         "(e.g. the scatter reading the Mean-K selection) sees whatever that buffer holds.")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run one 4 GiB device copy (for HBM counter scaling)")
     a = ap.parse_args()
@@ -277,11 +316,12 @@ def main():
                       "bound": bound, "achieved": round(ach, 2), "peak": peak,
                       "unit": unit, "frac": round(ach / peak, 4),
                       "per_launch": amount}
+    traffic = measured_traffic(a.workload)
+    for name, r in rows.items():
+        t = traffic.get(name)
+        r["traffic"] = None if t is None else round(t)
     dom = max(rows, key=lambda k: rows[k]["ms"])
     d = rows[dom]
-    kernels = {"kvs_rule_score": "rule_logits_mfma + rule_lse_merge + rule_colsum",
-               "kvs_meank_score": "meank_lse + meank_colsum + meank_reduce",
-               "kvs_meank_build": "meank_build_raw", "kvs_rerope_scatter": "rerope_scatter_kernel"}
     rule_ms = sum(per_call[k] for k in ("kvs_qmem_update", "kvs_rule_score", "kvs_topk_select[rule]",
                                          "kvs_slotmap_redirect"))
     rule_bytes = sum(work[k][1] for k in ("kvs_qmem_update", "kvs_rule_score", "kvs_topk_select[rule]",
@@ -297,9 +337,9 @@ def main():
         "config": {"workload": a.workload, "rule": {k: c[k] for k in ("L", "H_q", "H_kv", "D", "N", "pi", "q_s", "q_e", "C", "lam")},
                    "meank": {k: m[k] for k in ("L", "H_q", "H_kv", "D", "N", "Mq", "n_sink", "n_recent", "budget", "theta")},
                    "tokens_per_step": tokens},
-        "roofline": {"call": dom, "kernels": kernels.get(dom, dom), "bound": d["bound"],
+        "roofline": {"call": dom, "kernels": " + ".join(CALL_KERNELS.get(dom, [dom])), "bound": d["bound"],
                      "achieved": d["achieved"], "peak": d["peak"], "unit": d["unit"], "frac": d["frac"],
-                     "traffic": None},
+                     "per_launch": d["per_launch"], "traffic": d["traffic"]},
         "rule_turn": {"ms": round(rule_ms, 4), "tokens_per_s": c["N"] / (rule_ms * 1e-3),
                       "hbm_gbps": rule_bytes / (rule_ms * 1e-3) / 1e9,
                       "frac_hbm_peak": rule_bytes / (rule_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
