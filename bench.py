@@ -229,7 +229,7 @@ def cpu_baseline(s):
     keep, _, _ = oracle.topk_select(rule, (0, c["pi"]), (c["q_s"], c["q_e"]), c["C"])
     oracle.slotmap_redirect(s.slots.cpu().numpy(), keep, c["dead_slot"])
     t["topk_slot"] = time.perf_counter() - t0
-    # Mean-K on lg_m (layer, KV head) pairs of layer 0 and 1
+    # Mean-K on the first lg_m (layer, KV head) pairs
     G = m["H_q"] // m["H_kv"]
     LG = m["L"] * m["H_kv"]
     pairs = [(p // m["H_kv"], p % m["H_kv"]) for p in range(lg_m)]

@@ -100,6 +100,18 @@ def test_rule_bf16_shapes(L, H_q, H_kv, D, N, pi, q_s, q_e):
     check_rule(K, M, pi, q_s, q_e, f"rule L{L} Hq{H_q} Hkv{H_kv} D{D} N{N}")
 
 
+@pytest.mark.parametrize("dtype,L,H_q,H_kv,D,N", [
+    ("bf16", 1, 8, 2, 128, 131073),    # 65 chunks of 2048, one-row tail
+    ("f32", 1, 4, 2, 64, 131073),      # float32 keys, long cache
+    ("f32", 2, 24, 2, 128, 1500),      # float32 keys, G = 12
+    ("bf16", 2, 32, 8, 128, 2049),     # two chunks, the second one row long
+])
+def test_rule_long_and_f32(dtype, L, H_q, H_kv, D, N):
+    K = W.normal((L, H_kv, N, D), 14, W.T_K, dtype, DEV)
+    M = W.memory_vectors(L, H_q, D, 14, DEV)
+    check_rule(K, M, 7, N - 100, N - 40, f"rule {dtype} L{L} Hq{H_q} Hkv{H_kv} D{D} N{N}")
+
+
 def test_rule_large_logits_keep_precision():
     # |M| ~ 10 and K spread ~ 3: logits of tens; the hi/lo split of M keeps them exact enough.
     L, H_q, H_kv, D, N = 1, 8, 2, 128, 3000
