@@ -17,7 +17,8 @@ Sources (cited by page title and section/equation in every function):
   model-native retrieval" (Mean-K index and block relevance R_b; both display
   equations were lost in extraction, only their symbol glossaries remain) and
   section "Engineering and cost: tiered movement, page-table aliasing and
-  position-consistent reconstruction" (execution view, re-RoPE from raw K).
+  position-consistent reconstruction" (execution view, re-RoPE from raw K,
+  differential working-set update, proactive stage-out).
 
 Every function is the plain definition in float64.  bf16 inputs are widened
 from their uint16 bit patterns, which is exact.
@@ -34,8 +35,9 @@ from .qmem import qmem_update, enc_span
 from .rule import forced_mask, rule_score
 from .select import topk_select, slotmap_redirect, meank_select
 from .rope import rope_omega, rope_rotate
-from .meank import meank_build, meank_score, candidate_blocks
+from .meank import meank_build, meank_append, meank_score, candidate_blocks
 from .scatter import rerope_scatter
+from .workset import working_set_diff, working_set_update
 
 __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "as_f64",
@@ -43,6 +45,7 @@ __all__ = [
     "forced_mask", "rule_score",
     "topk_select", "slotmap_redirect", "meank_select",
     "rope_omega", "rope_rotate",
-    "meank_build", "meank_score", "candidate_blocks",
+    "meank_build", "meank_append", "meank_score", "candidate_blocks",
     "rerope_scatter",
+    "working_set_diff", "working_set_update",
 ]

@@ -23,7 +23,7 @@ import math
 
 import numpy as np
 
-from .bf16 import as_f64
+from .bf16 import as_f64, bf16_bits_to_f64, f64_to_bf16_bits
 from .rope import rope_rotate
 
 
@@ -46,6 +46,43 @@ def meank_build(K, block=32, k_is_rope=False, pos0=0, theta=1e6):
         lo, hi = b * block, min(N, (b + 1) * block)
         index[:, :, b, :] = raw[:, :, lo:hi, :].mean(axis=2)
     return index, raw
+
+
+def meank_append(k_chunk, t0, pos0, theta, stage, block=32):
+    """Incremental Mean-K append with de-RoPE stage-out during chunked prefill.
+
+    KVMEM, section "Engineering and cost ...": proactive stage-out creates the
+    raw-K copy (the reconstruction authority) while chunked prefill runs; the
+    index of section "Design and trade-offs ... Mean-K" is the per-block mean
+    of that position-free K.  Reading: token t of the workspace sits at
+    position pos0 + t; the chunk holds post-RoPE keys of tokens
+    t0 .. t0+n-1; their raw K is RoPE removed and rounded to bf16
+    (nearest-even) into the stage, and every block the chunk touches is
+    re-averaged over the staged raw K of all its tokens so far (a partial block
+    averages over the tokens it has, and is redone when the next chunk fills
+    it).  So after any sequence of appends the index equals the raw-mode
+    build over the stage.
+
+    k_chunk: [L, H_kv, n, D] bf16 bits (or floats); stage: [L, H_kv, cap, D]
+    uint16 bf16 bits, rows < t0 already staged.
+    Returns (stage_out uint16 bits, first touched block b0, means float64
+    [L, H_kv, n_touched, D] for blocks b0 .. b0+n_touched-1).
+    """
+    k = as_f64(k_chunk)
+    L, H_kv, n, D = k.shape
+    st = np.array(stage, dtype=np.uint16, copy=True)
+    if n == 0:
+        return st, t0 // block, np.zeros((L, H_kv, 0, D))
+    raw = rope_rotate(k, pos0 + t0 + np.arange(n), theta, inverse=True)
+    st[:, :, t0:t0 + n, :] = f64_to_bf16_bits(raw)
+    t1 = t0 + n
+    b0, b1 = t0 // block, -(-t1 // block)
+    staged = bf16_bits_to_f64(st[:, :, b0 * block:t1, :])
+    means = np.zeros((L, H_kv, b1 - b0, D))
+    for b in range(b0, b1):
+        lo, hi = b * block, min(t1, (b + 1) * block)
+        means[:, :, b - b0, :] = staged[:, :, lo - b0 * block:hi - b0 * block, :].mean(axis=2)
+    return st, b0, means
 
 
 def candidate_blocks(nB, n_sink, n_recent):

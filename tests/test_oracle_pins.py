@@ -353,6 +353,124 @@ def test_meank_build_derope_round_trip_and_position_independence():
         np.testing.assert_allclose(idx, oracle.meank_build(raw)[0], atol=1e-10)
 
 
+def _append_all(post, pos0, chunks, theta=1e6, cap=None):
+    """Run meank_append over consecutive chunks; return (stage bits, index dict block -> mean)."""
+    L, H, N, D = post.shape
+    stage = np.zeros((L, H, cap or N, D), dtype=np.uint16)
+    index, t0 = {}, 0
+    for n in chunks:
+        stage, b0, means = oracle.meank_append(post[:, :, t0:t0 + n], t0, pos0, theta, stage)
+        for i in range(means.shape[2]):
+            index[b0 + i] = means[:, :, i]
+        t0 += n
+    return stage, index
+
+
+def test_meank_append_stage_is_derope_of_the_chunk():
+    # Catches a wrong position offset for chunk rows (pos0 + i instead of pos0 + t0 + i)
+    # or a wrong rotation direction: the stage must be the a6 de-RoPE of the same keys.
+    r = rng(507)
+    post = oracle.f64_to_bf16_bits(r.standard_normal((2, 2, 150, 32)))
+    for pos0 in (0, 999000):
+        stage, _ = _append_all(post, pos0, [37, 1, 64, 48])
+        _, raw = oracle.meank_build(post, k_is_rope=True, pos0=pos0, theta=1e6)
+        np.testing.assert_array_equal(stage, oracle.f64_to_bf16_bits(raw))
+
+
+def test_meank_append_index_is_raw_build_of_the_stage():
+    # Catches dropped earlier rows of a partially filled block, a wrong divisor for a
+    # partial block, or averaging unrounded instead of staged values.
+    r = rng(508)
+    post = oracle.f64_to_bf16_bits(r.standard_normal((1, 3, 200, 16)))
+    for chunks in ([200], [5, 27, 32, 100, 36], [31, 2, 31, 136], [64, 0, 136]):
+        stage, index = _append_all(post, 777, chunks)
+        want, _ = oracle.meank_build(oracle.bf16_bits_to_f64(stage))
+        assert sorted(index) == list(range(want.shape[2]))
+        for b, m in index.items():
+            np.testing.assert_allclose(m, want[:, :, b], rtol=0, atol=1e-15)
+
+
+def test_meank_append_round_trip_recovers_raw():
+    # RoPE applied forward (pinned by complex multiplication) then removed by the
+    # append gives the raw keys back to bf16 rounding.
+    r = rng(509)
+    raw = oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(r.standard_normal((2, 1, 70, 64))))
+    pos0 = 123456
+    post = oracle.f64_to_bf16_bits(oracle.rope_rotate(raw, pos0 + np.arange(70), 1e6))
+    stage, _ = _append_all(post, pos0, [33, 37])
+    got = oracle.bf16_bits_to_f64(stage)
+    assert np.max(np.abs(got - raw)) <= 2 * 2.0 ** -8 * np.max(np.abs(raw))
+
+
+def _pool_from_scatter(raw_k, raw_v, blocks, pages, pool_pages, pos_base, theta=1e6):
+    L, H, _, D = raw_k.shape
+    kp = np.zeros((L, H, 32 * pool_pages, D))
+    vp = np.zeros((L, H, 32 * pool_pages, D))
+    return oracle.rerope_scatter(raw_k, raw_v, blocks, pages, pos_base, theta, kp, vp)
+
+
+def test_workset_empty_previous_is_the_scatter():
+    # With nothing resident the update is the plain re-RoPE scatter onto pages 0, 1, ...
+    r = rng(510)
+    raw_k, raw_v = r.standard_normal((2, 2, 32 * 20, 16)), r.standard_normal((2, 2, 32 * 20, 16))
+    new = [1, 4, 5, 11, 19]
+    kp, vp = np.zeros((2, 2, 32 * 8, 16)), np.zeros((2, 2, 32 * 8, 16))
+    k, v, pages, old_rank, out = oracle.working_set_update(raw_k, raw_v, [], [], new, 64, 1e6, kp, vp)
+    ks, vs = oracle.rerope_scatter(raw_k, raw_v, new, None, 64, 1e6, kp, vp)
+    assert pages.tolist() == [0, 1, 2, 3, 4] and (old_rank == -1).all() and len(out) == 0
+    np.testing.assert_array_equal(k, ks)
+    np.testing.assert_array_equal(v, vs)
+
+
+def test_workset_moved_blocks_match_rope_at_new_position():
+    # A retained block rotated by its position delta must equal raw K RoPE'd at the new
+    # compact position: catches a wrong sign of the delta or a delta in blocks, not tokens.
+    r = rng(511)
+    raw_k, raw_v = r.standard_normal((1, 2, 32 * 30, 32)), r.standard_normal((1, 2, 32 * 30, 32))
+    prev, prev_pages = [2, 3, 7, 10, 15, 21], [5, 0, 7, 2, 9, 4]
+    k0, v0 = _pool_from_scatter(raw_k, raw_v, prev, prev_pages, 12, 100)
+    new = [0, 3, 7, 12, 13, 15, 29]
+    k, v, pages, old_rank, out = oracle.working_set_update(raw_k, raw_v, prev, prev_pages, new, 100, 1e6, k0, v0)
+    want_k, want_v = oracle.rerope_scatter(raw_k, raw_v, new, pages, 100, 1e6, k0, v0)
+    for rr, p in enumerate(pages):
+        rows = slice(32 * p, 32 * p + 32)
+        np.testing.assert_allclose(k[:, :, rows], want_k[:, :, rows], atol=1e-10)
+        np.testing.assert_array_equal(v[:, :, rows], want_v[:, :, rows])
+
+
+def test_workset_classes_pages_and_untouched_rows():
+    # Brute-force set algebra for the classes; free pages go out in ascending order;
+    # pages of unmoved retained blocks and of outgoing blocks are left bit-identical.
+    r = rng(512)
+    for trial in range(20):
+        pool = 40
+        prev = sorted(r.choice(100, size=r.integers(0, 20), replace=False).tolist())
+        prev_pages = r.permutation(pool)[:len(prev)].tolist()
+        new = sorted(r.choice(100, size=r.integers(0, 25), replace=False).tolist())
+        pages, old_rank, out = oracle.working_set_diff(prev, prev_pages, new, pool)
+        retained = set(prev) & set(new)
+        assert {b for b, i in zip(new, old_rank) if i >= 0} == retained
+        assert len(out) == len(set(prev) - set(new))
+        assert len(set(pages.tolist())) == len(new) and all(0 <= p < pool for p in pages)
+        held = {prev_pages[prev.index(b)] for b in retained}
+        free = sorted(set(range(pool)) - held)
+        inc_pages = [int(p) for p, i in zip(pages, old_rank) if i < 0]
+        assert inc_pages == free[:len(inc_pages)]
+        for b, p, i in zip(new, pages, old_rank):
+            if i >= 0:
+                assert p == prev_pages[prev.index(b)]
+    raw_k = r.standard_normal((1, 1, 32 * 10, 8))
+    prev, prev_pages = [1, 2, 6], [3, 1, 0]
+    k0 = r.standard_normal((1, 1, 32 * 6, 8))
+    v0 = r.standard_normal((1, 1, 32 * 6, 8))
+    new = [1, 2, 8]          # 1, 2 keep ranks 0, 1; 6 goes out and its page 0 takes 8
+    k, v, pages, _, out = oracle.working_set_update(raw_k, raw_k, prev, prev_pages, new, 0, 1e6, k0, v0)
+    for p in (3, 1, 2, 4, 5):
+        np.testing.assert_array_equal(k[:, :, 32 * p:32 * p + 32], k0[:, :, 32 * p:32 * p + 32])
+        np.testing.assert_array_equal(v[:, :, 32 * p:32 * p + 32], v0[:, :, 32 * p:32 * p + 32])
+    assert out.tolist() == [0] and pages.tolist() == [3, 1, 0]
+
+
 def test_meank_planted_evidence_is_selected():
     # Blocks whose raw K is shifted along a direction the queries share must win.
     r = rng(506)
