@@ -136,6 +136,22 @@ kvs_status kvs_meank_build(const void* K, int32_t L, int32_t H_kv, int32_t D, in
                                            as_stream(stream)));
 }
 
+kvs_status kvs_meank_append(const void* k_chunk, int32_t L, int32_t H_kv, int32_t D, int64_t t0,
+                            int64_t n_new, int64_t pos0, double theta, void* raw_stage, int64_t cap,
+                            void* index, void* stream) {
+  if (L < 1 || H_kv < 1 || t0 < 0 || n_new < 0 || cap < 0 || pos0 < 0) return KVS_ERR_ARG;
+  if (!(std::isfinite(theta) && theta > 0.0)) return KVS_ERR_ARG;
+  if (!head_dim_ok(D)) return KVS_ERR_UNSUPPORTED;
+  if (t0 > cap || n_new > cap - t0 || numel4(L, H_kv, cap, D) < 0 || (cap + 31) / 32 > kMaxIndex ||
+      (int64_t)L * H_kv > 65535 * 32)
+    return KVS_ERR_SHAPE;
+  if (n_new == 0) return KVS_OK;
+  if (!k_chunk || !raw_stage || !index || !a16(k_chunk) || !a16(raw_stage) || !a16(index))
+    return KVS_ERR_ARG;
+  return hip_status(kvs_launch_meank_append(k_chunk, L, H_kv, D, t0, n_new, pos0, theta, raw_stage, cap,
+                                            index, as_stream(stream)));
+}
+
 size_t kvs_meank_score_workspace(int32_t L, int32_t H_q, int32_t H_kv, int64_t Mq, int64_t nB) {
   if (L < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv || Mq < 0 || nB < 0) return 0;
   return kvs_meank_ws_bytes(L, H_q, H_kv, Mq, nB);

@@ -72,6 +72,10 @@ hipError_t kvs_launch_meank_build(const void* K, int L, int H_kv, int D, int64_t
                                   int64_t pos0, double theta, void* raw_out, void* index,
                                   hipStream_t st);
 
+hipError_t kvs_launch_meank_append(const void* chunk, int L, int H_kv, int D, int64_t t0, int64_t n_new,
+                                   int64_t pos0, double theta, void* stage, int64_t cap, void* index,
+                                   hipStream_t st);
+
 hipError_t kvs_launch_meank_score(const void* Q, const void* index, int L, int H_q, int H_kv,
                                   int64_t Mq, int64_t nB, int64_t c0, int64_t c1, float* R,
                                   void* ws, hipStream_t st);

@@ -110,6 +110,74 @@ __global__ __launch_bounds__(256) void meank_build_derope(const uint16_t* __rest
   }
 }
 
+// Incremental append with de-RoPE stage-out (KVMEM, section "Engineering and
+// cost ...": proactive stage-out during chunked prefill, raw K as the
+// reconstruction authority; index as in the Mean-K section).  A workgroup owns
+// one block the chunk touches and kLgPerWg (layer, KV head) slices of it: it
+// builds the block's rotation table once in LDS, removes RoPE from the
+// chunk's rows, rounds them to bf16 into the stage, and re-averages the block
+// over the staged rows it has so far (earlier rows come from the stage).  The
+// sum runs in the same order as meank_build_raw, so the result equals the raw
+// build of the stage bit for bit.
+constexpr int kLgPerWg = 32;
+
+template <int D>
+__global__ __launch_bounds__(256) void meank_append_kernel(const uint16_t* __restrict__ chunk, int64_t n_new,
+                                                           int64_t t0, int64_t cap, int64_t nB_cap, int64_t b0,
+                                                           int LG, int64_t pos0, double log2_theta,
+                                                           uint16_t* __restrict__ stage,
+                                                           uint16_t* __restrict__ index) {
+  constexpr int LPR = D / 8, RPL = 64 / LPR, LOADS = kBlk / RPL;
+  __shared__ float2 tab[kBlk][D / 2];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int cl = lane % LPR, rr = lane / LPR;
+  const int64_t b = b0 + blockIdx.x;
+  const int64_t tb = b * kBlk;
+  const int64_t t1 = t0 + n_new;
+  const int nb = (int)min<int64_t>(kBlk, t1 - tb);
+  build_rope_table<D>(tab, pos0 + tb, log2_theta);
+  __syncthreads();
+  const int lg1 = min(LG, (int)(blockIdx.y + 1) * kLgPerWg);
+  for (int lg = (int)blockIdx.y * kLgPerWg + wave; lg < lg1; lg += 4) {
+    const uint16_t* src = chunk + (size_t)lg * n_new * D + cl * 8;
+    uint16_t* st = stage + (size_t)lg * cap * D + cl * 8;
+    u32x4 w[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int64_t t = tb + i * RPL + rr;
+      w[i] = u32x4{0u, 0u, 0u, 0u};
+      if (t < t0) w[i] = *reinterpret_cast<const u32x4*>(st + (size_t)t * D);
+      else if (t < t1) w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t)(t - t0) * D));
+    }
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int r = i * RPL + rr;
+      const int64_t t = tb + r;
+      float x[8];
+      unpack8(w[i], x);
+      rotate8<D>(x, tab[r], cl, -1);        // every lane takes part: rotate8 shuffles
+      if (t >= t0 && t < t1) {
+        const u32x4 y = pack8(x);
+        *reinterpret_cast<u32x4*>(st + (size_t)t * D) = y;
+        w[i] = y;
+      }
+      unpack8(w[i], x);                     // staged (rounded) raw K, zero past the end
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += x[e];
+    }
+#pragma unroll
+    for (int o = LPR; o < 64; o <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o, kWave);
+    if (rr == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = nb == kBlk ? acc[e] * (1.f / kBlk) : acc[e] / (float)nb;
+      *reinterpret_cast<u32x4*>(index + ((size_t)lg * nB_cap + b) * D + cl * 8) = pack8(acc);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t kvs_launch_meank_build(const void* K, int L, int H_kv, int D, int64_t N, int k_is_rope,
@@ -137,5 +205,26 @@ hipError_t kvs_launch_meank_build(const void* K, int L, int H_kv, int D, int64_t
     else
       hipLaunchKernelGGL(meank_build_derope<64>, grid, block, 0, st, Kb, N, nB, LG, pos0, l2t, raw, idx);
   }
+  return hipGetLastError();
+}
+
+hipError_t kvs_launch_meank_append(const void* chunk, int L, int H_kv, int D, int64_t t0, int64_t n_new,
+                                   int64_t pos0, double theta, void* stage, int64_t cap, void* index,
+                                   hipStream_t st) {
+  if (n_new == 0) return hipSuccess;
+  const int LG = L * H_kv;
+  const int64_t b0 = t0 / kBlk, b1 = (t0 + n_new + kBlk - 1) / kBlk;
+  const int64_t nB_cap = (cap + kBlk - 1) / kBlk;
+  const double l2t = __builtin_log2(theta);
+  const dim3 grid((unsigned)(b1 - b0), ceil_div(LG, kLgPerWg)), block(256);
+  const uint16_t* c = static_cast<const uint16_t*>(chunk);
+  uint16_t* s = static_cast<uint16_t*>(stage);
+  uint16_t* idx = static_cast<uint16_t*>(index);
+  if (D == 128)
+    hipLaunchKernelGGL(meank_append_kernel<128>, grid, block, 0, st, c, n_new, t0, cap, nB_cap, b0, LG, pos0,
+                       l2t, s, idx);
+  else
+    hipLaunchKernelGGL(meank_append_kernel<64>, grid, block, 0, st, c, n_new, t0, cap, nB_cap, b0, LG, pos0,
+                       l2t, s, idx);
   return hipGetLastError();
 }

@@ -32,6 +32,7 @@ _SIGNATURES = [
     ("kvs_topk_select", _I32, [_P, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
     ("kvs_slotmap_redirect", _I32, [_P, _P, _I64, _I64, _P, _P]),
     ("kvs_meank_build", _I32, [_P, _I32, _I32, _I32, _I64, _I32, _I32, _I64, _F64, _P, _P, _P]),
+    ("kvs_meank_append", _I32, [_P, _I32, _I32, _I32, _I64, _I64, _I64, _F64, _P, _I64, _P, _P]),
     ("kvs_meank_score_workspace", _SZ, [_I32, _I32, _I32, _I64, _I64]),
     ("kvs_meank_score", _I32, [_P, _P, _I32, _I32, _I32, _I32, _I64, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     ("kvs_rerope_scatter", _I32, [_P, _P, _I64, _P, _P, _I64, _I32, _I32, _I32, _I32, _I64, _F64,
@@ -197,6 +198,24 @@ def kvs_meank_build(K, k_is_rope=False, pos0=0, theta=1e6, raw_k_out=None, index
     _check("kvs_meank_build", load().kvs_meank_build(
         _ptr(K), L, H_kv, D, N, block, int(bool(k_is_rope)), int(pos0), float(theta),
         _ptr(raw_k_out), _ptr(index), _stream(K)))
+    return index
+
+
+def kvs_meank_append(k_chunk, t0, raw_stage, index, pos0=0, theta=1e6):
+    """Append the post-RoPE keys k_chunk [L, H_kv, n, D] (bf16) of tokens t0..t0+n-1:
+    their raw K goes to raw_stage [L, H_kv, cap, D], the blocks they touch to index
+    [L, H_kv, ceil(cap/32), D].  Returns index."""
+    _dev(k_chunk, raw_stage, index)
+    for t, name in ((k_chunk, "k_chunk"), (raw_stage, "raw_stage"), (index, "index")):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16")
+    L, H_kv, n, D = k_chunk.shape
+    cap = raw_stage.shape[2]
+    _need(tuple(raw_stage.shape) == (L, H_kv, cap, D), "raw_stage must be [L, H_kv, cap, D] like k_chunk")
+    _need(tuple(index.shape) == (L, H_kv, -(-cap // 32), D), "index must be [L, H_kv, ceil(cap/32), D]")
+    _check("kvs_meank_append", load().kvs_meank_append(
+        _ptr(k_chunk), L, H_kv, D, int(t0), n, int(pos0), float(theta), _ptr(raw_stage), cap,
+        _ptr(index), _stream(raw_stage)))
     return index
 
 

@@ -151,6 +151,33 @@ kvs_status kvs_meank_build(const void* K, int32_t L, int32_t H_kv, int32_t D, in
                            int32_t block, int32_t k_is_rope, int64_t pos0, double theta,
                            void* raw_k_out, void* index, void* stream);
 
+/*
+ * Incremental Mean-K append with de-RoPE stage-out -- KVMEM, section
+ * "Engineering and cost ...": proactive stage-out writes the raw-K copy (the
+ * reconstruction authority) while chunked prefill runs, and the index of the
+ * Mean-K section is the per-block mean of that position-free K.
+ * Token t of the workspace sits at position pos0 + t.  The chunk holds the
+ * post-RoPE keys of tokens t0 .. t0+n_new-1.  For every layer and KV head:
+ *   raw_stage[l,g,t,:] = bf16(RoPE(-(pos0 + t)) k_chunk[l,g,t-t0,:])   (t0 <= t < t0+n_new)
+ *   index[l,g,b,:] = mean of raw_stage[l,g,32b .. min(32b+32, t0+n_new)-1,:]
+ *     for every block b with 32b < t0+n_new and 32b+32 > t0 (the blocks the
+ *     chunk touches; a partial last block averages over the tokens it has and
+ *     is redone by the next append).
+ * After any sequence of appends, the index equals kvs_meank_build run in raw
+ * mode on raw_stage[:, :, 0:t0+n_new] bit for bit.
+ *   k_chunk    [L, H_kv, n_new, D] bf16, device.
+ *   raw_stage  [L, H_kv, cap, D] bf16, device: rows [32*floor(t0/32), t0) are
+ *              read (they must hold earlier appends), rows [t0, t0+n_new) written.
+ *   index      [L, H_kv, ceil(cap/32), D] bf16, device: touched blocks written.
+ *   theta      RoPE base (omega_i = theta^(-2i/D), rotate-half pairing).
+ * n_new == 0 is a no-op.  Errors: KVS_ERR_ARG (null, negative, theta not
+ * finite and positive), KVS_ERR_SHAPE (t0 + n_new > cap, overflow),
+ * KVS_ERR_UNSUPPORTED (D not 64/128).
+ */
+kvs_status kvs_meank_append(const void* k_chunk, int32_t L, int32_t H_kv, int32_t D, int64_t t0,
+                            int64_t n_new, int64_t pos0, double theta, void* raw_stage,
+                            int64_t cap, void* index, void* stream);
+
 /* Workspace bytes kvs_meank_score needs. */
 size_t kvs_meank_score_workspace(int32_t L, int32_t H_q, int32_t H_kv, int64_t Mq, int64_t nB);
 

@@ -27,7 +27,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = header_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(kvs.ENTRY_POINTS) == names
@@ -88,6 +88,13 @@ def test_topk_slot_meank_rerope_rejections(lib):
     assert lib.kvs_meank_build(FAKE, 2, 2, 128, 64, 32, 1, 0, math.inf, None, FAKE, None) == 1
     assert lib.kvs_meank_build(FAKE, 2, 2, 128, 64, 32, 1, -5, 1e6, None, FAKE, None) == 1
     assert lib.kvs_meank_build(None, 2, 2, 128, 64, 32, 0, 0, 1e6, None, FAKE, None) == 1
+    a = lib.kvs_meank_append
+    assert a(FAKE, 2, 2, 128, 40, 30, 0, 1e6, FAKE, 64, FAKE, None) == 2      # t0 + n_new > cap
+    assert a(FAKE, 2, 2, 128, -1, 30, 0, 1e6, FAKE, 64, FAKE, None) == 1
+    assert a(FAKE, 2, 2, 128, 0, 30, 0, 0.0, FAKE, 64, FAKE, None) == 1       # theta
+    assert a(FAKE, 2, 2, 96, 0, 30, 0, 1e6, FAKE, 64, FAKE, None) == 4
+    assert a(None, 2, 2, 128, 0, 30, 0, 1e6, FAKE, 64, FAKE, None) == 1
+    assert a(None, 2, 2, 128, 10, 0, 0, 1e6, None, 64, None, None) == 0       # empty chunk: no-op
     ws = lib.kvs_meank_score_workspace(2, 8, 2, 50, 300)
     assert ws > 0
     assert lib.kvs_meank_score(FAKE, FAKE, 2, 8, 2, 64, 50, 300, 4, 7, FAKE, FAKE, ws, None) == 4

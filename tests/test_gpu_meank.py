@@ -62,6 +62,88 @@ def test_meank_build_full_size_sampled():
     del K
 
 
+# ---------------------------------------------------------------- incremental append (stage-out)
+
+def _append_case(L, H_kv, D, cap, chunks, pos0, seed):
+    post = W.normal((L, H_kv, sum(chunks), D), seed, W.T_K, "bf16", DEV)
+    stage = torch.zeros((L, H_kv, cap, D), dtype=torch.bfloat16, device=DEV)
+    index = torch.zeros((L, H_kv, -(-cap // 32), D), dtype=torch.bfloat16, device=DEV)
+    o_stage = np.zeros((L, H_kv, cap, D), dtype=np.uint16)
+    t0 = 0
+    for n in chunks:
+        chunk = post[:, :, t0:t0 + n].contiguous()
+        kvs.kvs_meank_append(chunk, t0, stage, index, pos0=pos0, theta=1e6)
+        torch.cuda.synchronize()
+        o_stage, b0, means = oracle.meank_append(host(chunk), t0, pos0, 1e6, o_stage)
+        g_stage = bits(stage)
+        if n:
+            assert_within_ulp(g_stage[:, :, t0:t0 + n], oracle.bf16_bits_to_f64(o_stage[:, :, t0:t0 + n]),
+                              f"stage rows [{t0}, {t0 + n})", atol=1e-6)
+            got = bits(index[:, :, b0:b0 + means.shape[2]])
+            check_append_index(got, means, o_stage, b0, t0 + n, f"index blocks from {b0} after chunk at {t0}")
+        t0 += n
+    return stage, index, t0
+
+
+def check_append_index(got_bits, means, o_stage, b0, t_end, what):
+    """Index within 1 ulp of the oracle's mean, plus the mean of 1 ulp of each staged row
+    (the GPU's own stage may round each row 1 ulp apart from the oracle's), plus 1e-5."""
+    g = oracle.bf16_bits_to_f64(got_bits)
+    for i in range(means.shape[2]):
+        lo, hi = 32 * (b0 + i), min(32 * (b0 + i) + 32, t_end)
+        rows_ulp = bf16_ulp(oracle.bf16_bits_to_f64(o_stage[:, :, lo:hi])).mean(axis=2)
+        bound = bf16_ulp(means[:, :, i]) + rows_ulp + 1e-5
+        err = np.abs(g[:, :, i] - means[:, :, i])
+        assert (err <= bound).all(), f"{what}: block {b0 + i} max excess {(err - bound).max():.3e}"
+
+
+@pytest.mark.parametrize("L,H_kv,D,cap,chunks,pos0", [
+    (2, 3, 128, 300, [37, 1, 64, 0, 100, 50], 999000),   # ragged chunks, unaligned starts, large positions
+    (1, 2, 64, 96, [96], 0),                             # one aligned chunk, D = 64
+    (3, 1, 128, 1000, [31, 1, 32, 33, 500], 12345),      # chunks that end exactly on block boundaries
+])
+def test_meank_append_against_oracle(L, H_kv, D, cap, chunks, pos0):
+    _append_case(L, H_kv, D, cap, chunks, pos0, 31)
+
+
+def test_meank_append_equals_raw_build_of_stage():
+    """The appended index is the raw-mode build of the stage, bit for bit."""
+    stage, index, t_end = _append_case(2, 4, 128, 700, [100, 200, 3, 350], 4096, 32)
+    built = kvs.kvs_meank_build(stage[:, :, :t_end].contiguous())
+    torch.cuda.synchronize()
+    nb = -(-t_end // 32)
+    assert torch.equal(built, index[:, :, :nb])
+
+
+def test_meank_append_full_shape_sampled():
+    """An 8192-token chunk at meank-256k's L and H_kv, unaligned start; sampled blocks."""
+    c = W.config("meank-256k")
+    L, H_kv, D = c["L"], c["H_kv"], c["D"]
+    t0, n, cap = 8192 + 13, 8192, 16448
+    prefix = W.normal((L, H_kv, t0, D), 41, W.T_K, "bf16", DEV)
+    chunk = W.normal((L, H_kv, n, D), 42, W.T_K, "bf16", DEV)
+    stage = torch.zeros((L, H_kv, cap, D), dtype=torch.bfloat16, device=DEV)
+    index = torch.zeros((L, H_kv, cap // 32, D), dtype=torch.bfloat16, device=DEV)
+    kvs.kvs_meank_append(prefix, 0, stage, index, pos0=0)
+    kvs.kvs_meank_append(chunk, t0, stage, index, pos0=0)
+    torch.cuda.synchronize()
+    r = np.random.default_rng(6)
+    b0 = t0 // 32
+    for b in [b0, b0 + 1, (t0 + n) // 32] + [int(x) for x in r.integers(b0, (t0 + n) // 32, 20)]:
+        l, g = int(r.integers(L)), int(r.integers(H_kv))
+        lo, hi = 32 * b, min(32 * b + 32, t0 + n)
+        o_stage = np.zeros((1, 1, hi, D), dtype=np.uint16)
+        if lo < t0:      # rows of the block staged by the first call
+            o_stage, _, _ = oracle.meank_append(host(prefix[l:l + 1, g:g + 1, :t0]), 0, 0, 1e6,
+                                                np.zeros((1, 1, hi, D), dtype=np.uint16))
+        o_stage, ob0, means = oracle.meank_append(host(chunk[l:l + 1, g:g + 1, max(0, lo - t0):hi - t0]),
+                                                  max(lo, t0), 0, 1e6, o_stage)
+        assert ob0 == b
+        check_append_index(bits(index[l, g, b])[None, None, None], means[:, :, :1], o_stage, b, hi,
+                           f"block {(l, g, b)}")
+    del prefix, chunk, stage
+
+
 # ---------------------------------------------------------------- block relevance
 
 def check_score(Q, index, n_sink, n_recent, what):
