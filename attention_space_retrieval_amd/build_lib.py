@@ -27,6 +27,7 @@ SOURCES = [
     "topk.hip",
     "meank_build.hip",
     "meank_score.hip",
+    "workset.hip",
     "rerope_scatter.hip",
 ]
 

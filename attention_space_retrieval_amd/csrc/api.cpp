@@ -197,4 +197,38 @@ kvs_status kvs_rerope_scatter(const void* k_src, const void* v_src, int64_t src_
                                       err_flag, as_stream(stream)));
 }
 
+size_t kvs_working_set_workspace(int64_t pool_pages) {
+  if (pool_pages < 0 || pool_pages > kMaxIndex) return 0;
+  return kvs_workset_ws_bytes(pool_pages);
+}
+
+kvs_status kvs_working_set_update(const void* k_src, const void* v_src, int64_t src_tokens,
+                                  const int32_t* prev_blocks, const int32_t* prev_pages, int64_t n_prev,
+                                  const int32_t* new_blocks, int64_t n_new, int32_t L, int32_t H_kv,
+                                  int32_t D, int32_t block, int64_t pos_base, double theta,
+                                  void* k_pool, void* v_pool, int64_t pool_pages, int32_t* pages_out,
+                                  int32_t* old_rank_out, int32_t* outgoing_pages_out,
+                                  int64_t* counts_out, int32_t* err_flag, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  if (L < 1 || H_kv < 1 || src_tokens < 0 || n_prev < 0 || n_new < 0 || pool_pages < 0 || pos_base < 0)
+    return KVS_ERR_ARG;
+  if (!(std::isfinite(theta) && theta > 0.0)) return KVS_ERR_ARG;
+  if (!k_src || !k_pool || !counts_out || (n_new > 0 && (!new_blocks || !pages_out || !old_rank_out)) ||
+      (n_prev > 0 && (!prev_blocks || !prev_pages || !outgoing_pages_out)))
+    return KVS_ERR_ARG;
+  if (!a16(k_src) || !a16(v_src) || !a16(k_pool) || !a16(v_pool)) return KVS_ERR_ARG;
+  if ((v_src == nullptr) != (v_pool == nullptr)) return KVS_ERR_ARG;
+  if (block != 32 || !head_dim_ok(D)) return KVS_ERR_UNSUPPORTED;
+  if (src_tokens % block != 0 || numel4(L, H_kv, src_tokens, D) < 0 ||
+      numel4(L, H_kv, pool_pages, (int64_t)block * D) < 0 || pool_pages > kMaxIndex ||
+      n_new > pool_pages || n_prev > pool_pages)
+    return KVS_ERR_SHAPE;
+  const size_t need = kvs_workset_ws_bytes(pool_pages);
+  if (need > 0 && (!ws || ws_bytes < need || !a16(ws))) return KVS_ERR_WORKSPACE;
+  return hip_status(kvs_launch_workset(k_src, v_src, src_tokens, prev_blocks, prev_pages, n_prev,
+                                       new_blocks, n_new, L, H_kv, D, pos_base, theta, k_pool, v_pool,
+                                       pool_pages, pages_out, old_rank_out, outgoing_pages_out,
+                                       counts_out, err_flag, ws, as_stream(stream)));
+}
+
 }  // extern "C"

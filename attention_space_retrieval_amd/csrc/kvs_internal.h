@@ -85,3 +85,12 @@ hipError_t kvs_launch_rerope(const void* k_src, const void* v_src, int64_t src_t
                              const int32_t* src_block, const int32_t* page_table, int64_t n_sel,
                              int L, int H_kv, int D, int64_t pos_base, double theta, void* k_pool,
                              void* v_pool, int64_t pool_pages, int32_t* err_flag, hipStream_t st);
+
+size_t kvs_workset_ws_bytes(int64_t pool_pages);
+hipError_t kvs_launch_workset(const void* k_src, const void* v_src, int64_t src_tokens,
+                              const int32_t* prev_blocks, const int32_t* prev_pages, int64_t n_prev,
+                              const int32_t* new_blocks, int64_t n_new, int L, int H_kv, int D,
+                              int64_t pos_base, double theta, void* k_pool, void* v_pool,
+                              int64_t pool_pages, int32_t* pages_out, int32_t* old_rank_out,
+                              int32_t* outgoing_out, int64_t* counts, int32_t* err_flag, void* ws,
+                              hipStream_t st);

@@ -37,6 +37,9 @@ _SIGNATURES = [
     ("kvs_meank_score", _I32, [_P, _P, _I32, _I32, _I32, _I32, _I64, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     ("kvs_rerope_scatter", _I32, [_P, _P, _I64, _P, _P, _I64, _I32, _I32, _I32, _I32, _I64, _F64,
                                   _P, _P, _I64, _P, _P]),
+    ("kvs_working_set_workspace", _SZ, [_I64]),
+    ("kvs_working_set_update", _I32, [_P, _P, _I64, _P, _P, _I64, _P, _I64, _I32, _I32, _I32, _I32, _I64,
+                                      _F64, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
 ]
 ENTRY_POINTS = [s[0] for s in _SIGNATURES]
 
@@ -266,3 +269,47 @@ def kvs_rerope_scatter(k_src, v_src, src_block, page_table, n_sel, pos_base, the
         _ptr(err_flag), _stream(k_src)))
     return k_pool, v_pool
 
+
+
+def kvs_working_set_workspace(pool_pages):
+    return load().kvs_working_set_workspace(pool_pages)
+
+
+def kvs_working_set_update(k_src, v_src, prev_blocks, prev_pages, new_blocks, pos_base, theta, k_pool,
+                           v_pool, err_flag=None, ws=None, block=32):
+    """Differential working-set update of the pools (in place).
+
+    prev_blocks/prev_pages: int32 G_{t-1} (ascending) and their pages; new_blocks: int32 W_t
+    (ascending).  Returns (pages [n_new], old_rank [n_new], outgoing_pages [n_prev], counts [3]);
+    the first counts[2] entries of outgoing_pages are the released pages.
+    """
+    _dev(k_src, v_src, prev_blocks, prev_pages, new_blocks, k_pool, v_pool, err_flag, ws)
+    L, H_kv, src_tokens, D = k_src.shape
+    pool_pages = k_pool.shape[2] // block
+    _need(k_src.dtype == torch.bfloat16 and k_pool.dtype == torch.bfloat16, "K tensors must be bf16")
+    _need(k_pool.shape[0] == L and k_pool.shape[1] == H_kv and k_pool.shape[3] == D
+          and k_pool.shape[2] % block == 0, "k_pool must be [L, H_kv, pages*block, D]")
+    _need((v_src is None) == (v_pool is None), "v_src and v_pool go together")
+    _need(v_src is None or (v_src.shape == k_src.shape and v_pool.shape == k_pool.shape
+                            and v_src.dtype == torch.bfloat16 and v_pool.dtype == torch.bfloat16),
+          "V tensors must be bf16 shaped like the K tensors")
+    for t in (prev_blocks, prev_pages, new_blocks):
+        if t.dtype != torch.int32:
+            raise TypeError("block ids and pages must be int32")
+    n_prev, n_new = prev_blocks.numel(), new_blocks.numel()
+    _need(prev_pages.numel() == n_prev, "prev_pages needs one page per previous block")
+    _need(err_flag is None or (err_flag.dtype == torch.int32 and err_flag.numel() >= 1),
+          "err_flag must be int32 [1]")
+    dev = k_src.device
+    pages = torch.empty(n_new, dtype=torch.int32, device=dev)
+    old_rank = torch.empty(n_new, dtype=torch.int32, device=dev)
+    outgoing = torch.empty(max(n_prev, 1), dtype=torch.int32, device=dev)
+    counts = torch.empty(3, dtype=torch.int64, device=dev)
+    if ws is None:
+        ws = torch.empty(max(1, kvs_working_set_workspace(pool_pages)), dtype=torch.uint8, device=dev)
+    _check("kvs_working_set_update", load().kvs_working_set_update(
+        _ptr(k_src), _ptr(v_src), src_tokens, _ptr(prev_blocks), _ptr(prev_pages), n_prev,
+        _ptr(new_blocks), n_new, L, H_kv, D, block, int(pos_base), float(theta), _ptr(k_pool),
+        _ptr(v_pool), pool_pages, _ptr(pages), _ptr(old_rank), _ptr(outgoing), _ptr(counts),
+        _ptr(err_flag), _ptr(ws), ws.numel(), _stream(k_src)))
+    return pages, old_rank, outgoing[:n_prev], counts

@@ -221,6 +221,53 @@ kvs_status kvs_rerope_scatter(const void* k_src, const void* v_src, int64_t src_
                               double theta, void* k_pool, void* v_pool, int64_t pool_pages,
                               int32_t* err_flag, void* stream);
 
+/* Workspace bytes kvs_working_set_update needs for a pool of pool_pages pages. */
+size_t kvs_working_set_workspace(int64_t pool_pages);
+
+/*
+ * Differential working-set update of the execution view -- KVMEM, section
+ * "Engineering and cost: tiered movement, page-table aliasing and
+ * position-consistent reconstruction": consecutive steps' working sets
+ * overlap, and only blocks the step selects that the GPU page pool no longer
+ * holds (W_t minus G_{t-1}) are materialised again; retained, incoming and
+ * outgoing blocks are told apart.
+ * prev_blocks (G_{t-1}, the blocks the pool holds, with their pages) and
+ * new_blocks (W_t) are strictly ascending block ids; a block's compact index
+ * r is its rank, so it sits at positions pos_base + 32r .. +31.
+ *   retained  keeps its page.  If its rank moved from r_old to r, its K
+ *             (RoPE'd at the old positions) is rotated in place by the
+ *             position delta 32 (r - r_old); V is untouched.
+ *   incoming  takes a free page (one no retained block holds; free pages in
+ *             ascending order go to incoming blocks in ascending rank) and is
+ *             written like kvs_rerope_scatter: raw K rotated to its compact
+ *             positions, V copied.
+ *   outgoing  releases its page (contents left as they are).
+ *   k_src, v_src   [L, H_kv, src_tokens, D] bf16 raw (position-free) K and V;
+ *                  v_src and v_pool may both be NULL.
+ *   k_pool, v_pool [L, H_kv, pool_pages*32, D] bf16, updated in place.
+ *   pages_out      [n_new] int32: the new page table (page of rank r).
+ *   old_rank_out   [n_new] int32: rank in G_{t-1}, -1 for incoming blocks.
+ *   outgoing_pages_out [n_prev] int32: released pages in G_{t-1} order (first
+ *                  counts_out[2] entries).
+ *   counts_out     [3] int64: retained, incoming, outgoing.
+ *   err_flag       device int32 set to 1 (never cleared) when a block id is out
+ *                  of range or not ascending, a retained page is out of range
+ *                  or held twice; then pages_out is all -1 and no pool row is
+ *                  written.  May be NULL.
+ *   ws             device workspace of >= kvs_working_set_workspace() bytes.
+ * Errors: KVS_ERR_ARG, KVS_ERR_SHAPE (n_new or n_prev > pool_pages, src_tokens
+ * not a multiple of 32, overflow), KVS_ERR_UNSUPPORTED (block != 32, D not
+ * 64/128), KVS_ERR_WORKSPACE.
+ */
+kvs_status kvs_working_set_update(const void* k_src, const void* v_src, int64_t src_tokens,
+                                  const int32_t* prev_blocks, const int32_t* prev_pages,
+                                  int64_t n_prev, const int32_t* new_blocks, int64_t n_new,
+                                  int32_t L, int32_t H_kv, int32_t D, int32_t block,
+                                  int64_t pos_base, double theta, void* k_pool, void* v_pool,
+                                  int64_t pool_pages, int32_t* pages_out, int32_t* old_rank_out,
+                                  int32_t* outgoing_pages_out, int64_t* counts_out,
+                                  int32_t* err_flag, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

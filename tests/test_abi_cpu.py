@@ -27,7 +27,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = header_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(kvs.ENTRY_POINTS) == names
@@ -107,6 +107,30 @@ def test_topk_slot_meank_rerope_rejections(lib):
     assert r(FAKE, FAKE, 640, FAKE, None, 3, 2, 2, 128, 64, 0, 1e6, FAKE, FAKE, 8, None, None) == 4
     assert r(FAKE, FAKE, 640, FAKE, None, 3, 2, 2, 128, 32, 0, -1.0, FAKE, FAKE, 8, None, None) == 1
     assert r(FAKE, FAKE, 640, None, None, 3, 2, 2, 128, 32, 0, 1e6, FAKE, FAKE, 8, None, None) == 1
+
+
+def test_working_set_rejections(lib):
+    f = lib.kvs_working_set_update
+    ws = lib.kvs_working_set_workspace(8)
+    assert ws >= 8 * 4
+    base = [FAKE, FAKE, 640, FAKE, FAKE, 3, FAKE, 4, 2, 2, 128, 32, 0, 1e6, FAKE, FAKE, 8,
+            FAKE, FAKE, FAKE, FAKE, None, FAKE, ws, None]
+
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a7=9) == 2                 # more selected blocks than pool pages
+    assert call(a2=650) == 2               # src_tokens not a multiple of 32
+    assert call(a11=16) == 4               # block size
+    assert call(a10=96) == 4               # head dim
+    assert call(a13=-1.0) == 1             # theta
+    assert call(a0=None) == 1
+    assert call(a1=None) == 1              # V source without V pool
+    assert call(a20=None) == 1             # counts
+    assert call(a23=ws - 1) == 5
+    assert call(a6=None) == 1              # new blocks missing while n_new > 0
 
 
 def test_binding_refuses_cpu_tensors():

@@ -286,3 +286,124 @@ def test_meank_step_planted_evidence():
                                    np.zeros(k_pool.shape), np.zeros(k_pool.shape, dtype=np.uint16))
     assert_within_ulp(bits(k_pool), ko, "scattered K", atol=1e-6)
     np.testing.assert_array_equal(bits(v_pool), vo)
+
+
+# ---------------------------------------------------------------- differential working-set update
+
+def _host_bf16(shape, seed, tid):
+    return host(W.normal(shape, seed, tid, "bf16", "cpu"))
+
+
+def _workset_case(L, H_kv, D, src_blocks, pool_pages, prev, prev_pages, new, pos_base, with_v, seed,
+                  expect_err=False):
+    theta = 1e6
+    raw_k = _host_bf16((L, H_kv, 32 * src_blocks, D), seed, W.T_K)
+    raw_v = _host_bf16((L, H_kv, 32 * src_blocks, D), seed, W.T_V) if with_v else None
+    # pool as the previous step left it: G_{t-1} scattered at its ranks, other pages arbitrary
+    k_init = _host_bf16((L, H_kv, 32 * pool_pages, D), seed, W.T_K + 20)
+    v_init = _host_bf16((L, H_kv, 32 * pool_pages, D), seed, W.T_V + 20) if with_v else None
+    if prev:
+        ks, vs = oracle.rerope_scatter(raw_k, raw_v if with_v else raw_k, prev, prev_pages, pos_base, theta,
+                                       oracle.bf16_bits_to_f64(k_init), v_init if with_v else k_init)
+        k_init = oracle.f64_to_bf16_bits(ks)
+        if with_v:
+            v_init = vs
+    dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(DEV)
+    i32 = lambda a: torch.tensor(a, dtype=torch.int32, device=DEV)
+    k_pool, v_pool = dev(k_init.copy()), (dev(v_init.copy()) if with_v else None)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    pages, rank, outgoing, counts = kvs.kvs_working_set_update(
+        dev(raw_k), dev(raw_v) if with_v else None, i32(prev), i32(prev_pages), i32(new), pos_base, theta,
+        k_pool, v_pool, err_flag=err)
+    torch.cuda.synchronize()
+    if expect_err:
+        assert int(err.item()) == 1
+        assert torch.all(pages == -1)
+        assert np.array_equal(bits(k_pool), k_init)
+        return
+    assert int(err.item()) == 0
+    k_o, v_o, pages_o, rank_o, out_o = oracle.working_set_update(
+        raw_k, raw_v if with_v else raw_k, prev, prev_pages, new, pos_base, theta, k_init,
+        v_init if with_v else k_init)
+    np.testing.assert_array_equal(pages.cpu().numpy(), pages_o)
+    np.testing.assert_array_equal(rank.cpu().numpy(), rank_o)
+    n_out = int(counts[2].item())
+    np.testing.assert_array_equal(outgoing[:n_out].cpu().numpy(), out_o)
+    n_ret = int((rank_o >= 0).sum())
+    assert counts.cpu().tolist() == [n_ret, len(new) - n_ret, len(out_o)]
+    assert_within_ulp(bits(k_pool), k_o, "pool K", atol=1e-6)
+    if with_v:
+        np.testing.assert_array_equal(bits(v_pool), v_o)
+    # rows the update must not touch stay bit-identical
+    touched = {int(p) for p, rr, r in zip(pages_o, rank_o, range(len(new))) if rr != r}
+    for p in range(pool_pages):
+        if p not in touched:
+            assert np.array_equal(bits(k_pool)[:, :, 32 * p:32 * p + 32], k_init[:, :, 32 * p:32 * p + 32]), p
+    return pages_o, rank_o
+
+
+def test_working_set_mixed_classes():
+    r = np.random.default_rng(60)
+    prev = sorted(r.choice(64, 20, replace=False).tolist())
+    prev_pages = r.permutation(40)[:20].tolist()
+    new = sorted(set(prev[::2]) | set(r.choice(64, 15, replace=False).tolist()))[:30]
+    pages, rank = _workset_case(2, 3, 128, 64, 40, prev, prev_pages, new, 96, True, 61)
+    assert (rank >= 0).any() and (rank < 0).any() and any(rr not in (-1, i) for i, rr in enumerate(rank))
+
+
+@pytest.mark.parametrize("case", ["empty-prev", "same-set", "shift-down", "all-out", "d64-no-v"])
+def test_working_set_edge_cases(case):
+    prev, prev_pages = [3, 5, 8, 13, 21], [4, 0, 7, 2, 6]
+    D, with_v, new = 128, True, None
+    if case == "empty-prev":
+        prev, prev_pages, new = [], [], [1, 2, 3, 30]
+    elif case == "same-set":
+        new = list(prev)
+    elif case == "shift-down":
+        new = prev[1:] + [30]            # every retained block moves one rank down
+    elif case == "all-out":
+        new = []
+    else:
+        D, with_v, new = 64, False, [0, 5, 13, 22]
+    _workset_case(1, 2, D, 32, 8, prev, prev_pages, new, 4096, with_v, 62)
+
+
+def test_working_set_rejects_unsorted_selection():
+    _workset_case(1, 2, 128, 32, 8, [3, 5], [1, 2], [6, 4], 0, True, 63, expect_err=True)
+
+
+def test_working_set_full_shape_sampled():
+    """meank-256k's heads and budget: 2048 selected blocks, half of them carried over."""
+    c = W.config("meank-256k")
+    L, H_kv, D, nB, budget = c["L"], c["H_kv"], c["D"], c["N"] // 32, c["budget"]
+    r = np.random.default_rng(64)
+    prev = np.sort(r.choice(nB, budget, replace=False))
+    keep = r.choice(budget, budget // 2, replace=False)
+    fresh = np.setdiff1d(r.choice(nB, budget, replace=False), prev)[: budget - budget // 2]
+    new = np.sort(np.concatenate([prev[keep], fresh]))
+    prev_pages = r.permutation(budget).astype(np.int32)
+    k_src = W.normal((L, H_kv, c["N"], D), c["seed"], W.T_K, "bf16", DEV)
+    k_pool = W.normal((L, H_kv, 32 * budget, D), 65, W.T_K, "bf16", DEV)
+    k_init = k_pool.clone()
+    i32 = lambda a: torch.tensor(np.asarray(a), dtype=torch.int32, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    pages, rank, outgoing, counts = kvs.kvs_working_set_update(
+        k_src, None, i32(prev), i32(prev_pages), i32(new), 0, 1e6, k_pool, None, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    pages_o, rank_o, out_o = oracle.working_set_diff(prev.tolist(), prev_pages.tolist(), new.tolist(), budget)
+    np.testing.assert_array_equal(pages.cpu().numpy(), pages_o)
+    np.testing.assert_array_equal(rank.cpu().numpy(), rank_o)
+    np.testing.assert_array_equal(outgoing[:int(counts[2].item())].cpu().numpy(), out_o)
+    for i in r.choice(len(new), 24, replace=False):
+        l, g, p = int(r.integers(L)), int(r.integers(H_kv)), int(pages_o[i])
+        rows = slice(32 * p, 32 * p + 32)
+        if rank_o[i] >= 0:
+            want = oracle.rope_rotate(oracle.bf16_bits_to_f64(host(k_init[l, g, rows])),
+                                      np.full(32, 32 * (i - rank_o[i])), 1e6)
+        else:
+            b = int(new[i])
+            want = oracle.rope_rotate(oracle.bf16_bits_to_f64(host(k_src[l, g, 32 * b:32 * b + 32])),
+                                      32 * i + np.arange(32), 1e6)
+        assert_within_ulp(bits(k_pool[l, g, rows]), want, f"page {p} (rank {i})", atol=1e-6)
+    del k_src, k_pool, k_init
