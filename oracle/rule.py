@@ -27,11 +27,13 @@ def forced_mask(N, pi, q_s, q_e):
     return F
 
 
-def rule_score(K, M, pi, q_s, q_e):
+def rule_score(K, M, pi, q_s, q_e, exclude=None):
     """rule_j for j in [0, N); 0 on the forced set.
 
     K: [L, H_kv, N, D] post-RoPE keys (float or bf16 bits).
     M: [L, H_q, D] QueryMemory.
+    exclude: optional boolean [N]; those positions are not candidates either
+    (and score 0), used for positions without a key.
     """
     K = np.asarray(K)
     M = np.asarray(M, dtype=np.float64)
@@ -41,6 +43,8 @@ def rule_score(K, M, pi, q_s, q_e):
         raise ValueError("shape mismatch between K and M")
     G = H_q // H_kv
     cand = ~forced_mask(N, pi, q_s, q_e)
+    if exclude is not None:
+        cand &= ~np.asarray(exclude, dtype=bool)
     rule = np.zeros(N, dtype=np.float64)
     if not cand.any():
         return rule
@@ -54,3 +58,25 @@ def rule_score(K, M, pi, q_s, q_e):
                 a /= a.sum()
                 rule[cand] += a                        # Eq. (3)
     return rule
+
+
+def rule_score_paged(K_pool, slots, M, pi, q_s, q_e):
+    """Rule score with K read in place from a paged pool through the slot map.
+
+    IntentKV Sec. 3.1 gives the request's slot map S_r; the layout layer
+    (abstract, Sec. 1) keeps survivors in their slots of the paged cache and
+    sends dropped positions to a dead slot.  Reading: key row j of KV head g
+    in layer l is K_pool[l, S_r[j], g, :] (token-major pool, as SGLang and vLLM
+    store it); a position whose slot lies outside the pool has no key, so it
+    is not a candidate and scores 0.
+
+    K_pool: [L, pool_size, H_kv, D]; slots: [N] integers.
+    """
+    K_pool = as_f64(K_pool)
+    slots = np.asarray(slots, dtype=np.int64)
+    L, P, H_kv, D = K_pool.shape
+    N = slots.shape[0]
+    live = (slots >= 0) & (slots < P)
+    K = np.zeros((L, H_kv, N, D), dtype=np.float64)
+    K[:, :, live, :] = K_pool[:, slots[live], :, :].transpose(0, 2, 1, 3)
+    return rule_score(K, M, pi, q_s, q_e, exclude=~live)

@@ -110,6 +110,41 @@ def test_rule_brute_force_gqa_forced():
     np.testing.assert_allclose(got, _rule_brute(K, M, 2, 9, 11), rtol=1e-13, atol=1e-15)
 
 
+def test_rule_paged_equals_dense_under_any_slot_layout():
+    # A pool holding K[l, g, j] at slot perm[j] read through slots = perm gives the dense
+    # score exactly: catches a transposed pool index or reading slot j instead of S[j].
+    r = rng(14)
+    L, Hq, Hkv, N, D, P = 2, 8, 2, 40, 16, 64
+    K = r.standard_normal((L, Hkv, N, D))
+    M = r.standard_normal((L, Hq, D))
+    perm = r.permutation(P)[:N]
+    pool = r.standard_normal((L, P, Hkv, D))
+    pool[:, perm, :, :] = K.transpose(0, 2, 1, 3)
+    np.testing.assert_array_equal(oracle.rule_score_paged(pool, perm, M, 3, 30, 35),
+                                  oracle.rule_score(K, M, 3, 30, 35))
+
+
+def test_rule_paged_dead_slots_brute_force():
+    # Positions on the dead slot are no candidates: brute force over the live positions only.
+    r = rng(15)
+    L, Hq, Hkv, N, D, P = 1, 4, 2, 11, 5, 16
+    pool = r.standard_normal((L, P, Hkv, D))
+    M = r.standard_normal((L, Hq, D))
+    slots = r.permutation(P)[:N].copy()
+    slots[[2, 5, 6]] = -1
+    got = oracle.rule_score_paged(pool, slots, M, 1, 9, 10)
+    live = [j for j in range(N) if slots[j] >= 0 and not (j < 1 or 9 <= j < 10)]
+    want = np.zeros(N)
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        lg = {j: float(pool[0, slots[j], g] @ M[0, h]) / math.sqrt(D) for j in live}
+        z = sum(math.exp(v) for v in lg.values())
+        for j in live:
+            want[j] += math.exp(lg[j]) / z
+    np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-15)
+    assert got[2] == got[5] == got[6] == 0.0
+
+
 def test_rule_mass_and_forced_zero():
     r = rng(6)
     L, Hq, Hkv, N, D = 3, 8, 2, 200, 16
