@@ -87,8 +87,31 @@ kvs_status kvs_rule_score(const void* K, int32_t k_dtype, const float* M, int32_
   pi = pi > N ? N : pi;
   int64_t s = q_s, e = q_e;
   clip_range(N, s, e);
-  return hip_status(kvs_launch_rule(K, k_dtype, M, L, H_q, H_kv, D, N, pi, s, e, rule, ws,
+  return hip_status(kvs_launch_rule(K, k_dtype, nullptr, 0, M, L, H_q, H_kv, D, N, pi, s, e, rule, ws,
                                     as_stream(stream)));
+}
+
+kvs_status kvs_rule_score_paged(const void* K_pool, int32_t k_dtype, const int64_t* slots,
+                                int64_t pool_size, const float* M, int32_t L, int32_t H_q,
+                                int32_t H_kv, int32_t D, int64_t N, int64_t pi, int64_t q_s,
+                                int64_t q_e, float* rule, void* ws, size_t ws_bytes, void* stream) {
+  if (!K_pool || !M || !rule || !a16(K_pool)) return KVS_ERR_ARG;
+  if (k_dtype != KVS_F32 && k_dtype != KVS_BF16) return KVS_ERR_DTYPE;
+  if (L < 1 || H_q < 1 || H_kv < 1 || N < 0 || pool_size < 1 || pi < 0 || q_s < 0 || q_e < q_s)
+    return KVS_ERR_ARG;
+  if (N > 0 && !slots) return KVS_ERR_ARG;
+  if (H_q % H_kv != 0 || N > kMaxIndex || pool_size > kMaxIndex || numel4(L, pool_size, H_kv, D) < 0 ||
+      numel4(L, H_q, N, 1) < 0 || (int64_t)L * H_kv > 65535)
+    return KVS_ERR_SHAPE;
+  if (!head_dim_ok(D) || H_q / H_kv > 16) return KVS_ERR_UNSUPPORTED;
+  if (N == 0) return KVS_OK;
+  const size_t need = kvs_rule_ws_bytes(L, H_q, H_kv, N);
+  if (!ws || ws_bytes < need || !a16(ws)) return KVS_ERR_WORKSPACE;
+  pi = pi > N ? N : pi;
+  int64_t s = q_s, e = q_e;
+  clip_range(N, s, e);
+  return hip_status(kvs_launch_rule(K_pool, k_dtype, slots, pool_size, M, L, H_q, H_kv, D, N, pi, s, e,
+                                    rule, ws, as_stream(stream)));
 }
 
 size_t kvs_topk_workspace(int64_t n) {

@@ -55,9 +55,11 @@ inline unsigned ceil_div(int64_t a, int64_t b) { return (unsigned)((a + b - 1) /
 hipError_t kvs_launch_qmem(const void* q, int dtype, int L, int H_q, int S, int D, float decay,
                            int first_turn, float* M, hipStream_t st);
 
-hipError_t kvs_launch_rule(const void* K, int dtype, const float* M, int L, int H_q, int H_kv,
-                           int D, int64_t N, int64_t pi, int64_t q_s, int64_t q_e, float* rule,
-                           void* ws, hipStream_t st);
+// slots == nullptr: K is dense [L, H_kv, N, D]; otherwise K is the token-major
+// pool [L, pool_size, H_kv, D] read through the slot map slots[N].
+hipError_t kvs_launch_rule(const void* K, int dtype, const int64_t* slots, int64_t pool_size,
+                           const float* M, int L, int H_q, int H_kv, int D, int64_t N, int64_t pi,
+                           int64_t q_s, int64_t q_e, float* rule, void* ws, hipStream_t st);
 size_t kvs_rule_ws_bytes(int L, int H_q, int H_kv, int64_t N);
 
 hipError_t kvs_launch_topk(const float* score, int64_t n, int64_t f0b, int64_t f0e, int64_t f1b,

@@ -39,10 +39,26 @@ __device__ __forceinline__ void online_add(float& m, float& s, float x) {
   m = mn;
 }
 
+// Paged keys: a token-major pool K_pool[l, slot, g, :] read in place through
+// the slot map; a chunk's slots are staged in LDS as int32 (-1 for a slot
+// outside the pool, whose position then drops out like a forced one).
+template <bool PAGED>
+__device__ __forceinline__ void stage_slots(int32_t* sslot, const int64_t* __restrict__ slots, int64_t row0,
+                                            int64_t row1, int64_t pool_size) {
+  if constexpr (PAGED) {
+    for (int64_t j = row0 + threadIdx.x; j < row1; j += 256) {
+      const int64_t sl = slots[j];
+      sslot[j - row0] = (sl >= 0 && sl < pool_size) ? (int32_t)sl : -1;
+    }
+    __syncthreads();
+  }
+}
+
 // NHG = number of 8-head groups (G <= 8*NHG).
-template <int D, int NHG>
+template <int D, int NHG, bool PAGED>
 __global__ __launch_bounds__(256) void rule_logits_mfma(
-    const uint16_t* __restrict__ K, const float* __restrict__ M, int H_q, int H_kv, int G,
+    const uint16_t* __restrict__ K, const int64_t* __restrict__ slots, int64_t pool_size,
+    const float* __restrict__ M, int H_q, int H_kv, int G,
     int64_t N, int64_t pi, int64_t q_s, int64_t q_e, float scale_log2, float* __restrict__ spill,
     float2* __restrict__ partials, int n_chunks) {
   constexpr int KS = D / 32;            // MFMA k-steps per row
@@ -85,6 +101,17 @@ __global__ __launch_bounds__(256) void rule_logits_mfma(
   const int64_t row1 = min(N, row0 + (int64_t)kChunk);
   const uint16_t* Kb = K + (size_t)lg * (size_t)N * D;
   const size_t head0 = (size_t)l * H_q + (size_t)g * G;
+  __shared__ int32_t sslot[PAGED ? kChunk : 1];
+  stage_slots<PAGED>(sslot, slots, row0, row1, pool_size);
+  // K row j of group (l, g), or null when the position has no row in the pool
+  auto row_ptr = [&](int64_t j) -> const uint16_t* {
+    if constexpr (PAGED) {
+      const int32_t sl = sslot[j - row0];
+      return sl < 0 ? nullptr : K + (((size_t)l * pool_size + sl) * H_kv + g) * D;
+    } else {
+      return Kb + (size_t)j * D;
+    }
+  };
 
   // K rows are read whole (16 lanes x 16 B = one 256-byte row, 4 rows per
   // instruction) with non-temporal loads: K is touched once, and full-row
@@ -101,8 +128,8 @@ __global__ __launch_bounds__(256) void rule_logits_mfma(
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int64_t j = t0 + i * RPI + lr;
-      w[i] = j < row1 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Kb + (size_t)j * D) + lc)
-                      : u32x4{0u, 0u, 0u, 0u};
+      const uint16_t* p = j < row1 ? row_ptr(j) : nullptr;
+      w[i] = p ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + lc) : u32x4{0u, 0u, 0u, 0u};
     }
   };
   auto to_operand = [&](const u32x4* w, bf16x8* B) {
@@ -123,7 +150,7 @@ __global__ __launch_bounds__(256) void rule_logits_mfma(
     to_operand(W, B);
     const int64_t j = t0 + r;
     const bool vj = j < row1;
-    const bool forced = is_forced(j, pi, q_s, q_e);
+    const bool forced = is_forced(j, pi, q_s, q_e) || (PAGED && vj && sslot[j - row0] < 0);
 #pragma unroll
     for (int hg = 0; hg < NHG; ++hg) {
       f32x4 c = {0.f, 0.f, 0.f, 0.f};
@@ -169,9 +196,10 @@ __global__ __launch_bounds__(256) void rule_logits_mfma(
 }
 
 // fp32 keys: plain VALU dot products, one row per thread, same outputs.
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256) void rule_logits_f32(
-    const float* __restrict__ K, const float* __restrict__ M, int H_q, int H_kv, int G, int64_t N,
+    const float* __restrict__ K, const int64_t* __restrict__ slots, int64_t pool_size,
+    const float* __restrict__ M, int H_q, int H_kv, int G, int64_t N,
     int64_t pi, int64_t q_s, int64_t q_e, float scale_log2, float* __restrict__ spill,
     float2* __restrict__ partials, int n_chunks) {
   constexpr int GMAX = 16;
@@ -190,9 +218,14 @@ __global__ __launch_bounds__(256) void rule_logits_f32(
   const int64_t row0 = (int64_t)chunk * kChunk;
   const int64_t row1 = min(N, row0 + (int64_t)kChunk);
   const float* Kb = K + (size_t)lg * (size_t)N * D;
+  __shared__ int32_t sslot[PAGED ? kChunk : 1];
+  stage_slots<PAGED>(sslot, slots, row0, row1, pool_size);
   for (int64_t j = row0 + threadIdx.x; j < row1; j += 256) {
-    const float* krow = Kb + (size_t)j * D;
-    const bool forced = is_forced(j, pi, q_s, q_e);
+    int32_t sl = 0;
+    if constexpr (PAGED) sl = sslot[j - row0];
+    const float* krow = PAGED ? K + (((size_t)l * pool_size + (sl < 0 ? 0 : sl)) * H_kv + g) * D
+                              : Kb + (size_t)j * D;
+    const bool forced = is_forced(j, pi, q_s, q_e) || sl < 0;
 #pragma unroll
     for (int h = 0; h < GMAX; ++h) {
       if (h < G) {
@@ -264,9 +297,9 @@ size_t kvs_rule_ws_bytes(int L, int H_q, int /*H_kv*/, int64_t N) {
   return align256(LH * (size_t)N * 4) + align256(LH * n_chunks * 8) + align256(LH * 4);
 }
 
-hipError_t kvs_launch_rule(const void* K, int dtype, const float* M, int L, int H_q, int H_kv,
-                           int D, int64_t N, int64_t pi, int64_t q_s, int64_t q_e, float* rule,
-                           void* ws, hipStream_t st) {
+hipError_t kvs_launch_rule(const void* K, int dtype, const int64_t* slots, int64_t pool_size,
+                           const float* M, int L, int H_q, int H_kv, int D, int64_t N, int64_t pi,
+                           int64_t q_s, int64_t q_e, float* rule, void* ws, hipStream_t st) {
   const int LH = L * H_q;
   const int G = H_q / H_kv;
   const int n_chunks = (int)ceil_div(N, kChunk);
@@ -277,23 +310,27 @@ hipError_t kvs_launch_rule(const void* K, int dtype, const float* M, int L, int 
   w += align256((size_t)LH * n_chunks * 8);
   float* lse2 = reinterpret_cast<float*>(w);
   const float scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)D));
+  const bool paged = slots != nullptr;
   dim3 grid(n_chunks, L * H_kv), block(256);
   if (dtype == 1) {
     const uint16_t* Kb = static_cast<const uint16_t*>(K);
-#define RULE_LAUNCH(DD, NH)                                                                    \
-  hipLaunchKernelGGL((rule_logits_mfma<DD, NH>), grid, block, 0, st, Kb, M, H_q, H_kv, G, N, pi, \
-                     q_s, q_e, scale_log2, spill, partials, n_chunks)
-    if (D == 128) { if (G <= 8) RULE_LAUNCH(128, 1); else RULE_LAUNCH(128, 2); }
-    else { if (G <= 8) RULE_LAUNCH(64, 1); else RULE_LAUNCH(64, 2); }
+#define RULE_LAUNCH(DD, NH, PG)                                                                     \
+  hipLaunchKernelGGL((rule_logits_mfma<DD, NH, PG>), grid, block, 0, st, Kb, slots, pool_size, M, H_q, \
+                     H_kv, G, N, pi, q_s, q_e, scale_log2, spill, partials, n_chunks)
+#define RULE_LAUNCH_D(DD) \
+  if (paged) { if (G <= 8) RULE_LAUNCH(DD, 1, true); else RULE_LAUNCH(DD, 2, true); } \
+  else { if (G <= 8) RULE_LAUNCH(DD, 1, false); else RULE_LAUNCH(DD, 2, false); }
+    if (D == 128) { RULE_LAUNCH_D(128) } else { RULE_LAUNCH_D(64) }
+#undef RULE_LAUNCH_D
 #undef RULE_LAUNCH
   } else {
     const float* Kf = static_cast<const float*>(K);
-    if (D == 128)
-      hipLaunchKernelGGL((rule_logits_f32<128>), grid, block, 0, st, Kf, M, H_q, H_kv, G, N, pi, q_s,
-                         q_e, scale_log2, spill, partials, n_chunks);
-    else
-      hipLaunchKernelGGL((rule_logits_f32<64>), grid, block, 0, st, Kf, M, H_q, H_kv, G, N, pi, q_s,
-                         q_e, scale_log2, spill, partials, n_chunks);
+#define RULE_F32(DD, PG)                                                                            \
+  hipLaunchKernelGGL((rule_logits_f32<DD, PG>), grid, block, 0, st, Kf, slots, pool_size, M, H_q, H_kv, \
+                     G, N, pi, q_s, q_e, scale_log2, spill, partials, n_chunks)
+    if (D == 128) { if (paged) RULE_F32(128, true); else RULE_F32(128, false); }
+    else { if (paged) RULE_F32(64, true); else RULE_F32(64, false); }
+#undef RULE_F32
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -28,6 +28,8 @@ _SIGNATURES = [
     ("kvs_qmem_update", _I32, [_P, _I32, _I32, _I32, _I32, _I32, _F32, _I32, _P, _P]),
     ("kvs_rule_score_workspace", _SZ, [_I32, _I32, _I32, _I64]),
     ("kvs_rule_score", _I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _I64, _I64, _I64, _I64, _P, _P, _SZ, _P]),
+    ("kvs_rule_score_paged", _I32, [_P, _I32, _P, _I64, _P, _I32, _I32, _I32, _I32, _I64, _I64, _I64,
+                                    _I64, _P, _P, _SZ, _P]),
     ("kvs_topk_workspace", _SZ, [_I64]),
     ("kvs_topk_select", _I32, [_P, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
     ("kvs_slotmap_redirect", _I32, [_P, _P, _I64, _I64, _P, _P]),
@@ -143,6 +145,27 @@ def kvs_rule_score(K, M, pi, q_s, q_e, rule=None, ws=None):
     _check("kvs_rule_score", load().kvs_rule_score(
         _ptr(K), _dtype_code(K), _ptr(M), L, H_q, H_kv, D, N, pi, q_s, q_e, _ptr(rule),
         _ptr(ws), ws.numel(), _stream(K)))
+    return rule
+
+
+def kvs_rule_score_paged(K_pool, slots, M, pi, q_s, q_e, rule=None, ws=None):
+    """rule [N] from the token-major pool K_pool [L, pool_size, H_kv, D] read through slots [N] (int64)."""
+    _dev(K_pool, slots, M, rule, ws)
+    L, pool_size, H_kv, D = K_pool.shape
+    _need(M.dtype == torch.float32 and M.dim() == 3 and M.shape[0] == L and M.shape[2] == D,
+          "M must be float32 [L, H_q, D]")
+    if slots.dtype != torch.int64:
+        raise TypeError("slots must be int64")
+    H_q, N = M.shape[1], slots.numel()
+    if rule is None:
+        rule = torch.empty(N, dtype=torch.float32, device=K_pool.device)
+    _need(rule.dtype == torch.float32 and rule.numel() == N, "rule must be float32 [N]")
+    if ws is None:
+        ws = torch.empty(max(1, kvs_rule_score_workspace(L, H_q, H_kv, N)), dtype=torch.uint8,
+                         device=K_pool.device)
+    _check("kvs_rule_score_paged", load().kvs_rule_score_paged(
+        _ptr(K_pool), _dtype_code(K_pool), _ptr(slots), pool_size, _ptr(M), L, H_q, H_kv, D, N, int(pi),
+        int(q_s), int(q_e), _ptr(rule), _ptr(ws), ws.numel(), _stream(K_pool)))
     return rule
 
 

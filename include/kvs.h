@@ -98,6 +98,25 @@ kvs_status kvs_rule_score(const void* K, int32_t k_dtype, const float* M, int32_
                           int64_t q_s, int64_t q_e, float* rule, void* ws, size_t ws_bytes,
                           void* stream);
 
+/*
+ * Rule score reading K in place from a paged pool -- IntentKV Sec. 3.1
+ * (slot map S_r of the request) and the layout layer of the abstract and
+ * Sec. 1 (SGLang/vLLM paged caches; survivors keep their slot).  Same result
+ * as kvs_rule_score on K[l,g,j,:] = K_pool[l, slots[j], g, :], with one more
+ * rule: a position whose slot lies outside [0, pool_size) -- the dead slot
+ * of an earlier eviction -- has no key, so it drops out of every softmax like
+ * a forced position and scores 0.
+ *   K_pool   [L, pool_size, H_kv, D] token-major pool, dtype k_dtype.
+ *   slots    [N] int64 slot map (device).
+ *   ws       device workspace of >= kvs_rule_score_workspace(L, H_q, H_kv, N) bytes.
+ * Other arguments and errors as kvs_rule_score (pool_size < 1 -> KVS_ERR_ARG).
+ */
+kvs_status kvs_rule_score_paged(const void* K_pool, int32_t k_dtype, const int64_t* slots,
+                                int64_t pool_size, const float* M, int32_t L, int32_t H_q,
+                                int32_t H_kv, int32_t D, int64_t N, int64_t pi, int64_t q_s,
+                                int64_t q_e, float* rule, void* ws, size_t ws_bytes,
+                                void* stream);
+
 /* Workspace bytes kvs_topk_select needs for n scores. */
 size_t kvs_topk_workspace(int64_t n);
 

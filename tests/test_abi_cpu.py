@@ -27,7 +27,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = header_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(kvs.ENTRY_POINTS) == names
@@ -107,6 +107,24 @@ def test_topk_slot_meank_rerope_rejections(lib):
     assert r(FAKE, FAKE, 640, FAKE, None, 3, 2, 2, 128, 64, 0, 1e6, FAKE, FAKE, 8, None, None) == 4
     assert r(FAKE, FAKE, 640, FAKE, None, 3, 2, 2, 128, 32, 0, -1.0, FAKE, FAKE, 8, None, None) == 1
     assert r(FAKE, FAKE, 640, None, None, 3, 2, 2, 128, 32, 0, 1e6, FAKE, FAKE, 8, None, None) == 1
+
+
+def test_rule_paged_rejections(lib):
+    f = lib.kvs_rule_score_paged
+    ws = lib.kvs_rule_score_workspace(2, 4, 2, 1024)
+    ok = [FAKE, 1, FAKE, 2048, FAKE, 2, 4, 2, 128, 1024, 16, 992, 1024, FAKE, FAKE, ws, None]
+
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a2=None) == 1            # no slot map
+    assert call(a3=0) == 1               # empty pool
+    assert call(a1=5) == 3               # dtype
+    assert call(a7=3) == 2               # H_q % H_kv
+    assert call(a8=96) == 4
+    assert call(a15=ws - 1) == 5
 
 
 def test_working_set_rejections(lib):

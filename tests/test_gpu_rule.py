@@ -154,6 +154,52 @@ def test_rule_full_size(name):
     assert_valid_selection(want, idx[:nk].cpu().numpy(), F, c["C"] - int(F.sum()), 2 * RULE_RTOL)
 
 
+# ---------------------------------------------------------------- rule score through the slot map
+
+def _paged_inputs(L, H_q, H_kv, D, N, pool_size, dtype, seed, dead=()):
+    """Token-major pool with the cache's rows at a seeded permutation of slots (some dead)."""
+    K = W.normal((L, H_kv, N, D), seed, W.T_K, dtype, DEV)
+    pool = W.normal((L, pool_size, H_kv, D), seed, W.T_K + 30, dtype, DEV)
+    perm = torch.from_numpy(np.random.default_rng(seed).permutation(pool_size)[:N].copy()).to(DEV)
+    pool[:, perm] = K.permute(0, 2, 1, 3)
+    slots = perm.clone()
+    if len(dead):
+        slots[list(dead)] = -1
+    M = W.memory_vectors(L, H_q, D, seed, DEV)
+    return K, pool, slots, M
+
+
+@pytest.mark.parametrize("dtype,L,H_q,H_kv,D,N,pool_size,dead", [
+    ("bf16", 2, 32, 8, 128, 5000, 6000, (7, 8, 4000)),
+    ("bf16", 1, 24, 2, 64, 2100, 2100, ()),
+    ("f32", 2, 4, 2, 64, 1024, 1500, (0, 1023)),
+])
+def test_rule_paged_against_oracle(dtype, L, H_q, H_kv, D, N, pool_size, dead):
+    K, pool, slots, M = _paged_inputs(L, H_q, H_kv, D, N, pool_size, dtype, 15, dead)
+    pi, q_s, q_e = 16, N - 64, N
+    got = kvs.kvs_rule_score_paged(pool, slots, M, pi, q_s, q_e)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    want = oracle.rule_score_paged(host(pool), slots.cpu().numpy(), host(M), pi, q_s, q_e)
+    out = oracle.forced_mask(N, pi, q_s, q_e)
+    out[list(dead)] = True
+    assert np.all(got[out] == 0.0)
+    assert_rel(got[~out], want[~out], RULE_RTOL, f"paged rule {dtype} D{D}")
+
+
+@pytest.mark.parametrize("name", ["rule-8b"])
+def test_rule_paged_full_size_equals_dense(name):
+    """At full size, the pool read through a permuted slot map gives the dense scores bit for bit."""
+    c = W.config(name)
+    L, H_q, H_kv, D, N = c["L"], c["H_q"], c["H_kv"], c["D"], c["N"]
+    K, pool, slots, M = _paged_inputs(L, H_q, H_kv, D, N, N + 4096, "bf16", 16)
+    dense = kvs.kvs_rule_score(K, M, c["pi"], c["q_s"], c["q_e"])
+    paged = kvs.kvs_rule_score_paged(pool, slots, M, c["pi"], c["q_s"], c["q_e"])
+    torch.cuda.synchronize()
+    assert torch.equal(dense, paged)
+    del K, pool
+
+
 # ---------------------------------------------------------------- top-k
 
 def check_topk(score, f0, f1, C):
