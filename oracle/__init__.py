@@ -32,7 +32,7 @@ pairing of the pages' models, and which layer-heads KVMEM lets vote.
 
 from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits, as_f64
 from .qmem import qmem_update, enc_span
-from .rule import forced_mask, rule_score, rule_score_paged
+from .rule import forced_mask, rule_score, rule_score_paged, window_score
 from .select import topk_select, slotmap_redirect, meank_select
 from .rope import rope_omega, rope_rotate
 from .meank import meank_build, meank_append, meank_score, candidate_blocks
@@ -42,7 +42,7 @@ from .workset import working_set_diff, working_set_update
 __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "as_f64",
     "qmem_update", "enc_span",
-    "forced_mask", "rule_score", "rule_score_paged",
+    "forced_mask", "rule_score", "rule_score_paged", "window_score",
     "topk_select", "slotmap_redirect", "meank_select",
     "rope_omega", "rope_rotate",
     "meank_build", "meank_append", "meank_score", "candidate_blocks",

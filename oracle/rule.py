@@ -80,3 +80,38 @@ def rule_score_paged(K_pool, slots, M, pi, q_s, q_e):
     K = np.zeros((L, H_kv, N, D), dtype=np.float64)
     K[:, :, live, :] = K_pool[:, slots[live], :, :].transpose(0, 2, 1, 3)
     return rule_score(K, M, pi, q_s, q_e, exclude=~live)
+
+
+def window_score(K, Qw, pi, q_s, q_e):
+    """Window score: SnapKV's window of W query rows, the form IntentKV Sec. 3.2
+    says Eq. (3) replaces with a single accumulated query state.
+
+    Reading: for every layer l, query head h and window row w, a softmax over
+    the candidate positions H (Sec. 3.1) of Qw[l,h,w] . K[l,g(h),j] / sqrt(D);
+    score_j sums them over (l, h, w).  SnapKV's pooling and per-head selection
+    are not described by the pages and are left out.
+
+    K: [L, H_kv, N, D]; Qw: [L, H_q, W, D] post-RoPE window query rows.
+    """
+    K = np.asarray(K)
+    Qw = as_f64(Qw)
+    L, H_kv, N, D = K.shape
+    H_q, W = Qw.shape[1], Qw.shape[2]
+    if Qw.shape[0] != L or Qw.shape[3] != D or H_q % H_kv != 0:
+        raise ValueError("shape mismatch between K and Qw")
+    G = H_q // H_kv
+    cand = ~forced_mask(N, pi, q_s, q_e)
+    score = np.zeros(N, dtype=np.float64)
+    if not cand.any() or W == 0:
+        return score
+    scale = 1.0 / math.sqrt(D)
+    for l in range(L):
+        for g in range(H_kv):
+            Kc = as_f64(K[l, g])[cand]                      # [|H|, D]
+            for h in range(g * G, (g + 1) * G):
+                S = (Qw[l, h] @ Kc.T) * scale                # [W, |H|]
+                S -= S.max(axis=1, keepdims=True)
+                P = np.exp(S)
+                P /= P.sum(axis=1, keepdims=True)            # softmax over H per window row
+                score[cand] += P.sum(axis=0)
+    return score

@@ -145,6 +145,35 @@ def test_rule_paged_dead_slots_brute_force():
     assert got[2] == got[5] == got[6] == 0.0
 
 
+def test_window_one_row_is_the_rule_score():
+    # A window of one row holding M is exactly the rule score (Eq. 3 replaces the window by M).
+    r = rng(16)
+    K = r.standard_normal((2, 2, 50, 8))
+    M = r.standard_normal((2, 4, 8))
+    np.testing.assert_allclose(oracle.window_score(K, M[:, :, None, :], 3, 40, 45),
+                               oracle.rule_score(K, M, 3, 40, 45), rtol=1e-13, atol=1e-16)
+
+
+def test_window_brute_force_mass_and_additivity():
+    r = rng(17)
+    L, Hq, Hkv, N, D, Wn = 1, 4, 2, 12, 5, 3
+    K = r.standard_normal((L, Hkv, N, D))
+    Qw = r.standard_normal((L, Hq, Wn, D))
+    got = oracle.window_score(K, Qw, 2, 8, 10)
+    H = [j for j in range(N) if not (j < 2 or 8 <= j < 10)]
+    want = np.zeros(N)
+    for h in range(Hq):
+        for w in range(Wn):
+            lg = {j: float(Qw[0, h, w] @ K[0, h // 2, j]) / math.sqrt(D) for j in H}
+            z = sum(math.exp(v) for v in lg.values())
+            for j in H:
+                want[j] += math.exp(lg[j]) / z
+    np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-16)
+    assert abs(got.sum() - L * Hq * Wn) < 1e-12                  # each row's softmax sums to one
+    split = oracle.window_score(K, Qw[:, :, :1], 2, 8, 10) + oracle.window_score(K, Qw[:, :, 1:], 2, 8, 10)
+    np.testing.assert_allclose(got, split, rtol=1e-13)
+
+
 def test_rule_mass_and_forced_zero():
     r = rng(6)
     L, Hq, Hkv, N, D = 3, 8, 2, 200, 16
