@@ -220,6 +220,26 @@ kvs_status kvs_rerope_scatter(const void* k_src, const void* v_src, int64_t src_
                                       err_flag, as_stream(stream)));
 }
 
+size_t kvs_window_score_workspace(int32_t L, int32_t H_q, int32_t H_kv, int64_t W, int64_t N) {
+  if (L < 1 || H_q < 1 || H_kv < 1 || H_q % H_kv || W < 0 || N < 0 || N > kMaxIndex) return 0;
+  return kvs_window_ws_bytes(L, H_q, H_kv, W, N);
+}
+
+kvs_status kvs_window_score(const void* K, const void* Qw, int32_t L, int32_t H_q, int32_t H_kv,
+                            int32_t D, int64_t N, int64_t W, int64_t pi, int64_t q_s, int64_t q_e,
+                            float* score, void* ws, size_t ws_bytes, void* stream) {
+  if (!K || !Qw || !score || !a16(K) || !a16(Qw)) return KVS_ERR_ARG;
+  if (L < 1 || H_q < 1 || H_kv < 1 || N < 0 || W < 1 || pi < 0 || q_s < 0 || q_e < q_s) return KVS_ERR_ARG;
+  if (H_q % H_kv != 0 || N > kMaxIndex || numel4(L, H_kv, N, D) < 0 || numel4(L, H_q, W, D) < 0 ||
+      (int64_t)L * H_kv > 65535 || (int64_t)(H_q / H_kv) * W > (int64_t)1 << 24)
+    return KVS_ERR_SHAPE;
+  if (D != 128) return KVS_ERR_UNSUPPORTED;
+  if (N == 0) return KVS_OK;
+  const size_t need = kvs_window_ws_bytes(L, H_q, H_kv, W, N);
+  if (!ws || ws_bytes < need || !a16(ws)) return KVS_ERR_WORKSPACE;
+  return hip_status(kvs_launch_window(K, Qw, L, H_q, H_kv, W, N, pi, q_s, q_e, score, ws, as_stream(stream)));
+}
+
 size_t kvs_working_set_workspace(int64_t pool_pages) {
   if (pool_pages < 0 || pool_pages > kMaxIndex) return 0;
   return kvs_workset_ws_bytes(pool_pages);

@@ -96,3 +96,7 @@ hipError_t kvs_launch_workset(const void* k_src, const void* v_src, int64_t src_
                               int64_t pool_pages, int32_t* pages_out, int32_t* old_rank_out,
                               int32_t* outgoing_out, int64_t* counts, int32_t* err_flag, void* ws,
                               hipStream_t st);
+
+size_t kvs_window_ws_bytes(int L, int H_q, int H_kv, int64_t W, int64_t N);
+hipError_t kvs_launch_window(const void* K, const void* Qw, int L, int H_q, int H_kv, int64_t W, int64_t N,
+                             int64_t pi, int64_t q_s, int64_t q_e, float* score, void* ws, hipStream_t st);

@@ -162,14 +162,19 @@ __device__ __forceinline__ void step_mma_epi(const bf16x8* A, const bf16x8* B0, 
 // Pass-1 accumulation of one C tile's sum `a` taken against reference m.  The
 // reference only moves when a tile could overflow: then the tile is redone
 // against its exact max (rare; terms below 2^-126 of the reference are
-// negligible against the terms that set it).
-template <bool TAIL>
+// negligible against the terms that set it).  MASK tiles (the last one, or
+// one that meets the excluded span [h0, h1)) are always redone with the
+// positions past c1 or inside the span taken out.
+template <bool MASK>
 __device__ __forceinline__ void lse_fold(const f32x16& c, float scale, float& m, float& s, float a,
-                                         int64_t b0, int h, int64_t c1) {
-  if (TAIL || !(a <= kRebase)) {
+                                         int64_t b0, int h, int64_t c1, int64_t h0, int64_t h1) {
+  if (MASK || !(a <= kRebase)) {
     float x[16];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) x[v] = (TAIL && b0 + c_row(v, h) >= c1) ? -INFINITY : c[v];
+    for (int v = 0; v < 16; ++v) {
+      const int64_t pos = b0 + c_row(v, h);
+      x[v] = (MASK && (pos >= c1 || (pos >= h0 && pos < h1))) ? -INFINITY : c[v];
+    }
     float t = fmaxf(fmaxf(x[0], x[1]), x[2]);
 #pragma unroll
     for (int v = 3; v < 15; v += 2) t = fmaxf(fmaxf(t, x[v]), x[v + 1]);
@@ -199,12 +204,19 @@ __device__ __forceinline__ void xcd_map(int T, int LG, int& lg, int& tile) {
   }
 }
 
-template <bool PASS1>
+// Columns (streamed in pass 1, persistent in pass 2) are the candidates
+// [c0, c1).  With SPAN (the window score) they also exclude [h0, h1), and
+// pass 1 may split the candidate range over n_split workgroups (gridDim.y);
+// each then writes a (max, sum) partial per row to part1 and meank_lse_merge
+// combines them.  R_b instantiates SPAN = false, which compiles both out.
+template <bool PASS1, bool SPAN>
 __global__ __launch_bounds__(256, 2) void meank_pass(const uint16_t* __restrict__ Q,
                                                      const uint16_t* __restrict__ index, int LG,
                                                      int64_t rows, int64_t rows_pad, int64_t nB,
-                                                     int64_t c0, int64_t c1, int T, float scale,
+                                                     int64_t c0, int64_t c1, int64_t h0, int64_t h1,
+                                                     int T, float scale, int n_split,
                                                      float* __restrict__ lse2,
+                                                     float2* __restrict__ part1,
                                                      float* __restrict__ colpart) {
   __shared__ __attribute__((aligned(16))) char tiles[2][kTile * kLdsRow];
   __shared__ __attribute__((aligned(16))) float lses[2][kTile];
@@ -226,9 +238,23 @@ __global__ __launch_bounds__(256, 2) void meank_pass(const uint16_t* __restrict_
     load_persistent(Ig, c0 + p0 + n, c0 + p0 + n < c1, h, B0);
     load_persistent(Ig, c0 + p0 + 32 + n, c0 + p0 + 32 + n < c1, h, B1);
   }
-  // streamed operand: pass 1 = index tiles over [c0, c1), pass 2 = query tiles over [0, rows)
+  // streamed operand: pass 1 = index tiles over this split of [c0, c1), pass 2 = query tiles over [0, rows)
   const uint16_t* sbase = PASS1 ? Ig : Qg;
-  const int64_t s_begin = PASS1 ? c0 : 0, s_end = PASS1 ? c1 : rows;
+  int64_t s_begin = PASS1 ? c0 : 0, s_end = PASS1 ? c1 : rows;
+  if (!SPAN) { h0 = 0; h1 = 0; n_split = 1; }
+  if (PASS1 && SPAN && n_split > 1) {
+    const int64_t span = ((c1 - c0 + n_split - 1) / n_split + kTile - 1) / kTile * kTile;
+    s_begin = c0 + span * blockIdx.y;
+    s_end = min(c1, s_begin + span);
+    if (s_begin >= s_end) {             // nothing left for this split: an empty partial
+      if (h == 0) {
+        const int64_t r0 = p0 + n, r1 = p0 + 32 + n;
+        if (r0 < rows_pad) part1[((size_t)lg * rows_pad + r0) * n_split + blockIdx.y] = make_float2(-INFINITY, 0.f);
+        if (r1 < rows_pad) part1[((size_t)lg * rows_pad + r1) * n_split + blockIdx.y] = make_float2(-INFINITY, 0.f);
+      }
+      return;
+    }
+  }
   const int nt = (int)((s_end - s_begin + kTile - 1) / kTile);
 
   Stage st;
@@ -251,12 +277,14 @@ __global__ __launch_bounds__(256, 2) void meank_pass(const uint16_t* __restrict_
   // pass 1: running reference and sum per persistent row; pass 2: column sums
   float m0, m1, s0 = 0.f, s1 = 0.f;
   if (PASS1) {
-    // the first tile may also be the partial last one: mask its padding columns
+    // the first tile may also be the partial last one, or meet the excluded span: mask those columns
     f32x16 x0 = cA0, x1 = cA1;
-    if (nt == 1) {
+    if (SPAN || nt == 1) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        if (s_begin + c_row(v, h) >= c1) { x0[v] = -INFINITY; x1[v] = -INFINITY; }
+      for (int v = 0; v < 16; ++v) {
+        const int64_t pos = s_begin + c_row(v, h);
+        if (pos >= s_end || (SPAN && pos >= h0 && pos < h1)) { x0[v] = -INFINITY; x1[v] = -INFINITY; }
+      }
     }
     m0 = fmaxf(tile_max(x0) * scale, -3.0e38f);
     m1 = fmaxf(tile_max(x1) * scale, -3.0e38f);
@@ -273,10 +301,14 @@ __global__ __launch_bounds__(256, 2) void meank_pass(const uint16_t* __restrict_
     float a0, a1;
     step_mma_epi<PASS1>(A, B0, B1, cn0, cn1, cc0, cc1, scale, lc, m0, m1, a0, a1);
     if (PASS1) {
-      // rebase only when some lane's tile sum could overflow (wave-uniform, rare)
-      if (__builtin_expect(__ballot(!(a0 <= kRebase) || !(a1 <= kRebase)) != 0, 0)) {
-        lse_fold<false>(cc0, scale, m0, s0, a0, 0, h, c1);
-        lse_fold<false>(cc1, scale, m1, s1, a1, 0, h, c1);
+      const int64_t tb = s_begin + (int64_t)t * kTile;
+      if (SPAN && tb < h1 && tb + kTile > h0) {    // tile meets the excluded span (wave-uniform)
+        lse_fold<true>(cc0, scale, m0, s0, a0, tb, h, s_end, h0, h1);
+        lse_fold<true>(cc1, scale, m1, s1, a1, tb, h, s_end, h0, h1);
+      } else if (__builtin_expect(__ballot(!(a0 <= kRebase) || !(a1 <= kRebase)) != 0, 0)) {
+        // rebase only when some lane's tile sum could overflow (wave-uniform, rare)
+        lse_fold<false>(cc0, scale, m0, s0, a0, 0, h, c1, h0, h1);
+        lse_fold<false>(cc1, scale, m1, s1, a1, 0, h, c1, h0, h1);
       } else {
         s0 += a0;
         s1 += a1;
@@ -306,8 +338,8 @@ __global__ __launch_bounds__(256, 2) void meank_pass(const uint16_t* __restrict_
   // last tile (the only one that can be partial)
   if (PASS1) {
     const int64_t b0 = s_begin + (int64_t)(nt - 1) * kTile;
-    lse_fold<true>(*last0, scale, m0, s0, 0.f, b0, h, c1);
-    lse_fold<true>(*last1, scale, m1, s1, 0.f, b0, h, c1);
+    lse_fold<true>(*last0, scale, m0, s0, 0.f, b0, h, s_end, h0, h1);
+    lse_fold<true>(*last1, scale, m1, s1, 0.f, b0, h, s_end, h0, h1);
   } else {
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
@@ -327,8 +359,13 @@ __global__ __launch_bounds__(256, 2) void meank_pass(const uint16_t* __restrict_
     lse_merge(m1, s1, mm, ss);
     if (h == 0) {
       const int64_t r0 = p0 + n, r1 = p0 + 32 + n;
-      if (r0 < rows_pad) lse2[(size_t)lg * rows_pad + r0] = (r0 < rows && s0 > 0.f) ? m0 + log2f(s0) : INFINITY;
-      if (r1 < rows_pad) lse2[(size_t)lg * rows_pad + r1] = (r1 < rows && s1 > 0.f) ? m1 + log2f(s1) : INFINITY;
+      if (SPAN && n_split > 1) {
+        if (r0 < rows_pad) part1[((size_t)lg * rows_pad + r0) * n_split + blockIdx.y] = make_float2(m0, s0);
+        if (r1 < rows_pad) part1[((size_t)lg * rows_pad + r1) * n_split + blockIdx.y] = make_float2(m1, s1);
+      } else {
+        if (r0 < rows_pad) lse2[(size_t)lg * rows_pad + r0] = (r0 < rows && s0 > 0.f) ? m0 + log2f(s0) : INFINITY;
+        if (r1 < rows_pad) lse2[(size_t)lg * rows_pad + r1] = (r1 < rows && s1 > 0.f) ? m1 + log2f(s1) : INFINITY;
+      }
     }
   } else {
     s0 += __shfl_xor(s0, 32, kWave);
@@ -341,15 +378,31 @@ __global__ __launch_bounds__(256, 2) void meank_pass(const uint16_t* __restrict_
   }
 }
 
-// R_b = sum over (l, g) of the partials, fixed order, / (L * H_q).  A workgroup
-// owns 64 blocks; wave w sums lg = w, w+4, ... and the 4 waves combine in order.
+// Row lse from the pass-1 split partials, merged in split order.
+__global__ __launch_bounds__(256) void meank_lse_merge(const float2* __restrict__ part1, int64_t n_rows,
+                                                       int64_t rows, int64_t rows_pad, int n_split,
+                                                       float* __restrict__ lse2) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_rows) return;
+  float m = -INFINITY, s = 0.f;
+  for (int c = 0; c < n_split; ++c) {
+    const float2 p = part1[(size_t)i * n_split + c];
+    lse_merge(m, s, p.x, p.y);
+  }
+  lse2[i] = (i % rows_pad < rows && s > 0.f) ? m + log2f(s) : INFINITY;
+}
+
+// R_b = sum over (l, g) of the partials, fixed order, / LH.  A workgroup
+// owns 64 columns; wave w sums lg = w, w+4, ... and the 4 waves combine in
+// order.  Columns outside [c0, c1) (or, with SPAN, inside [h0, h1)) get 0.
+template <bool SPAN>
 __global__ __launch_bounds__(256) void meank_reduce(const float* __restrict__ colpart, int LG,
-                                                    int64_t nB, int64_t c0, int64_t c1, float LH,
-                                                    float* __restrict__ R) {
+                                                    int64_t nB, int64_t c0, int64_t c1, int64_t h0,
+                                                    int64_t h1, float LH, float* __restrict__ R) {
   __shared__ float part[4][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t b = (int64_t)blockIdx.x * 64 + lane;
-  const bool cand = b >= c0 && b < c1;
+  const bool cand = b >= c0 && b < c1 && !(SPAN && b >= h0 && b < h1);
   float s = 0.f;
   if (cand) {
 #pragma unroll 8
@@ -387,19 +440,103 @@ hipError_t kvs_launch_meank_score(const void* Q, const void* index, int L, int H
   const uint16_t* Ib = static_cast<const uint16_t*>(index);
   if (c1 > c0 && rows > 0) {
     const int T1 = (int)ceil_div(rows_pad, kPerWG);
-    hipLaunchKernelGGL((meank_pass<true>), dim3((unsigned)T1 * LG), dim3(256), 0, st, Qb, Ib, LG, rows,
-                       rows_pad, nB, c0, c1, T1, scale, lse2, colpart);
+    hipLaunchKernelGGL((meank_pass<true, false>), dim3((unsigned)T1 * LG), dim3(256), 0, st, Qb, Ib, LG, rows,
+                       rows_pad, nB, c0, c1, (int64_t)0, (int64_t)0, T1, scale, 1, lse2, nullptr, colpart);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int T2 = (int)ceil_div(c1 - c0, kPerWG);
-    hipLaunchKernelGGL((meank_pass<false>), dim3((unsigned)T2 * LG), dim3(256), 0, st, Qb, Ib, LG, rows,
-                       rows_pad, nB, c0, c1, T2, scale, lse2, colpart);
+    hipLaunchKernelGGL((meank_pass<false, false>), dim3((unsigned)T2 * LG), dim3(256), 0, st, Qb, Ib, LG, rows,
+                       rows_pad, nB, c0, c1, (int64_t)0, (int64_t)0, T2, scale, 1, lse2, nullptr, colpart);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   } else {
     c1 = c0;   // no candidates (or no queries): every R_b is 0
   }
-  hipLaunchKernelGGL(meank_reduce, dim3(ceil_div(nB, 64)), dim3(256), 0, st, colpart, LG, nB, c0, c1,
-                     (float)(L * H_q), R);
+  hipLaunchKernelGGL(meank_reduce<false>, dim3(ceil_div(nB, 64)), dim3(256), 0, st, colpart, LG, nB, c0, c1,
+                     (int64_t)0, (int64_t)0, (float)(L * H_q), R);
+  return hipGetLastError();
+}
+
+// Window score (the SnapKV query window that IntentKV's Eq. 3 replaces by one
+// memory vector): the same two-pass engine with the window's G*W query rows
+// of each KV group in place of the Mean-K queries and the cache's keys in
+// place of the block index.  Candidates are [pi, N) minus [q_s, q_e); pass 1
+// is split along N so that a short window still fills the device.
+namespace {
+
+struct WindowPlan {
+  int64_t rows, rows_pad, c0, c1, h0, h1;
+  int T1, T2, n_split;
+};
+
+WindowPlan window_plan(int L, int H_q, int H_kv, int64_t W, int64_t N, int64_t pi, int64_t q_s, int64_t q_e) {
+  WindowPlan p;
+  const int LG = L * H_kv;
+  p.rows = (int64_t)(H_q / H_kv) * W;
+  p.rows_pad = pad32(p.rows);
+  p.c0 = pi < N ? pi : N;
+  p.c1 = N;
+  p.h0 = q_s > p.c0 ? q_s : p.c0;
+  p.h1 = q_e < N ? q_e : N;
+  if (p.h1 < p.h0) p.h1 = p.h0;
+  p.T1 = (int)ceil_div(p.rows_pad, kPerWG);
+  p.T2 = (int)ceil_div(p.c1 - p.c0 > 0 ? p.c1 - p.c0 : 1, kPerWG);
+  // at least ~2048 workgroups in pass 1, and at least 8 tiles per split
+  const int64_t want = ceil_div(2048, (int64_t)p.T1 * LG);
+  const int64_t most = ceil_div(p.c1 - p.c0 > 0 ? p.c1 - p.c0 : 1, 8 * kTile);
+  p.n_split = (int)(want < most ? want : most);
+  if (p.n_split < 1) p.n_split = 1;
+  if (p.n_split > 65535) p.n_split = 65535;
+  return p;
+}
+
+}  // namespace
+
+size_t kvs_window_ws_bytes(int L, int H_q, int H_kv, int64_t W, int64_t N) {
+  const WindowPlan p = window_plan(L, H_q, H_kv, W, N, 0, 0, 0);
+  const size_t LG = (size_t)L * H_kv;
+  return align256(LG * (size_t)p.rows_pad * 4) + align256(LG * (size_t)p.rows_pad * p.n_split * 8) +
+         align256(LG * (size_t)N * 4);
+}
+
+hipError_t kvs_launch_window(const void* K, const void* Qw, int L, int H_q, int H_kv, int64_t W, int64_t N,
+                             int64_t pi, int64_t q_s, int64_t q_e, float* score, void* ws, hipStream_t st) {
+  const int LG = L * H_kv;
+  WindowPlan p = window_plan(L, H_q, H_kv, W, N, pi, q_s, q_e);
+  // the split count (and so the workspace) does not depend on pi or the span
+  p.n_split = window_plan(L, H_q, H_kv, W, N, 0, 0, 0).n_split;
+  char* w = static_cast<char*>(ws);
+  float* lse2 = reinterpret_cast<float*>(w);
+  w += align256((size_t)LG * p.rows_pad * 4);
+  float2* part1 = reinterpret_cast<float2*>(w);
+  w += align256((size_t)LG * p.rows_pad * p.n_split * 8);
+  float* colpart = reinterpret_cast<float*>(w);
+  const float scale = (float)(1.4426950408889634 / __builtin_sqrt((double)D));
+  const uint16_t* Qb = static_cast<const uint16_t*>(Qw);
+  const uint16_t* Kb = static_cast<const uint16_t*>(K);
+  int64_t c0 = p.c0, c1 = p.c1;
+  const bool any = c1 > c0 && !(p.h0 <= c0 && p.h1 >= c1) && p.rows > 0;
+  if (any) {
+    hipLaunchKernelGGL((meank_pass<true, true>), dim3((unsigned)p.T1 * LG, (unsigned)p.n_split), dim3(256), 0, st, Qb,
+                       Kb, LG, p.rows, p.rows_pad, N, c0, c1, p.h0, p.h1, p.T1, scale, p.n_split, lse2, part1,
+                       colpart);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (p.n_split > 1) {
+      const int64_t n_rows = (int64_t)LG * p.rows_pad;
+      hipLaunchKernelGGL(meank_lse_merge, dim3(ceil_div(n_rows, 256)), dim3(256), 0, st, part1, n_rows, p.rows,
+                         p.rows_pad, p.n_split, lse2);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((meank_pass<false, true>), dim3((unsigned)p.T2 * LG), dim3(256), 0, st, Qb, Kb, LG, p.rows,
+                       p.rows_pad, N, c0, c1, p.h0, p.h1, p.T2, scale, 1, lse2, part1, colpart);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else {
+    c1 = c0;   // no candidates (or an empty window): every score is 0
+  }
+  hipLaunchKernelGGL(meank_reduce<true>, dim3(ceil_div(N, 64)), dim3(256), 0, st, colpart, LG, N, c0, c1, p.h0,
+                     p.h1, 1.0f, score);
   return hipGetLastError();
 }

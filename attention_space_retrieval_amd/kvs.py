@@ -30,6 +30,8 @@ _SIGNATURES = [
     ("kvs_rule_score", _I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _I64, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     ("kvs_rule_score_paged", _I32, [_P, _I32, _P, _I64, _P, _I32, _I32, _I32, _I32, _I64, _I64, _I64,
                                     _I64, _P, _P, _SZ, _P]),
+    ("kvs_window_score_workspace", _SZ, [_I32, _I32, _I32, _I64, _I64]),
+    ("kvs_window_score", _I32, [_P, _P, _I32, _I32, _I32, _I32, _I64, _I64, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     ("kvs_topk_workspace", _SZ, [_I64]),
     ("kvs_topk_select", _I32, [_P, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
     ("kvs_slotmap_redirect", _I32, [_P, _P, _I64, _I64, _P, _P]),
@@ -167,6 +169,30 @@ def kvs_rule_score_paged(K_pool, slots, M, pi, q_s, q_e, rule=None, ws=None):
         _ptr(K_pool), _dtype_code(K_pool), _ptr(slots), pool_size, _ptr(M), L, H_q, H_kv, D, N, int(pi),
         int(q_s), int(q_e), _ptr(rule), _ptr(ws), ws.numel(), _stream(K_pool)))
     return rule
+
+
+def kvs_window_score_workspace(L, H_q, H_kv, W, N):
+    return load().kvs_window_score_workspace(L, H_q, H_kv, W, N)
+
+
+def kvs_window_score(K, Qw, pi, q_s, q_e, score=None, ws=None):
+    """score [N] float32 from bf16 K [L, H_kv, N, D] and bf16 window rows Qw [L, H_q, W, D]."""
+    _dev(K, Qw, score, ws)
+    if K.dtype != torch.bfloat16 or Qw.dtype != torch.bfloat16:
+        raise TypeError("K and Qw must be bfloat16")
+    L, H_kv, N, D = K.shape
+    H_q, W = Qw.shape[1], Qw.shape[2]
+    _need(Qw.shape[0] == L and Qw.shape[3] == D, "Qw must be [L, H_q, W, D] like K")
+    if score is None:
+        score = torch.empty(N, dtype=torch.float32, device=K.device)
+    _need(score.dtype == torch.float32 and score.numel() == N, "score must be float32 [N]")
+    if ws is None:
+        ws = torch.empty(max(1, kvs_window_score_workspace(L, H_q, H_kv, W, N)), dtype=torch.uint8,
+                         device=K.device)
+    _check("kvs_window_score", load().kvs_window_score(
+        _ptr(K), _ptr(Qw), L, H_q, H_kv, D, N, W, int(pi), int(q_s), int(q_e), _ptr(score), _ptr(ws),
+        ws.numel(), _stream(K)))
+    return score
 
 
 def kvs_topk_workspace(n):

@@ -11,7 +11,9 @@ Prints one JSON line.  `value` counts K-cache tokens scored per second over the
 whole step (the rule cache's N plus the Mean-K workspace's N).  Per-call times
 come from HIP events on the stream the library launches on; `roofline` is the
 call with the largest share of the step, priced against MI355X's published
-peaks; its `traffic` (and each call's) is the HBM bytes per launch that
+peaks; `next_rows` times the calls beyond the step (paged rule score, window
+score, Mean-K append, working-set update) on the same workload's shapes after
+the timed steps, outside `value`.  `traffic` (per call) is the HBM bytes per launch that
 rocprofv3's FETCH_SIZE/WRITE_SIZE counters measured, read from the committed
 summary under profiles/ and scaled by the counters' reading of a device copy of
 known size, or null when the kernel source has changed since.  `cpu_baseline`
@@ -41,11 +43,18 @@ WORKLOADS = {"rule-8b+meank-256k": ("rule-8b", "meank-256k"),
 # kernels each call launches (rocprofv3 short names); the two top-k calls share one kernel
 CALL_KERNELS = {
     "kvs_qmem_update": ["qmem_kernel<128, true>"],
-    "kvs_rule_score": ["rule_logits_mfma<128, 1>", "rule_lse_merge", "rule_colsum"],
+    "kvs_rule_score": ["rule_logits_mfma<128, 1, false>", "rule_lse_merge", "rule_colsum"],
     "kvs_slotmap_redirect": ["slotmap_kernel"],
     "kvs_meank_build": ["meank_build_raw<128>"],
-    "kvs_meank_score": ["meank_pass<true>", "meank_pass<false>", "meank_reduce"],
+    "kvs_meank_score": ["meank_pass<true, false>", "meank_pass<false, false>", "meank_reduce<false>"],
     "kvs_rerope_scatter": ["rerope_scatter_kernel<128>"],
+    # rows beyond the step (timed after it): the paged rule score's merge and column sum are the
+    # dense call's kernels on the same sizes
+    "kvs_rule_score_paged": ["rule_logits_mfma<128, 1, true>", "rule_lse_merge", "rule_colsum"],
+    "kvs_window_score": ["meank_pass<true, true>", "meank_lse_merge", "meank_pass<false, true>",
+                         "meank_reduce<true>"],
+    "kvs_meank_append": ["meank_append_kernel<128>"],
+    "kvs_working_set_update": ["workset_diff", "workset_apply<128>"],
 }
 
 
@@ -146,6 +155,85 @@ class Setup:
         }
 
 
+class NextRows:
+    """Inputs for the rows beyond the step, at the same workload's shapes.
+
+    * kvs_rule_score_paged: the rule cache read through a permuted slot map from a
+      token-major pool with 4096 spare slots.
+    * kvs_window_score: the rule cache with a 32-row window of query rows per head.
+    * kvs_meank_append: an 8192-token chunk of the Mean-K workspace appended after
+      an 8192-token prefix (stage-out and index of the touched blocks).
+    * kvs_working_set_update: the step's selection against a previous one that
+      shares half of its blocks, on the step's page pool.
+    """
+
+    def __init__(self, s, dev):
+        c, m = s.rc, s.mc
+        self.s = s
+        L, H_q, H_kv, D, N = c["L"], c["H_q"], c["H_kv"], c["D"], c["N"]
+        r = np.random.default_rng([c["seed"], 99])
+        perm = torch.from_numpy(r.permutation(N + 4096)[:N].copy()).to(dev)
+        self.pool = torch.empty((L, N + 4096, H_kv, D), dtype=torch.bfloat16, device=dev)
+        self.pool[:, perm] = s.K.permute(0, 2, 1, 3)
+        self.slots = perm
+        self.rule_p = torch.empty_like(s.rule)
+        self.W = 32
+        self.Qw = W.normal((L, H_q, self.W, D), c["seed"], W.T_Q + 40, "bf16", dev)
+        self.win = torch.empty_like(s.rule)
+        self.ws_win = torch.empty(kvs.kvs_window_score_workspace(L, H_q, H_kv, self.W, N), dtype=torch.uint8,
+                                  device=dev)
+        Lm, Hm, Dm = m["L"], m["H_kv"], m["D"]
+        self.n_app, self.t0 = 8192, 8192
+        cap = self.t0 + self.n_app
+        self.chunk = s.Kraw[:, :, self.t0:cap].contiguous()
+        self.stage = torch.zeros((Lm, Hm, cap, Dm), dtype=torch.bfloat16, device=dev)
+        self.app_index = torch.zeros((Lm, Hm, cap // 32, Dm), dtype=torch.bfloat16, device=dev)
+        kvs.kvs_meank_append(s.Kraw[:, :, :self.t0].contiguous(), 0, self.stage, self.app_index)
+        nB, budget = s.nB, s.n_sel
+        new = np.sort(r.choice(nB, budget, replace=False))
+        keep = new[np.sort(r.choice(budget, budget // 2, replace=False))]
+        others = np.setdiff1d(np.arange(nB), new)
+        prev = np.sort(np.concatenate([keep, r.choice(others, budget - len(keep), replace=False)]))
+        prev_pages = r.permutation(budget)
+        rank = {int(b): i for i, b in enumerate(prev)}
+        self.n_moved = sum(1 for i, b in enumerate(new) if int(b) in rank and rank[int(b)] != i)
+        self.n_incoming = sum(1 for b in new if int(b) not in rank)
+        i32 = lambda a: torch.tensor(np.asarray(a), dtype=torch.int32, device=dev)
+        self.prev, self.prev_pages, self.new = i32(prev), i32(prev_pages), i32(new)
+        self.ws_ws = torch.empty(kvs.kvs_working_set_workspace(budget), dtype=torch.uint8, device=dev)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+
+    def calls(self):
+        s, c, m = self.s, self.s.rc, self.s.mc
+        return [
+            ("kvs_rule_score_paged", lambda: kvs.kvs_rule_score_paged(
+                self.pool, self.slots, s.M, c["pi"], c["q_s"], c["q_e"], rule=self.rule_p, ws=s.ws_rule)),
+            ("kvs_window_score", lambda: kvs.kvs_window_score(
+                s.K, self.Qw, c["pi"], c["q_s"], c["q_e"], score=self.win, ws=self.ws_win)),
+            ("kvs_meank_append", lambda: kvs.kvs_meank_append(self.chunk, self.t0, self.stage, self.app_index)),
+            ("kvs_working_set_update", lambda: kvs.kvs_working_set_update(
+                s.Kraw, s.v_src if s.src_block is None else None, self.prev, self.prev_pages, self.new,
+                m["pos_base"], m["theta"], s.k_pool, s.v_pool if s.src_block is None else None,
+                err_flag=self.err, ws=self.ws_ws)),
+        ]
+
+    def work(self):
+        s, c, m = self.s, self.s.rc, self.s.mc
+        N, LG_r = c["N"], c["L"] * c["H_kv"]
+        kbytes = LG_r * N * c["D"] * 2
+        blk = m["L"] * m["H_kv"] * 32 * m["D"] * 2
+        n_blk = -(-(self.t0 + self.n_app) // 32) - self.t0 // 32
+        v_too = 2 if s.src_block is None else 1
+        return {
+            "kvs_rule_score_paged": ("hbm", kbytes + 8 * N + c["L"] * c["H_q"] * c["D"] * 4 + 4 * N),
+            "kvs_window_score": ("hbm", kbytes + c["L"] * c["H_q"] * self.W * c["D"] * 2 + 4 * N),
+            "kvs_meank_append": ("hbm", 2 * m["L"] * m["H_kv"] * self.n_app * m["D"] * 2
+                                 + m["L"] * m["H_kv"] * n_blk * m["D"] * 2),
+            "kvs_working_set_update": ("hbm", 2 * self.n_moved * blk + 2 * v_too * self.n_incoming * blk),
+        }
+
+
 def measured_traffic(workload):
     """HBM bytes per call from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary.
 
@@ -170,10 +258,8 @@ def measured_traffic(workload):
     return out
 
 
-def run_gpu(s, steps, warmup, only=None):
-    calls = s.calls()
-    if only:
-        calls = [c for c in calls if c[0] in only]
+def run_calls(calls, steps, warmup):
+    """Warm up, then time `steps` passes over `calls` with HIP events between the calls."""
     for _ in range(warmup):
         for _, f in calls:
             f()
@@ -193,6 +279,14 @@ def run_gpu(s, steps, warmup, only=None):
              for i, (name, _) in enumerate(calls)}
     per_call = {name: float(np.mean(v)) for name, v in times.items()}
     spread = {name: (float(np.min(v)), float(np.max(v))) for name, v in times.items()}
+    return wall, per_call, spread
+
+
+def run_gpu(s, steps, warmup, only=None):
+    calls = s.calls()
+    if only:
+        calls = [c for c in calls if c[0] in only]
+    wall, per_call, spread = run_calls(calls, steps, warmup)
     assert int(s.err.item()) == 0, "scatter reported an out-of-range block"
     return wall, per_call, spread
 
@@ -277,6 +371,9 @@ def main():
                     help="comma-separated call names to time alone (profiling; not a headline figure). "
                          "Calls left out are not run, so a call that consumes another's output "
                          "(e.g. the scatter reading the Mean-K selection) sees whatever that buffer holds.")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip timing the calls beyond the step (paged rule score, window score, "
+                         "Mean-K append, working-set update)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run one 4 GiB device copy (for HBM counter scaling)")
     a = ap.parse_args()
@@ -296,6 +393,24 @@ def main():
                           "calls_ms_min_max": spread}))
         return
     ms_per_step = 1000.0 * wall / a.steps
+    next_rows = None
+    if not a.no_next_rows:
+        log("[bench] timing the rows beyond the step")
+        nr = NextRows(s, dev)
+        _, nr_ms, nr_spread = run_calls(nr.calls(), a.steps, a.warmup)
+        assert int(nr.err.item()) == 0, "working-set update rejected its input"
+        next_rows = {}
+        for name, ms in nr_ms.items():
+            bound, amount = nr.work()[name]
+            ach = amount / (ms * 1e-3) / 1e9
+            next_rows[name] = {"ms": round(ms, 4), "ms_min": round(nr_spread[name][0], 4),
+                               "ms_max": round(nr_spread[name][1], 4), "bound": bound, "achieved": round(ach, 2),
+                               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                               "per_launch": amount}
+        next_rows["kvs_working_set_update"]["classes"] = {"moved": nr.n_moved, "incoming": nr.n_incoming,
+                                                          "selected": int(nr.new.numel())}
+        next_rows["kvs_window_score"]["window_rows"] = nr.W
+        del nr
     if a.copy_calibration:
         x = torch.empty(1 << 31, dtype=torch.int16, device=dev)
         y = torch.empty_like(x)
@@ -317,7 +432,7 @@ def main():
                       "unit": unit, "frac": round(ach / peak, 4),
                       "per_launch": amount}
     traffic = measured_traffic(a.workload)
-    for name, r in rows.items():
+    for name, r in list(rows.items()) + list((next_rows or {}).items()):
         t = traffic.get(name)
         r["traffic"] = None if t is None else round(t)
     dom = max(rows, key=lambda k: rows[k]["ms"])
@@ -345,6 +460,7 @@ def main():
                       "frac_hbm_peak": rule_bytes / (rule_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "meank_score_tflops": rows["kvs_meank_score"]["achieved"],
         "calls": rows,
+        "next_rows": next_rows,
     }
     if not a.no_cpu_baseline:
         log("[bench] timing the oracle on a bounded CPU sample")

@@ -117,6 +117,28 @@ kvs_status kvs_rule_score_paged(const void* K_pool, int32_t k_dtype, const int64
                                 int64_t q_e, float* rule, void* ws, size_t ws_bytes,
                                 void* stream);
 
+/* Workspace bytes kvs_window_score needs for these sizes. */
+size_t kvs_window_score_workspace(int32_t L, int32_t H_q, int32_t H_kv, int64_t W, int64_t N);
+
+/*
+ * Window score -- the SnapKV-style window of W tail query rows that IntentKV
+ * Sec. 3.2 says Eq. (3) replaces with one accumulated query state: for every
+ * layer l, query head h and window row w a softmax over the candidate
+ * positions H = [0,N) minus F (Sec. 3.1) of Qw[l,h,w] . K[l,h/G,j] / sqrt(D),
+ * summed over (l, h, w):  score_j = sum_{l,h,w} a_{l,h,w,j}.  With W = 1 and
+ * Qw = M this is kvs_rule_score.  SnapKV's pooling and per-head selection are
+ * not part of it.
+ *   K        [L, H_kv, N, D] bf16 post-RoPE keys.
+ *   Qw       [L, H_q, W, D] bf16 post-RoPE window query rows.
+ *   score    [N] float32 output; 0 on F; sum over H = L*H_q*W.
+ *   ws       device workspace of >= kvs_window_score_workspace() bytes.
+ * Errors: KVS_ERR_ARG (null, W < 1, bad range), KVS_ERR_SHAPE,
+ * KVS_ERR_UNSUPPORTED (D != 128), KVS_ERR_WORKSPACE.
+ */
+kvs_status kvs_window_score(const void* K, const void* Qw, int32_t L, int32_t H_q, int32_t H_kv,
+                            int32_t D, int64_t N, int64_t W, int64_t pi, int64_t q_s, int64_t q_e,
+                            float* score, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes kvs_topk_select needs for n scores. */
 size_t kvs_topk_workspace(int64_t n);
 

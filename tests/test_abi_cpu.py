@@ -27,7 +27,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = header_functions()
-    assert len(names) == 16
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(kvs.ENTRY_POINTS) == names
@@ -125,6 +125,17 @@ def test_rule_paged_rejections(lib):
     assert call(a7=3) == 2               # H_q % H_kv
     assert call(a8=96) == 4
     assert call(a15=ws - 1) == 5
+
+
+def test_window_rejections(lib):
+    f = lib.kvs_window_score
+    ws = lib.kvs_window_score_workspace(2, 8, 2, 16, 1000)
+    assert ws > 0
+    assert f(FAKE, FAKE, 2, 8, 2, 128, 1000, 0, 4, 990, 1000, FAKE, FAKE, ws, None) == 1      # W = 0
+    assert f(FAKE, FAKE, 2, 8, 3, 128, 1000, 16, 4, 990, 1000, FAKE, FAKE, ws, None) == 2
+    assert f(FAKE, FAKE, 2, 8, 2, 64, 1000, 16, 4, 990, 1000, FAKE, FAKE, ws, None) == 4
+    assert f(FAKE, FAKE, 2, 8, 2, 128, 1000, 16, 4, 990, 1000, FAKE, FAKE, ws - 1, None) == 5
+    assert f(None, FAKE, 2, 8, 2, 128, 1000, 16, 4, 990, 1000, FAKE, FAKE, ws, None) == 1
 
 
 def test_working_set_rejections(lib):

@@ -16,6 +16,7 @@ import torch
 
 import oracle
 from attention_space_retrieval_amd import kvs, workloads as W
+from attention_space_retrieval_amd import workloads as W_
 from tests.helpers import assert_rel, assert_valid_selection, host
 
 pytestmark = pytest.mark.gpu
@@ -198,6 +199,59 @@ def test_rule_paged_full_size_equals_dense(name):
     torch.cuda.synchronize()
     assert torch.equal(dense, paged)
     del K, pool
+
+
+# ---------------------------------------------------------------- window score
+
+@pytest.mark.parametrize("L,H_q,H_kv,N,W,pi,q_s,q_e", [
+    (2, 32, 8, 5000, 32, 64, 4936, 5000),      # span at the end: candidates [pi, q_s)
+    (2, 8, 2, 3000, 16, 10, 1000, 1100),       # span in the middle: a hole in the candidates
+    (1, 40, 8, 777, 7, 0, 0, 0),               # G = 5, odd W, no forced positions, ragged N
+    (1, 4, 4, 300, 1, 299, 0, 0),              # one candidate
+])
+def test_window_score_against_oracle(L, H_q, H_kv, N, W, pi, q_s, q_e):
+    K = W_.normal((L, H_kv, N, 128), 17, W_.T_K, "bf16", DEV)
+    Qw = W_.normal((L, H_q, W, 128), 17, W_.T_Q, "bf16", DEV)
+    got = kvs.kvs_window_score(K, Qw, pi, q_s, q_e)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    want = oracle.window_score(host(K), host(Qw), pi, q_s, q_e)
+    F = oracle.forced_mask(N, pi, q_s, q_e)
+    assert np.all(got[F] == 0.0)
+    assert_rel(got[~F], want[~F], RULE_RTOL, f"window score W{W} N{N}")
+    assert abs(got.sum(dtype=np.float64) - L * H_q * W) <= 1e-4 * L * H_q * W
+
+
+def test_window_one_row_matches_rule_score():
+    """W = 1 with the QueryMemory as the window row gives the rule score (to float32 rounding)."""
+    L, H_q, H_kv, N, D = 2, 16, 4, 4000, 128
+    K = W_.normal((L, H_kv, N, D), 18, W_.T_K, "bf16", DEV)
+    M = W_.memory_vectors(L, H_q, D, 18, DEV)
+    Mb = M.to(torch.bfloat16)
+    rule = kvs.kvs_rule_score(K, Mb.float(), 5, 3990, 4000)
+    win = kvs.kvs_window_score(K, Mb[:, :, None, :].contiguous(), 5, 3990, 4000)
+    torch.cuda.synchronize()
+    F = oracle.forced_mask(N, 5, 3990, 4000)
+    assert_rel(win.cpu().numpy()[~F], rule.cpu().numpy()[~F], RULE_RTOL, "window(W=1) vs rule")
+
+
+def test_window_score_full_size_sampled():
+    """rule-8b's cache with a 32-row window: sampled layers' contribution checked against the oracle."""
+    c = W_.config("rule-8b")
+    L, H_q, H_kv, D, N = c["L"], c["H_q"], c["H_kv"], c["D"], c["N"]
+    K = W_.normal((L, H_kv, N, D), c["seed"], W_.T_K, "bf16", DEV)
+    Qw = W_.normal((L, H_q, 32, D), c["seed"], W_.T_Q, "bf16", DEV)
+    got = kvs.kvs_window_score(K, Qw, c["pi"], c["q_s"], c["q_e"])
+    # two layers alone, through the same library call, against the oracle
+    two = kvs.kvs_window_score(K[:2].contiguous(), Qw[:2].contiguous(), c["pi"], c["q_s"], c["q_e"])
+    torch.cuda.synchronize()
+    F = oracle.forced_mask(N, c["pi"], c["q_s"], c["q_e"])
+    want = oracle.window_score(host(K[:2]), host(Qw[:2]), c["pi"], c["q_s"], c["q_e"])
+    assert_rel(two.cpu().numpy()[~F], want[~F], RULE_RTOL, "window score, 2 layers of rule-8b")
+    g = got.cpu().numpy()
+    assert np.all(g[F] == 0.0) and np.all(g[~F] > 0.0)
+    assert abs(g.sum(dtype=np.float64) - L * H_q * 32) <= 1e-4 * L * H_q * 32
+    del K, Qw
 
 
 # ---------------------------------------------------------------- top-k
