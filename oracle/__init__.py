@@ -27,7 +27,9 @@ Parity status: every function here is pinned by the CPU tests against closed
 forms, invariants, library special cases and brute force, except for the
 conventions no page value can confirm (listed as "parity unpinned" in the
 function docstrings): the decay value lambda the IntentKV paper used, the RoPE
-pairing of the pages' models, and which layer-heads KVMEM lets vote.
+pairing of the pages' models, which layer-heads KVMEM lets vote, how positions
+on the dead slot enter later rule scoring, and the window score beyond its
+plainest reading (sum of per-row softmaxes, no pooling).
 """
 
 from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits, as_f64

@@ -68,7 +68,8 @@ def rule_score_paged(K_pool, slots, M, pi, q_s, q_e):
     sends dropped positions to a dead slot.  Reading: key row j of KV head g
     in layer l is K_pool[l, S_r[j], g, :] (token-major pool, as SGLang and vLLM
     store it); a position whose slot lies outside the pool has no key, so it
-    is not a candidate and scores 0.
+    is not a candidate and scores 0.  Parity unpinned: the pages do not say
+    how dead positions enter later scoring.
 
     K_pool: [L, pool_size, H_kv, D]; slots: [N] integers.
     """
@@ -89,7 +90,8 @@ def window_score(K, Qw, pi, q_s, q_e):
     Reading: for every layer l, query head h and window row w, a softmax over
     the candidate positions H (Sec. 3.1) of Qw[l,h,w] . K[l,g(h),j] / sqrt(D);
     score_j sums them over (l, h, w).  SnapKV's pooling and per-head selection
-    are not described by the pages and are left out.
+    are not described by the pages and are left out.  Parity unpinned beyond
+    this reading (W = 1 with Qw = M is pinned to the rule score).
 
     K: [L, H_kv, N, D]; Qw: [L, H_q, W, D] post-RoPE window query rows.
     """
