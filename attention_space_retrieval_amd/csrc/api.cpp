@@ -23,6 +23,10 @@ int64_t numel4(int64_t a, int64_t b, int64_t c, int64_t d) {
 
 bool head_dim_ok(int32_t D) { return D == 64 || D == 128; }
 
+// A 1-D launch of 256-thread workgroups covers at most 2^32 - 1 work-items.
+bool grid_ok(int64_t workgroups) { return workgroups >= 0 && workgroups < ((int64_t)1 << 24); }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
 // The kernels move 16-byte vectors: tensor bases (and workspaces) must be 16-byte aligned.
 bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -153,7 +157,7 @@ kvs_status kvs_meank_build(const void* K, int32_t L, int32_t H_kv, int32_t D, in
   if (L < 1 || H_kv < 1 || N < 0 || pos0 < 0) return KVS_ERR_ARG;
   if (k_is_rope && !(std::isfinite(theta) && theta > 0.0)) return KVS_ERR_ARG;
   if (block != 32 || !head_dim_ok(D)) return KVS_ERR_UNSUPPORTED;
-  if (numel4(L, H_kv, N, D) < 0 || (N + 31) / 32 > kMaxIndex) return KVS_ERR_SHAPE;
+  if (numel4(L, H_kv, N, D) < 0 || (N + 31) / 32 > kMaxIndex || !grid_ok(cdiv(N, 32))) return KVS_ERR_SHAPE;
   return hip_status(kvs_launch_meank_build(K, L, H_kv, D, N, k_is_rope ? 1 : 0, pos0, theta,
                                            k_is_rope ? raw_k_out : nullptr, index,
                                            as_stream(stream)));
@@ -166,7 +170,7 @@ kvs_status kvs_meank_append(const void* k_chunk, int32_t L, int32_t H_kv, int32_
   if (!(std::isfinite(theta) && theta > 0.0)) return KVS_ERR_ARG;
   if (!head_dim_ok(D)) return KVS_ERR_UNSUPPORTED;
   if (t0 > cap || n_new > cap - t0 || numel4(L, H_kv, cap, D) < 0 || (cap + 31) / 32 > kMaxIndex ||
-      (int64_t)L * H_kv > 65535 * 32)
+      (int64_t)L * H_kv > 65535 * 32 || !grid_ok(cdiv(cap, 32)))
     return KVS_ERR_SHAPE;
   if (n_new == 0) return KVS_OK;
   if (!k_chunk || !raw_stage || !index || !a16(k_chunk) || !a16(raw_stage) || !a16(index))
@@ -190,6 +194,8 @@ kvs_status kvs_meank_score(const void* Q, const void* index, int32_t L, int32_t 
       (int64_t)L * H_kv > 65535 || nB > kMaxIndex)
     return KVS_ERR_SHAPE;
   if (D != 128) return KVS_ERR_UNSUPPORTED;
+  if (!grid_ok(cdiv((int64_t)(H_q / H_kv) * Mq, 256) * L * H_kv) || !grid_ok(cdiv(nB, 256) * L * H_kv))
+    return KVS_ERR_SHAPE;
   if (nB == 0) return KVS_OK;
   const size_t need = kvs_meank_ws_bytes(L, H_q, H_kv, Mq, nB);
   if (!ws || ws_bytes < need || !a16(ws)) return KVS_ERR_WORKSPACE;
@@ -213,7 +219,7 @@ kvs_status kvs_rerope_scatter(const void* k_src, const void* v_src, int64_t src_
   if (!(std::isfinite(theta) && theta > 0.0)) return KVS_ERR_ARG;
   if (block != 32 || !head_dim_ok(D)) return KVS_ERR_UNSUPPORTED;
   if (src_tokens % block != 0 || numel4(L, H_kv, src_tokens, D) < 0 ||
-      numel4(L, H_kv, pool_pages, (int64_t)block * D) < 0 || n_sel > kMaxIndex)
+      numel4(L, H_kv, pool_pages, (int64_t)block * D) < 0 || !grid_ok(n_sel))
     return KVS_ERR_SHAPE;
   return hip_status(kvs_launch_rerope(k_src, v_src, src_tokens, src_block, page_table, n_sel, L,
                                       H_kv, D, pos_base, theta, k_pool, v_pool, pool_pages,
@@ -231,7 +237,8 @@ kvs_status kvs_window_score(const void* K, const void* Qw, int32_t L, int32_t H_
   if (!K || !Qw || !score || !a16(K) || !a16(Qw)) return KVS_ERR_ARG;
   if (L < 1 || H_q < 1 || H_kv < 1 || N < 0 || W < 1 || pi < 0 || q_s < 0 || q_e < q_s) return KVS_ERR_ARG;
   if (H_q % H_kv != 0 || N > kMaxIndex || numel4(L, H_kv, N, D) < 0 || numel4(L, H_q, W, D) < 0 ||
-      (int64_t)L * H_kv > 65535 || (int64_t)(H_q / H_kv) * W > (int64_t)1 << 24)
+      (int64_t)L * H_kv > 65535 || (int64_t)(H_q / H_kv) * W > (int64_t)1 << 24 ||
+      !grid_ok(cdiv((int64_t)(H_q / H_kv) * W, 256) * L * H_kv) || !grid_ok(cdiv(N, 256) * L * H_kv))
     return KVS_ERR_SHAPE;
   if (D != 128) return KVS_ERR_UNSUPPORTED;
   if (N == 0) return KVS_OK;
@@ -264,7 +271,7 @@ kvs_status kvs_working_set_update(const void* k_src, const void* v_src, int64_t 
   if (block != 32 || !head_dim_ok(D)) return KVS_ERR_UNSUPPORTED;
   if (src_tokens % block != 0 || numel4(L, H_kv, src_tokens, D) < 0 ||
       numel4(L, H_kv, pool_pages, (int64_t)block * D) < 0 || pool_pages > kMaxIndex ||
-      n_new > pool_pages || n_prev > pool_pages)
+      n_new > pool_pages || n_prev > pool_pages || !grid_ok(n_new))
     return KVS_ERR_SHAPE;
   const size_t need = kvs_workset_ws_bytes(pool_pages);
   if (need > 0 && (!ws || ws_bytes < need || !a16(ws))) return KVS_ERR_WORKSPACE;

@@ -31,6 +31,8 @@
  *     dimension, N tokens.
  *   - bf16 means IEEE binary32 with the low 16 bits dropped (uint16 storage).
  *   - A data pointer may be NULL only where its tensor holds no elements.
+ *   - Sizes that would need a launch of 2^24 or more 256-thread workgroups
+ *     (far beyond any single-GPU cache) return KVS_ERR_SHAPE.
  */
 #ifndef KVS_H_
 #define KVS_H_

@@ -162,6 +162,13 @@ def test_working_set_rejections(lib):
     assert call(a6=None) == 1              # new blocks missing while n_new > 0
 
 
+def test_oversized_launches_are_rejected(lib):
+    r = lib.kvs_rerope_scatter
+    assert r(FAKE, None, 640, FAKE, None, 1 << 24, 2, 2, 128, 32, 0, 1e6, FAKE, None, 8, None, None) == 2
+    ws = 1 << 30
+    assert lib.kvs_meank_score(FAKE, FAKE, 4, 8, 2, 128, 50, (1 << 31) - 1, 4, 7, FAKE, FAKE, ws, None) == 2
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(ValueError, match="GPU"):
