@@ -204,6 +204,78 @@ def test_meank_score_full_size_properties():
     assert abs(r.sum() - c["Mq"]) <= 1e-4 * c["Mq"]
 
 
+def test_meank_1m_step_full_size():
+    """meank-1m end to end in the benchmark's launch shapes: build from 128 GiB of raw K (sampled blocks
+    against the oracle), R_b over 32768 blocks (one (layer, KV head) against the oracle at full
+    extent, the rest by mass and sign), the sink/recent + budget selection (a valid top-C* of the
+    scores it was given), and the re-RoPE scatter of 4096 blocks from the packed staging buffers
+    through a page table (sampled pages against the oracle)."""
+    c = W.config("meank-1m")
+    L, H_q, H_kv, D, N, Mq = c["L"], c["H_q"], c["H_kv"], c["D"], c["N"], c["Mq"]
+    nB, G, budget = N // 32, c["H_q"] // c["H_kv"], c["budget"]
+    r = np.random.default_rng(8)
+    print("[meank-1m] build", flush=True)
+    K = W.normal((L, H_kv, N, D), c["seed"], W.T_K, "bf16", DEV)
+    index = kvs.kvs_meank_build(K)
+    torch.cuda.synchronize()
+    for _ in range(24):
+        l, g, b = int(r.integers(L)), int(r.integers(H_kv)), int(r.integers(nB))
+        want, _ = oracle.meank_build(host(K[l, g, 32 * b:32 * b + 32])[None, None])
+        assert_within_ulp(bits(index[l, g, b])[None, None, None], want, f"index block {(l, g, b)}", atol=1e-5)
+    del K
+    torch.cuda.empty_cache()
+    print("[meank-1m] score", flush=True)
+    Q = W.normal((L, H_q, Mq, D), c["seed"], W.T_Q, "bf16", DEV)
+    R = kvs.kvs_meank_score(Q, index, c["n_sink"], c["n_recent"])
+    # one (layer, KV head) alone through the same library call, at its full extent, against the oracle
+    l, g = 17, 5
+    Q1 = Q[l:l + 1, g * G:(g + 1) * G].contiguous()
+    I1 = index[l:l + 1, g:g + 1].contiguous()
+    R1 = kvs.kvs_meank_score(Q1, I1, c["n_sink"], c["n_recent"])
+    torch.cuda.synchronize()
+    cand = oracle.candidate_blocks(nB, c["n_sink"], c["n_recent"])
+    want1 = oracle.meank_score(host(Q1), host(I1), c["n_sink"], c["n_recent"])
+    assert_rel(R1.cpu().numpy()[cand], want1[cand], R_RTOL, "R_b of one (layer, KV head) at meank-1m")
+    Rn = R.cpu().numpy().astype(np.float64)
+    assert np.all(Rn[~cand] == 0) and np.all(Rn[cand] > 0)
+    assert abs(Rn.sum() - Mq) <= 1e-4 * Mq
+    del Q, Q1, I1, index
+    print("[meank-1m] select", flush=True)
+    keep, idx, nk = kvs.kvs_topk_select(R, (0, c["n_sink"]), (nB - c["n_recent"], nB), budget)
+    torch.cuda.synchronize()
+    nk = int(nk.item())
+    sel = idx[:nk].cpu().numpy()
+    assert nk == budget and np.all(np.diff(sel) > 0)
+    forced = ~cand
+    kept = np.zeros(nB, dtype=bool)
+    kept[sel] = True
+    assert kept[forced].all()
+    Rf = R.cpu().numpy()
+    assert Rf[kept & cand].min() >= Rf[~kept & cand].max()          # a top-C* of the scores it ranked
+    print("[meank-1m] scatter", flush=True)
+    shp = (L, H_kv, 32 * budget, D)
+    k_src = W.normal(shp, c["seed"], W.T_K + 10, "bf16", DEV)
+    v_src = W.normal(shp, c["seed"], W.T_V + 10, "bf16", DEV)
+    src_block = torch.arange(budget, dtype=torch.int32, device=DEV)
+    pt = W.page_permutation(budget, budget, c["seed"]).to(DEV)
+    k_pool = torch.empty(shp, dtype=torch.bfloat16, device=DEV)
+    v_pool = torch.empty(shp, dtype=torch.bfloat16, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kvs.kvs_rerope_scatter(k_src, v_src, src_block, pt, budget, c["pos_base"], c["theta"], k_pool, v_pool, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    ptn = pt.cpu().numpy()
+    for _ in range(16):
+        rr, l, g = int(r.integers(budget)), int(r.integers(L)), int(r.integers(H_kv))
+        rows = slice(32 * int(ptn[rr]), 32 * int(ptn[rr]) + 32)
+        want = oracle.rope_rotate(oracle.bf16_bits_to_f64(host(k_src[l, g, 32 * rr:32 * rr + 32])),
+                                  c["pos_base"] + 32 * rr + np.arange(32), c["theta"])
+        assert_within_ulp(bits(k_pool[l, g, rows]), want, f"page of block {rr}", atol=1e-6)
+        assert np.array_equal(bits(v_pool[l, g, rows]), host(v_src[l, g, 32 * rr:32 * rr + 32]))
+    del k_src, v_src, k_pool, v_pool, R
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------- re-RoPE scatter
 
 @pytest.mark.parametrize("D,pos_base,with_v,identity", [(128, 0, True, False), (128, 1000000, True, True),
