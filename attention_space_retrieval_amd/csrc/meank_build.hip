@@ -17,6 +17,17 @@ namespace {
 
 constexpr int kBlk = 32;
 
+// The index rows are a thin write stream inside a saturated read stream.
+// Stored as device-scope relaxed atomics they go through to memory at once
+// (the sc1 policy) instead of sitting dirty in L2 until the read stream evicts
+// them; on this part that takes ~0.5 ms off a 34 GB build.  Relaxed atomics
+// add no ordering or fences.
+__device__ __forceinline__ void store_through(uint16_t* p, u32x4 v) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(p);
+  __hip_atomic_store(q, (uint64_t)v.x | ((uint64_t)v.y << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, (uint64_t)v.z | ((uint64_t)v.w << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Raw mode.  One wavefront per block: each load instruction moves 64*8/D
 // whole contiguous rows (16-byte non-temporal loads, since K is read once), a
 // lane adds the rows it loaded for its 16-byte column chunk, and the row groups
@@ -56,7 +67,7 @@ __global__ __launch_bounds__(256) void meank_build_raw(const uint16_t* __restric
     if (rr == 0) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] = nb == kBlk ? acc[e] * (1.f / kBlk) : acc[e] / (float)nb;
-      *reinterpret_cast<u32x4*>(index + (size_t)gb * D + cl * 8) = pack8(acc);
+      store_through(index + (size_t)gb * D + cl * 8, pack8(acc));
     }
   }
 }
