@@ -1,24 +1,32 @@
-// Rotation table for one 32-token block, shared by the de-RoPE index build and
-// the re-RoPE scatter.  Rotate-half pairing (i, i + D/2), omega_i =
-// theta^(-2i/D); the angle p * omega_i is formed and reduced in float64 (at
-// p ~ 1e6 a float32 angle would be off by up to ~0.06 rad) and only the final
-// cos/sin are rounded to float32.
+// Rotation table for one 32-token block, shared by the de-RoPE index build,
+// the Mean-K append, the re-RoPE scatter and the working-set update.
+// Rotate-half pairing (i, i + D/2), omega_i = theta^(-2i/D).  The angle
+// p * omega_i is formed in float64 and reduced modulo 2 pi there (at p ~ 1e6 a
+// float32 angle would be off by up to ~0.06 rad); the reduced angle, in
+// [-pi, pi], goes through float32 sincos, whose few-ulp error is far below the
+// bf16 resolution of the rotated keys.
 #pragma once
 
 #include "kvs_internal.h"
 
 namespace kvs {
 
-// tab[t][i] = (cos, sin) of (p0 + t) * omega_i for t < 32, i < D/2.
+// tab[t][i] = (cos, sin) of (p0 + t) * omega_i for t < 32, i < D/2.  Called by
+// all threads of a workgroup whose size is a multiple of D/2, so each thread
+// keeps one frequency i.
 template <int D>
 __device__ __forceinline__ void build_rope_table(float2 (*tab)[D / 2], int64_t p0, double log2_theta) {
+  constexpr double kTwoPi = 6.283185307179586476925286766559;
+  constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
+  const int i = threadIdx.x % (D / 2);
+  const double omega = exp2(-(2.0 * i / D) * log2_theta);
   for (int x = threadIdx.x; x < 32 * (D / 2); x += blockDim.x) {
-    const int t = x / (D / 2), i = x - t * (D / 2);
-    const double omega = exp2(-(2.0 * i / D) * log2_theta);
+    const int t = x / (D / 2);
     const double a = (double)(p0 + t) * omega;
-    double s, c;
-    sincos(a, &s, &c);
-    tab[t][i] = make_float2((float)c, (float)s);
+    const double r = fma(-rint(a * kInvTwoPi), kTwoPi, a);
+    float s, c;
+    sincosf((float)r, &s, &c);
+    tab[t][i] = make_float2(c, s);
   }
 }
 
