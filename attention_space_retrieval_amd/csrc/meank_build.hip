@@ -24,13 +24,9 @@ constexpr int kBlk = 32;
 // store over the row's 256 bytes (the resource also bounds it in hardware);
 // two 8-byte write-through stores were ~0.3 ms slower.  `row` must be
 // wave-uniform: it becomes the scalar buffer resource.
-constexpr int kSc1 = 16;                      // cache-policy operand of the buffer intrinsics: sc1
-constexpr int kBufWord3 = 0x00020000;         // buffer resource word 3 for raw (untyped) access on gfx9
-
 template <int D>
 __device__ __forceinline__ void store_row_through(uint16_t* row, int cl, u32x4 v) {
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(row, 0, D * 2, kBufWord3);
-  __builtin_amdgcn_raw_buffer_store_b128(v, rs, cl * 16, 0, kSc1);
+  buf_store16<kBufSc1>(v, buf_rsrc(row, D * 2), cl * 16);
 }
 
 // Raw mode.  One wavefront per block: each load instruction moves 64*8/D

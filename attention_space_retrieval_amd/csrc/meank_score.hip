@@ -20,9 +20,11 @@
 //   reduce:          R_b = sum of the (l,g) partials in fixed order / (L*H_q).
 // Both passes share one engine: a 256-thread workgroup keeps 256 persistent
 // rows in registers, streams 8 KB tiles global -> LDS (double buffered, rows
-// XOR-swizzled in 16-byte chunks so the MFMA operand reads are bank-conflict
-// free) and software-pipelines each wave: the MFMAs of tile t+1 are issued
-// before the exp2 epilogue of tile t, so matrix and vector units overlap.
+// padded to 272 bytes so the 16-byte MFMA operand reads are bank-conflict free
+// and use immediate offsets) and software-pipelines each wave: each MFMA of
+// tile t+1 is followed by a slice of tile t's exp2 epilogue, so the matrix and
+// vector units overlap.  The same engine serves the window score (the SnapKV
+// window of query rows over the cache's keys; see the end of this file).
 // Workgroups are mapped XCD-aware: the tiles of one (l, g) land on the same
 // XCD and share its L2 copy of the streamed operand.
 // Operand k-slots: lane half h = lane/32 carries k-slots 8h..8h+7 of every
