@@ -48,9 +48,9 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
 
 inline unsigned ceil_div(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
 
-// 16-byte stores through a buffer resource over [base, base + bytes): a scalar
-// base and a 32-bit per-lane offset, bounds-checked by the hardware (writes
-// past `bytes` are dropped).  `base` must be wave-uniform.  aux is the cache
+// Buffer accesses through a resource over [base, base + bytes): a scalar base
+// and a 32-bit per-lane offset, bounds-checked by the hardware (writes past
+// `bytes` are dropped).  `base` must be wave-uniform.  aux is the cache
 // policy operand: 0 = default, kBufSc1 = write through to memory.
 constexpr int kBufWord3 = 0x00020000;   // resource word 3 for raw (untyped) access on gfx9
 constexpr int kBufSc1 = 16;
@@ -61,6 +61,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int
 template <int AUX = 0>
 __device__ __forceinline__ void buf_store16(u32x4 v, __amdgpu_buffer_rsrc_t r, int byte_off) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, AUX);
+}
+// 4- and 1-byte forms; a load past `bytes` returns 0.
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0);
+}
+__device__ __forceinline__ void buf_store4(uint32_t v, __amdgpu_buffer_rsrc_t r, int byte_off) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, byte_off, 0, 0);
+}
+__device__ __forceinline__ void buf_store1(uint8_t v, __amdgpu_buffer_rsrc_t r, int byte_off) {
+  __builtin_amdgcn_raw_buffer_store_b8(v, r, byte_off, 0, 0);
 }
 
 }  // namespace kvs

@@ -25,10 +25,6 @@ namespace {
 constexpr int kChunk = 2048;   // positions per workgroup in the logit pass
 constexpr int kColTile = 64;   // positions per workgroup in the column sum
 
-__device__ __forceinline__ __bf16 bf16_from_bits(uint32_t b) {
-  return __builtin_bit_cast(__bf16, (uint16_t)b);
-}
-
 __device__ __forceinline__ bool is_forced(int64_t j, int64_t pi, int64_t q_s, int64_t q_e) {
   return j < pi || (j >= q_s && j < q_e);
 }
@@ -37,6 +33,28 @@ __device__ __forceinline__ void online_add(float& m, float& s, float x) {
   const float mn = fmaxf(m, x);
   s = s * __builtin_amdgcn_exp2f(m - mn) + __builtin_amdgcn_exp2f(x - mn);
   m = mn;
+}
+
+// One lane's 8 A-operand values for k-step s: M[head] * log2(e)/sqrt(D) at
+// dims d0..d0+7, high bf16 part (hi) or the bf16 rounding of the remainder,
+// packed two per register so the operand stays in 4 registers.
+__device__ __forceinline__ bf16x8 m_operand(const float* __restrict__ mrow, bool valid, bool hi, int d0,
+                                            float scale_log2) {
+  u32x4 w = {0u, 0u, 0u, 0u};
+  if (valid) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      uint32_t b[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const float x = mrow[d0 + e + k] * scale_log2;
+        const uint32_t hb = f32_to_bf16_bits(x);
+        b[k] = hi ? hb : f32_to_bf16_bits(x - __uint_as_float(hb << 16));
+      }
+      w[e / 2] = b[0] | (b[1] << 16);
+    }
+  }
+  return __builtin_bit_cast(bf16x8, w);
 }
 
 // Paged keys: a token-major pool K_pool[l, slot, g, :] read in place through
@@ -77,18 +95,7 @@ __global__ __launch_bounds__(256) void rule_logits_mfma(
     const int hl = hg * 8 + (r & 7);
     const float* mrow = M + ((size_t)l * H_q + (size_t)g * G + hl) * D;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t bits = 0;
-        if (hl < G) {
-          const float x = mrow[q * QW + 8 * s + e] * scale_log2;
-          const uint32_t hb = f32_to_bf16_bits(x);
-          bits = r < 8 ? hb : f32_to_bf16_bits(x - __uint_as_float(hb << 16));
-        }
-        A[hg][s][e] = bf16_from_bits(bits);
-      }
-    }
+    for (int s = 0; s < KS; ++s) A[hg][s] = m_operand(mrow, hl < G, r < 8, q * QW + 8 * s, scale_log2);
   }
 
   float mx[NHG][4], sm[NHG][4];

@@ -1,15 +1,15 @@
 // Budgeted top-k with a forced set (IntentKV, Sec. 3.1, Eq. 1) and the
 // slot-map redirect of the IntentKV layout layer.
 //
-// Scores map to order-preserving uint32 keys (sign-flip trick; NaN -> 0, the
-// lowest key; -0 -> +0), so the selection is integer-only and exact.  One
-// 1024-thread workgroup (keys staged in LDS when they fit) runs a radix select
-// over the key range
-// [kmin, kmax] of the candidates, 8 bits per pass with one LDS histogram per
-// wave (no cross-wave atomic contention on hot bins), to find the threshold
-// key T and the number of threshold ties k to keep.  The emit pass gives each
-// wave a contiguous segment of positions; ballot/popcount ranks make the
-// output ascending and hand the k ties to the lowest indices.
+// Scores map to order-preserving uint32 keys (sign-flip trick; NaN below every
+// number; -0 -> +0), so the selection is integer-only and exact.  One
+// 1024-thread workgroup runs a radix select over the key range [kmin, kmax] of
+// the candidates, 8 bits per pass from the top of that range down, with one
+// LDS histogram per wave (no cross-wave atomic contention on hot bins), to
+// find the threshold key T and
+// the number of threshold ties k to keep; ballot/popcount ranks make the
+// output ascending and hand the k ties to the lowest indices.  Up to 32768
+// scores the keys stay in registers for the whole selection.
 #include "kvs_internal.h"
 
 using namespace kvs;
@@ -35,17 +35,13 @@ struct Forced {
   __device__ bool operator()(int j) const { return (j >= f0b && j < f0e) || (j >= f1b && j < f1e); }
 };
 
-// Keys for n <= kCacheKeys are staged once in LDS (gfx950 gives a workgroup up
-// to 160 KB) so every pass after the first reads LDS; larger inputs re-read the
-// scores from global memory (L2-resident) with 4 loads in flight per thread.
-constexpr int kCacheKeys = 32768;
+// Inputs too large for the register-resident kernel below: every pass re-reads
+// the scores from global memory (L2-resident) with 4 loads in flight per thread.
 constexpr int kUnroll = 4;
 
-template <bool CACHED>
 __global__ __launch_bounds__(kThreads) void topk_select_kernel(
     const float* __restrict__ score, int n, Forced forced, int c_star, int n_forced,
     uint8_t* __restrict__ keep_mask, int32_t* __restrict__ keep_idx, int64_t* __restrict__ n_kept) {
-  __shared__ uint32_t keys[CACHED ? kCacheKeys : 1];
   __shared__ uint32_t hist[kWaves][256];
   __shared__ uint32_t wmin[kWaves], wmax[kWaves];
   __shared__ uint32_t wcnt[kWaves][2];
@@ -53,24 +49,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const bool none = c_star == 0;   // C <= |F|: keep the forced set only
 
-  auto key_at = [&](int j) -> uint32_t { return CACHED ? keys[j] : score_key(score[j]); };
-
-  if (CACHED) {
-    for (int j0 = tid; j0 < n; j0 += kThreads * kUnroll) {
-      float v[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int j = j0 + u * kThreads;
-        v[u] = j < n ? score[j] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int j = j0 + u * kThreads;
-        if (j < n) keys[j] = score_key(v[u]);
-      }
-    }
-    __syncthreads();
-  }
+  auto key_at = [&](int j) -> uint32_t { return score_key(score[j]); };
 
   uint32_t kT = 0xffffffffu, k_tie = 0;
   if (!none) {
@@ -101,10 +80,10 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
     const int bits = range ? 32 - __clz(range) : 0;
     const int ndig = (bits + 7) / 8;
     uint32_t prefix = 0, k = (uint32_t)c_star;
-    for (int p = ndig - 1; p >= 0; --p) {
+    for (int p = 0; p < ndig; ++p) {
       for (int i = tid; i < kWaves * 256; i += kThreads) (&hist[0][0])[i] = 0u;
       __syncthreads();
-      const int sh = 8 * p;
+      const int sh = max(bits - 8 * (p + 1), 0), wd = bits - 8 * p - sh;   // top-aligned digits
       for (int j0 = tid; j0 < n; j0 += kThreads * kUnroll) {
         uint32_t kk[kUnroll];
 #pragma unroll
@@ -117,8 +96,8 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
           const int j = j0 + u * kThreads;
           if (j >= n || forced(j)) continue;
           const uint32_t rel = kk[u] - mn;
-          const uint32_t hi = sh + 8 >= 32 ? 0u : rel >> (sh + 8);
-          if (hi == prefix) atomicAdd(&hist[wave][(rel >> sh) & 255u], 1u);
+          const uint32_t hi = (uint32_t)((uint64_t)rel >> (sh + wd));
+          if (hi == prefix) atomicAdd(&hist[wave][(rel >> sh) & ((1u << wd) - 1u)], 1u);
         }
       }
       __syncthreads();
@@ -143,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
           uint32_t a = above;
           for (int i = 3; i >= 0; --i) {
             if (a + c[i] >= k) {
-              state[0] = (prefix << 8) | (uint32_t)(4 * lane + i);
+              state[0] = (prefix << wd) | (uint32_t)(4 * lane + i);
               state[1] = k - a;
               break;
             }
@@ -197,6 +176,203 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
   if (tid == 0) *n_kept = (int64_t)n_forced + c_star;
 }
 
+// Keys held in registers, for n <= 1024 * KPT: thread t owns positions
+// j = 1024u + t (u < KPT), so the scores are read once, with every load of a
+// thread in flight together, and no pass after that touches memory.  The key
+// itself carries a position's class, so no per-position flags are kept:
+// candidates take the order-preserving key with NaN -> 1 (below -inf, which
+// maps to 0x007fffff), a forced position takes 0xffffffff (above +inf, 0xff800000)
+// and a position past n takes 0.  "Kept by value" is then just key > T.
+// Loads and stores go through bounds-checked buffer resources: loads past n
+// return 0, and stores past n (and the keep_idx store of a position that is
+// not kept, sent out of range) are dropped, so no position needs a branch.
+// The radix passes use double-buffered per-wave LDS histograms (a pass zeroes
+// the next pass's buffer), two barriers per pass.  The emit pass counts kept
+// and tie positions per (u, wave) with ballots, scans those counts in position
+// order, and writes every kept index at its final rank directly.
+constexpr uint32_t kKeyOut = 0u, kKeyForced = 0xffffffffu;
+
+__device__ __forceinline__ uint32_t cand_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 1u;
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int KPT>
+__global__ __launch_bounds__(kThreads) void topk_reg_kernel(
+    const float* __restrict__ score, int n, Forced forced, int c_star, int n_forced,
+    uint8_t* __restrict__ keep_mask, int32_t* __restrict__ keep_idx, int64_t* __restrict__ n_kept) {
+  constexpr int NCV = (KPT + 63) / 64;
+  __shared__ uint32_t hist[2][kWaves][256];
+  __shared__ uint32_t wred[kWaves][2];
+  __shared__ uint32_t state[2];
+  __shared__ uint32_t cnt[2][KPT][kWaves];   // [kept-by-value | ties][u][wave]
+  __shared__ uint32_t ubase[2][KPT];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const __amdgpu_buffer_rsrc_t rs = buf_rsrc(score, n * 4);
+  const __amdgpu_buffer_rsrc_t rm = buf_rsrc(keep_mask, n);
+  const __amdgpu_buffer_rsrc_t ri = buf_rsrc(keep_idx, n * 4);
+
+  uint32_t key[KPT];
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) key[u] = buf_load4(rs, 4 * (u * kThreads + tid));
+  uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    // position 1024u + tid against scalar bounds shifted by 1024u
+    const int o = u * kThreads;
+    const bool in = tid < n - o;
+    const bool f = ((uint32_t)(tid - (forced.f0b - o)) < (uint32_t)(forced.f0e - forced.f0b)) |
+                   ((uint32_t)(tid - (forced.f1b - o)) < (uint32_t)(forced.f1e - forced.f1b));
+    const uint32_t kc = cand_key(__uint_as_float(key[u]));
+    key[u] = !in ? kKeyOut : (f ? kKeyForced : kc);
+    const bool c = in & !f;
+    mn = min(mn, c ? kc : 0xffffffffu);
+    mx = max(mx, c ? kc : 0u);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  auto is_cand = [&](uint32_t k) -> bool { return (k != kKeyOut) & (k != kKeyForced); };
+
+  // C <= |F| (c_star == 0) keeps the forced set only: T = 0xfffffffe.
+  uint32_t kT = 0xfffffffeu, k_tie = 0;
+  if (c_star > 0) {
+    for (int i = tid; i < kWaves * 256; i += kThreads) (&hist[0][0][0])[i] = 0u;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
+      mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
+    }
+    if (lane == 0) { wred[wave][0] = mn; wred[wave][1] = mx; }
+    __syncthreads();
+    mn = wred[0][0]; mx = wred[0][1];
+    for (int w = 1; w < kWaves; ++w) { mn = min(mn, wred[w][0]); mx = max(mx, wred[w][1]); }
+    const uint32_t range = mx - mn;
+    const int bits = range ? 32 - __clz(range) : 0;
+    const int ndig = (bits + 7) / 8;
+    uint32_t prefix = 0, k = (uint32_t)c_star;
+    int buf = 0;
+    for (int p = 0; p < ndig; ++p) {
+      // digits are cut from the top of the range, so the first pass spreads
+      // the candidates over up to 256 bins however narrow their key range is
+      const int sh = max(bits - 8 * (p + 1), 0), wd = bits - 8 * p - sh;
+      uint32_t* h = &hist[buf][wave][0];
+      // keep key - mn from being hoisted out of the pass loop (a second KPT-register array)
+      uint32_t mnp = mn;
+      asm volatile("" : "+v"(mnp));
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) {
+        const uint32_t rel = key[u] - mnp;
+        const uint32_t hi = (uint32_t)((uint64_t)rel >> (sh + wd));
+        if (is_cand(key[u]) & (hi == prefix)) atomicAdd(h + ((rel >> sh) & ((1u << wd) - 1u)), 1u);
+      }
+      for (int i = tid; i < kWaves * 256; i += kThreads) (&hist[buf ^ 1][0][0])[i] = 0u;
+      __syncthreads();
+      if (wave == 0) {
+        uint32_t c[4] = {0u, 0u, 0u, 0u};
+        for (int w = 0; w < kWaves; ++w) {
+          const u32x4 hv = *reinterpret_cast<const u32x4*>(&hist[buf][w][4 * lane]);
+          c[0] += hv[0]; c[1] += hv[1]; c[2] += hv[2]; c[3] += hv[3];
+        }
+        const uint32_t lsum = c[0] + c[1] + c[2] + c[3];
+        // inclusive suffix sum over lanes: candidates in bins >= 4*lane
+        uint32_t incl = lsum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t t = (uint32_t)__shfl_down((int)incl, o, kWave);
+          if (lane + o < 64) incl += t;
+        }
+        const uint32_t above = incl - lsum;
+        if (above < k && k <= incl) {
+          uint32_t a = above;
+          for (int i = 3; i >= 0; --i) {
+            if (a + c[i] >= k) {
+              state[0] = (prefix << wd) | (uint32_t)(4 * lane + i);
+              state[1] = k - a;
+              break;
+            }
+            a += c[i];
+          }
+        }
+      }
+      __syncthreads();
+      prefix = state[0];
+      k = state[1];
+      buf ^= 1;
+    }
+    kT = mn + prefix;
+    k_tie = k;
+  }
+
+  // Emit.  Per (u, wave) counts of positions kept by value (forced, or key
+  // above T) and of threshold ties; lane u of cv[] collects u's.
+  uint32_t cv[2][NCV];
+#pragma unroll
+  for (int i = 0; i < NCV; ++i) { cv[0][i] = 0u; cv[1][i] = 0u; }
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const uint32_t nd = (uint32_t)__popcll(__ballot(key[u] > kT));
+    const uint32_t nt = (uint32_t)__popcll(__ballot(key[u] == kT));
+    if (lane == (u & 63)) { cv[0][u >> 6] = nd; cv[1][u >> 6] = nt; }
+  }
+#pragma unroll
+  for (int i = 0; i < NCV; ++i) {
+    const int u = 64 * i + lane;
+    if (u < KPT) { cnt[0][u][wave] = cv[0][i]; cnt[1][u][wave] = cv[1][i]; }
+  }
+  __syncthreads();
+  if (tid < 2 * KPT) {
+    const int which = tid / KPT, u = tid - which * KPT;
+    uint32_t run = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      const uint32_t c = cnt[which][u][w];
+      cnt[which][u][w] = run;
+      run += c;
+    }
+    ubase[which][u] = run;
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      const uint32_t a = 2 * lane < KPT ? ubase[which][2 * lane] : 0u;
+      const uint32_t b = 2 * lane + 1 < KPT ? ubase[which][2 * lane + 1] : 0u;
+      uint32_t incl = a + b;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = (uint32_t)__shfl_up((int)incl, o, kWave);
+        if (lane >= o) incl += t;
+      }
+      const uint32_t excl = incl - (a + b);
+      if (2 * lane < KPT) ubase[which][2 * lane] = excl;
+      if (2 * lane + 1 < KPT) ubase[which][2 * lane + 1] = excl + a;
+    }
+  }
+  __syncthreads();
+  // lane u of cv[] holds this wave's bases for u, read back as scalars
+#pragma unroll
+  for (int i = 0; i < NCV; ++i) {
+    const int u = min(64 * i + lane, KPT - 1);
+    cv[0][i] = ubase[0][u] + cnt[0][u][wave];
+    cv[1][i] = ubase[1][u] + cnt[1][u][wave];
+  }
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const int j = u * kThreads + tid;
+    const bool tie = key[u] == kT;
+    const uint64_t bt = __ballot(tie);
+    const uint32_t def_before = (uint32_t)__builtin_amdgcn_readlane((int)cv[0][u >> 6], u & 63);
+    const uint32_t tie_before = (uint32_t)__builtin_amdgcn_readlane((int)cv[1][u >> 6], u & 63);
+    const bool keep = (key[u] > kT) | (tie & (tie_before + rank_below(bt, lane) < k_tie));
+    const uint64_t bk = __ballot(keep);
+    buf_store1(keep ? 1 : 0, rm, j);
+    const uint32_t r = def_before + min(tie_before, k_tie) + rank_below(bk, lane);
+    buf_store4((uint32_t)j, ri, keep ? (int)(4 * r) : 0x7fffffff);
+    __builtin_amdgcn_sched_barrier(0);   // one position at a time: bounded register use
+  }
+  if (tid == 0) *n_kept = (int64_t)n_forced + c_star;
+}
+
 // C* >= |H|: everything is kept.
 __global__ __launch_bounds__(256) void keep_all_kernel(int n, uint8_t* __restrict__ keep_mask,
                                                        int32_t* __restrict__ keep_idx,
@@ -228,11 +404,14 @@ hipError_t kvs_launch_topk(const float* score, int64_t n, int64_t f0b, int64_t f
     return hipGetLastError();
   }
   Forced f{(int)f0b, (int)f0e, (int)f1b, (int)f1e};
-  if (n <= kCacheKeys)
-    hipLaunchKernelGGL(topk_select_kernel<true>, dim3(1), dim3(kThreads), 0, st, score, (int)n, f,
-                       (int)c_star, (int)n_forced, keep_mask, keep_idx, n_kept);
+#define TOPK_REG(KPT)                                                                               \
+  hipLaunchKernelGGL(topk_reg_kernel<KPT>, dim3(1), dim3(kThreads), 0, st, score, (int)n, f, (int)c_star, \
+                     (int)n_forced, keep_mask, keep_idx, n_kept)
+  if (n <= 8 * kThreads) TOPK_REG(8);
+  else if (n <= 32 * kThreads) TOPK_REG(32);
+#undef TOPK_REG
   else
-    hipLaunchKernelGGL(topk_select_kernel<false>, dim3(1), dim3(kThreads), 0, st, score, (int)n, f,
+    hipLaunchKernelGGL(topk_select_kernel, dim3(1), dim3(kThreads), 0, st, score, (int)n, f,
                        (int)c_star, (int)n_forced, keep_mask, keep_idx, n_kept);
   return hipGetLastError();
 }

@@ -279,10 +279,24 @@ def check_topk(score, f0, f1, C):
     (500, None, (0, 10), (490, 500), 5),           # C < |F|
     (500, None, (0, 10), (490, 500), 10000),       # C >= n
     (0, None, (0, 0), (0, 0), 5),                  # empty input
+    (8192, None, (0, 0), (0, 0), 1),               # register kernel size limits and one past them
+    (8193, 4, (0, 1), (8192, 8193), 4000),
+    (32768, None, (0, 64), (32704, 32768), 8192),
+    (32769, None, (0, 64), (32705, 32769), 8192),
+    (1025, None, (1000, 1025), (0, 0), 1),
 ])
 def test_topk_bit_exact(n, levels, f0, f1, C):
     score = W.scores_with_ties(n, n + 1, levels).to(DEV)
     check_topk(score, f0, f1, C)
+
+
+@pytest.mark.parametrize("n,C", [(32768, 8192), (92160, 8192), (8192, 2048)])
+def test_topk_concentrated_scores(n, C):
+    """Rule-score-like keys: every value within a few 1e-3 of the mean, so the
+    candidates share their high key bits and the radix passes run on the low ones."""
+    x = W.scores_with_ties(n, 4242)
+    score = (0.0353 * (1.0 + 0.0026 * x)).float().to(DEV)
+    check_topk(score, (0, 64), (n - 64, n), C)
 
 
 def test_topk_special_values():
