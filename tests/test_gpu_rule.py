@@ -121,6 +121,17 @@ def test_rule_large_logits_keep_precision():
     check_rule(K, M, 0, 0, 0, "large logits")
 
 
+@pytest.mark.parametrize("scale,G", [(60.0, 4), (100.0, 4), (100.0, 5)])
+def test_rule_wide_logit_range_escapes(scale, G):
+    # Logits spread over hundreds of log2 units: many keys fall more than 32
+    # below their 16-position tile maximum, so the 16-bit spill escapes them to
+    # float32; every candidate must still meet the tolerance.
+    L, H_kv, D, N = 2, 2, 128, 2500
+    K = W.normal((L, H_kv, N, D), 15, W.T_K, "bf16", DEV, scale=scale)
+    M = W.memory_vectors(L, H_kv * G, D, 15, DEV)
+    check_rule(K, M, 3, 2400, 2450, f"wide logits scale {scale} G {G}")
+
+
 def test_rule_all_forced_and_determinism():
     L, H_q, H_kv, D, N = 2, 8, 2, 128, 700
     K = W.normal((L, H_kv, N, D), 13, W.T_K, "bf16", DEV)
