@@ -40,10 +40,12 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 WORKLOADS = {"rule-8b+meank-256k": ("rule-8b", "meank-256k"),
              "rule-14b+meank-1m": ("rule-14b", "meank-1m")}
-# kernels each call launches (rocprofv3 short names); the two top-k calls share one kernel
+# kernels each call launches (rocprofv3 short names)
 CALL_KERNELS = {
     "kvs_qmem_update": ["qmem_kernel<128, true>"],
     "kvs_rule_score": ["rule_logits_mfma<128, 1, false>", "rule_lse_merge", "rule_colsum"],
+    "kvs_topk_select[rule]": ["topk_reg_kernel<32>"],
+    "kvs_topk_select[meank]": ["topk_reg_kernel<8>"],
     "kvs_slotmap_redirect": ["slotmap_kernel"],
     "kvs_meank_build": ["meank_build_raw<128>"],
     "kvs_meank_score": ["meank_pass<true, false>", "meank_pass<false, false>", "meank_reduce<false>"],
