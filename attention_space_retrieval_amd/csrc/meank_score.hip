@@ -268,12 +268,16 @@ __global__ __launch_bounds__(256, 2) void meank_pass(const uint16_t* __restrict_
   }
   __syncthreads();
 
+  // A wave whose persistent rows all lie past the end (the window score's
+  // G*W query rows fill half a workgroup) skips the tiles' MFMAs and
+  // epilogue; it still stages tiles and meets every barrier, and writes nothing.
+  const bool live = p0 < (PASS1 ? rows : c1 - c0);   // wave-uniform
   bf16x8 A[KS];
-  f32x16 cA0, cA1, cB0, cB1;          // ping-pong accumulators (tile t and t+1)
+  f32x16 cA0 = {}, cA1 = {}, cB0 = {}, cB1 = {};     // ping-pong accumulators (tile t and t+1)
   float lA[16], lB[16];               // pass 2: lse2 of the rows of tile t and t+1
   read_streamed(tiles[0], lane, A);
   if (!PASS1) read_lse16(lses[0], h, lA);
-  mma2(A, B0, B1, cA0, cA1);
+  if (live) mma2(A, B0, B1, cA0, cA1);
   __syncthreads();
 
   // pass 1: running reference and sum per persistent row; pass 2: column sums
@@ -300,8 +304,8 @@ __global__ __launch_bounds__(256, 2) void meank_pass(const uint16_t* __restrict_
     if (pre) stage_load<!PASS1>(st, sbase, s_begin + (int64_t)(t + 2) * kTile, s_end, Lg);
     read_streamed(tiles[(t + 1) & 1], lane, A);
     if (!PASS1) read_lse16(lses[(t + 1) & 1], h, ln);
-    float a0, a1;
-    step_mma_epi<PASS1>(A, B0, B1, cn0, cn1, cc0, cc1, scale, lc, m0, m1, a0, a1);
+    float a0 = 0.f, a1 = 0.f;
+    if (live) step_mma_epi<PASS1>(A, B0, B1, cn0, cn1, cc0, cc1, scale, lc, m0, m1, a0, a1);
     if (PASS1) {
       const int64_t tb = s_begin + (int64_t)t * kTile;
       if (SPAN && tb < h1 && tb + kTile > h0) {    // tile meets the excluded span (wave-uniform)
