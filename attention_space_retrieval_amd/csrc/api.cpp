@@ -25,6 +25,10 @@ bool head_dim_ok(int32_t D) { return D == 64 || D == 128; }
 
 // A 1-D launch of 256-thread workgroups covers at most 2^32 - 1 work-items.
 bool grid_ok(int64_t workgroups) { return workgroups >= 0 && workgroups < ((int64_t)1 << 24); }
+// The Mean-K / window engine addresses one streamed operand (index blocks,
+// query rows or keys of one (layer, KV head)) through a buffer resource with
+// 32-bit byte offsets, 256 bytes a row, a few tiles past the end included.
+constexpr int64_t kMaxStreamRows = ((int64_t)1 << 23) - 128;
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // The kernels move 16-byte vectors: tensor bases (and workspaces) must be 16-byte aligned.
@@ -194,7 +198,8 @@ kvs_status kvs_meank_score(const void* Q, const void* index, int32_t L, int32_t 
       (int64_t)L * H_kv > 65535 || nB > kMaxIndex)
     return KVS_ERR_SHAPE;
   if (D != 128) return KVS_ERR_UNSUPPORTED;
-  if (!grid_ok(cdiv((int64_t)(H_q / H_kv) * Mq, 256) * L * H_kv) || !grid_ok(cdiv(nB, 256) * L * H_kv))
+  if (!grid_ok(cdiv((int64_t)(H_q / H_kv) * Mq, 256) * L * H_kv) || !grid_ok(cdiv(nB, 256) * L * H_kv) ||
+      nB > kMaxStreamRows || (int64_t)(H_q / H_kv) * Mq > kMaxStreamRows)
     return KVS_ERR_SHAPE;
   if (nB == 0) return KVS_OK;
   const size_t need = kvs_meank_ws_bytes(L, H_q, H_kv, Mq, nB);
@@ -238,7 +243,8 @@ kvs_status kvs_window_score(const void* K, const void* Qw, int32_t L, int32_t H_
   if (L < 1 || H_q < 1 || H_kv < 1 || N < 0 || W < 1 || pi < 0 || q_s < 0 || q_e < q_s) return KVS_ERR_ARG;
   if (H_q % H_kv != 0 || N > kMaxIndex || numel4(L, H_kv, N, D) < 0 || numel4(L, H_q, W, D) < 0 ||
       (int64_t)L * H_kv > 65535 || (int64_t)(H_q / H_kv) * W > (int64_t)1 << 24 ||
-      !grid_ok(cdiv((int64_t)(H_q / H_kv) * W, 256) * L * H_kv) || !grid_ok(cdiv(N, 256) * L * H_kv))
+      !grid_ok(cdiv((int64_t)(H_q / H_kv) * W, 256) * L * H_kv) || !grid_ok(cdiv(N, 256) * L * H_kv) ||
+      N > kMaxStreamRows || (int64_t)(H_q / H_kv) * W > kMaxStreamRows)
     return KVS_ERR_SHAPE;
   if (D != 128) return KVS_ERR_UNSUPPORTED;
   if (N == 0) return KVS_OK;

@@ -60,24 +60,24 @@ struct Stage {
   float4 lse;
 };
 
-// Global -> registers for streamed tile rows [r0, r0+32) (rows >= limit are zero).
+// Global -> registers for streamed tile k: rows [32k, 32k+32) of a buffer
+// resource over the streamed rows (and, with lse, one over their lse2).  Rows
+// past the resource read as zero, so the loads need no branch: every tile,
+// the partial last one and those past the end alike, issues the same loads,
+// which lets the compiler keep a later tile's loads in flight while it waits
+// for an earlier one.
 template <bool WITH_LSE>
-__device__ __forceinline__ void stage_load(Stage& st, const uint16_t* base, int64_t r0, int64_t limit,
-                                           const float* lse) {
+__device__ __forceinline__ void stage_load(Stage& st, __amdgpu_buffer_rsrc_t rows, int k,
+                                           __amdgpu_buffer_rsrc_t lse) {
   const int t = threadIdx.x;
-  const char* tile = reinterpret_cast<const char*>(base + (size_t)r0 * D);
-  if (r0 + kTile <= limit) {            // full tile: no per-row checks
+  const int base = k * kTile * kRowBytes;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) st.w[i] = *reinterpret_cast<const u32x4*>(tile + (t + 256 * i) * 16);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int idx = t + 256 * i;
-      st.w[i] = r0 + (idx >> 4) < limit ? *reinterpret_cast<const u32x4*>(tile + idx * 16)
-                                        : u32x4{0u, 0u, 0u, 0u};
-    }
+  for (int i = 0; i < 2; ++i)
+    st.w[i] = __builtin_amdgcn_raw_buffer_load_b128(rows, base + (t + 256 * i) * 16, 0, 0);
+  if (WITH_LSE) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(lse, t < 8 ? (k * kTile + 4 * t) * 4 : 0x7ffffff0, 0, 0);
+    st.lse = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
   }
-  if (WITH_LSE && t < 8) st.lse = *reinterpret_cast<const float4*>(lse + r0 + 4 * t);
 }
 
 template <bool WITH_LSE>
@@ -259,13 +259,19 @@ __global__ __launch_bounds__(256, 2) void meank_pass(const uint16_t* __restrict_
   }
   const int nt = (int)((s_end - s_begin + kTile - 1) / kTile);
 
-  Stage st;
-  stage_load<!PASS1>(st, sbase, s_begin, s_end, Lg);
-  stage_store<!PASS1>(st, tiles[0], lses[0]);
-  if (nt > 1) {
-    stage_load<!PASS1>(st, sbase, s_begin + kTile, s_end, Lg);
-    stage_store<!PASS1>(st, tiles[1], lses[1]);
-  }
+  // Tiles reach LDS two at a time (double buffer); global loads run ahead of
+  // them in a ring of two register stages, so a tile's load is issued two
+  // iterations before its LDS store and an L2 miss has ~two tiles of MFMA
+  // work to hide behind.
+  // streamed rows [s_begin, s_end) and, in pass 2, their lse2 (tile k = rows 32k..)
+  const __amdgpu_buffer_rsrc_t srows = buf_rsrc(sbase + (size_t)s_begin * D, (int)((s_end - s_begin) * kRowBytes));
+  const __amdgpu_buffer_rsrc_t slse = buf_rsrc(Lg, PASS1 ? 0 : (int)(rows_pad * 4));
+  Stage st[2];
+  stage_load<!PASS1>(st[0], srows, 0, slse);
+  stage_store<!PASS1>(st[0], tiles[0], lses[0]);
+  stage_load<!PASS1>(st[0], srows, 1, slse);
+  stage_store<!PASS1>(st[0], tiles[1], lses[1]);
+  stage_load<!PASS1>(st[0], srows, 2, slse);
   __syncthreads();
 
   // A wave whose persistent rows all lie past the end (the window score's
@@ -298,10 +304,13 @@ __global__ __launch_bounds__(256, 2) void meank_pass(const uint16_t* __restrict_
     m1 = fmaxf(m1, __shfl_xor(m1, 32, kWave));
   }
 
-  // Process tile t (accumulators cc, lse lc) while issuing tile t+1 into cn.
-  auto body = [&](int t, f32x16& cc0, f32x16& cc1, float* lc, f32x16& cn0, f32x16& cn1, float* ln) {
+  // Process tile t (accumulators cc, lse lc) while issuing tile t+1 into cn;
+  // load tile t+3 into stage sl (t odd: st[0], t even: st[1]) and move tile
+  // t+2, loaded one iteration earlier, from stage ss into LDS.
+  auto body = [&](int t, f32x16& cc0, f32x16& cc1, float* lc, f32x16& cn0, f32x16& cn1, float* ln,
+                  Stage& sl, Stage& ss) {
     const bool pre = t + 2 < nt;
-    if (pre) stage_load<!PASS1>(st, sbase, s_begin + (int64_t)(t + 2) * kTile, s_end, Lg);
+    stage_load<!PASS1>(sl, srows, t + 3, slse);   // past the end: reads nothing, returns zeros
     read_streamed(tiles[(t + 1) & 1], lane, A);
     if (!PASS1) read_lse16(lses[(t + 1) & 1], h, ln);
     float a0 = 0.f, a1 = 0.f;
@@ -323,20 +332,20 @@ __global__ __launch_bounds__(256, 2) void meank_pass(const uint16_t* __restrict_
       s0 += a0;
       s1 += a1;
     }
-    if (pre) stage_store<!PASS1>(st, tiles[t & 1], lses[t & 1]);
+    if (pre) stage_store<!PASS1>(ss, tiles[t & 1], lses[t & 1]);
     __syncthreads();
   };
 
   int t = 0;
   for (; t + 2 < nt; t += 2) {
-    body(t, cA0, cA1, lA, cB0, cB1, lB);
-    body(t + 1, cB0, cB1, lB, cA0, cA1, lA);
+    body(t, cA0, cA1, lA, cB0, cB1, lB, st[1], st[0]);
+    body(t + 1, cB0, cB1, lB, cA0, cA1, lA, st[0], st[1]);
   }
   f32x16* last0 = &cA0;
   f32x16* last1 = &cA1;
   float* llast = lA;
   if (t + 1 < nt) {
-    body(t, cA0, cA1, lA, cB0, cB1, lB);
+    body(t, cA0, cA1, lA, cB0, cB1, lB, st[1], st[0]);
     last0 = &cB0;
     last1 = &cB1;
     llast = lB;

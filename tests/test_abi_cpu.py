@@ -167,6 +167,12 @@ def test_oversized_launches_are_rejected(lib):
     assert r(FAKE, None, 640, FAKE, None, 1 << 24, 2, 2, 128, 32, 0, 1e6, FAKE, None, 8, None, None) == 2
     ws = 1 << 30
     assert lib.kvs_meank_score(FAKE, FAKE, 4, 8, 2, 128, 50, (1 << 31) - 1, 4, 7, FAKE, FAKE, ws, None) == 2
+    # streamed operands past 2^23 - 128 rows (32-bit buffer offsets): index blocks, query rows, keys, window rows
+    big = (1 << 23) - 127
+    assert lib.kvs_meank_score(FAKE, FAKE, 1, 2, 2, 128, 4, big, 4, 7, FAKE, FAKE, ws, None) == 2
+    assert lib.kvs_meank_score(FAKE, FAKE, 1, 2, 1, 128, big // 2 + 1, 1000, 4, 7, FAKE, FAKE, ws, None) == 2
+    assert lib.kvs_window_score(FAKE, FAKE, 1, 2, 2, 128, big, 4, 4, 0, 0, FAKE, FAKE, ws, None) == 2
+    assert lib.kvs_window_score(FAKE, FAKE, 1, 2, 1, 128, 1000, big // 2 + 1, 4, 0, 0, FAKE, FAKE, ws, None) == 2
 
 
 def test_binding_refuses_cpu_tensors():
