@@ -9,7 +9,8 @@
 // find the threshold key T and
 // the number of threshold ties k to keep; ballot/popcount ranks make the
 // output ascending and hand the k ties to the lowest indices.  Up to 32768
-// scores the keys stay in registers for the whole selection.
+// scores the keys stay in registers for the whole selection; beyond that each
+// pass streams them from L2 in batches with all of a batch's loads in flight.
 #include "kvs_internal.h"
 
 using namespace kvs;
@@ -19,13 +20,6 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 
-__device__ __forceinline__ uint32_t score_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0u;
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
 __device__ __forceinline__ uint32_t rank_below(uint64_t mask, int lane) {
   return (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
 }
@@ -34,147 +28,6 @@ struct Forced {
   int f0b, f0e, f1b, f1e;
   __device__ bool operator()(int j) const { return (j >= f0b && j < f0e) || (j >= f1b && j < f1e); }
 };
-
-// Inputs too large for the register-resident kernel below: every pass re-reads
-// the scores from global memory (L2-resident) with 4 loads in flight per thread.
-constexpr int kUnroll = 4;
-
-__global__ __launch_bounds__(kThreads) void topk_select_kernel(
-    const float* __restrict__ score, int n, Forced forced, int c_star, int n_forced,
-    uint8_t* __restrict__ keep_mask, int32_t* __restrict__ keep_idx, int64_t* __restrict__ n_kept) {
-  __shared__ uint32_t hist[kWaves][256];
-  __shared__ uint32_t wmin[kWaves], wmax[kWaves];
-  __shared__ uint32_t wcnt[kWaves][2];
-  __shared__ uint32_t state[2];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const bool none = c_star == 0;   // C <= |F|: keep the forced set only
-
-  auto key_at = [&](int j) -> uint32_t { return score_key(score[j]); };
-
-  uint32_t kT = 0xffffffffu, k_tie = 0;
-  if (!none) {
-    uint32_t mn = 0xffffffffu, mx = 0u;
-    for (int j0 = tid; j0 < n; j0 += kThreads * kUnroll) {
-      uint32_t k[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int j = j0 + u * kThreads;
-        k[u] = j < n ? key_at(j) : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int j = j0 + u * kThreads;
-        if (j < n && !forced(j)) { mn = min(mn, k[u]); mx = max(mx, k[u]); }
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
-      mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
-    }
-    if (lane == 0) { wmin[wave] = mn; wmax[wave] = mx; }
-    __syncthreads();
-    mn = wmin[0]; mx = wmax[0];
-    for (int w = 1; w < kWaves; ++w) { mn = min(mn, wmin[w]); mx = max(mx, wmax[w]); }
-    const uint32_t range = mx - mn;
-    const int bits = range ? 32 - __clz(range) : 0;
-    const int ndig = (bits + 7) / 8;
-    uint32_t prefix = 0, k = (uint32_t)c_star;
-    for (int p = 0; p < ndig; ++p) {
-      for (int i = tid; i < kWaves * 256; i += kThreads) (&hist[0][0])[i] = 0u;
-      __syncthreads();
-      const int sh = max(bits - 8 * (p + 1), 0), wd = bits - 8 * p - sh;   // top-aligned digits
-      for (int j0 = tid; j0 < n; j0 += kThreads * kUnroll) {
-        uint32_t kk[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          const int j = j0 + u * kThreads;
-          kk[u] = j < n ? key_at(j) : 0u;
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          const int j = j0 + u * kThreads;
-          if (j >= n || forced(j)) continue;
-          const uint32_t rel = kk[u] - mn;
-          const uint32_t hi = (uint32_t)((uint64_t)rel >> (sh + wd));
-          if (hi == prefix) atomicAdd(&hist[wave][(rel >> sh) & ((1u << wd) - 1u)], 1u);
-        }
-      }
-      __syncthreads();
-      if (wave == 0) {
-        uint32_t c[4], lsum = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          uint32_t t = 0;
-          for (int w = 0; w < kWaves; ++w) t += hist[w][4 * lane + i];
-          c[i] = t;
-          lsum += t;
-        }
-        // inclusive suffix sum over lanes: elements in bins >= 4*lane
-        uint32_t incl = lsum;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t t = (uint32_t)__shfl_down((int)incl, o, kWave);
-          if (lane + o < 64) incl += t;
-        }
-        const uint32_t above = incl - lsum;
-        if (above < k && k <= incl) {
-          uint32_t a = above;
-          for (int i = 3; i >= 0; --i) {
-            if (a + c[i] >= k) {
-              state[0] = (prefix << wd) | (uint32_t)(4 * lane + i);
-              state[1] = k - a;
-              break;
-            }
-            a += c[i];
-          }
-        }
-      }
-      __syncthreads();
-      prefix = state[0];
-      k = state[1];
-      __syncthreads();
-    }
-    kT = mn + prefix;
-    k_tie = k;
-  }
-
-  // Emit: wave w owns positions [w*seg, (w+1)*seg).
-  const int seg = (((n + kWaves - 1) / kWaves) + 63) / 64 * 64;
-  const int s0 = wave * seg, s1 = min(n, s0 + seg);
-  uint32_t c_def = 0, c_tie = 0;
-  for (int base = s0; base < s1; base += 64) {
-    const int j = base + lane;
-    const bool in = j < s1;
-    const bool f = in && forced(j);
-    const bool cand = in && !f && !none;
-    const uint32_t key = cand ? key_at(j) : 0u;
-    c_def += (uint32_t)__popcll(__ballot(f || (cand && key > kT)));
-    c_tie += (uint32_t)__popcll(__ballot(cand && key == kT));
-  }
-  if (lane == 0) { wcnt[wave][0] = c_def; wcnt[wave][1] = c_tie; }
-  __syncthreads();
-  uint32_t def_base = 0, tie_base = 0;
-  for (int w = 0; w < wave; ++w) { def_base += wcnt[w][0]; tie_base += wcnt[w][1]; }
-  uint32_t out = def_base + min(tie_base, k_tie);
-  uint32_t tie_run = tie_base;
-  for (int base = s0; base < s1; base += 64) {
-    const int j = base + lane;
-    const bool in = j < s1;
-    const bool f = in && forced(j);
-    const bool cand = in && !f && !none;
-    const uint32_t key = cand ? key_at(j) : 0u;
-    const bool tie = cand && key == kT;
-    const uint64_t bt = __ballot(tie);
-    const bool keep = f || (cand && key > kT) || (tie && tie_run + rank_below(bt, lane) < k_tie);
-    const uint64_t bk = __ballot(keep);
-    if (in) keep_mask[j] = keep ? 1 : 0;
-    if (keep) keep_idx[out + rank_below(bk, lane)] = j;
-    tie_run += (uint32_t)__popcll(bt);
-    out += (uint32_t)__popcll(bk);
-  }
-  if (tid == 0) *n_kept = (int64_t)n_forced + c_star;
-}
 
 // Keys held in registers, for n <= 1024 * KPT: thread t owns positions
 // j = 1024u + t (u < KPT), so the scores are read once, with every load of a
@@ -373,6 +226,179 @@ __global__ __launch_bounds__(kThreads) void topk_reg_kernel(
   if (tid == 0) *n_kept = (int64_t)n_forced + c_star;
 }
 
+// Inputs too large to keep in registers: every pass streams the scores from
+// global memory (L2-resident after the first) in batches of kStreamU keys
+// per thread, all of a batch's loads in flight together, with the same key
+// classes, top-aligned digits and double-buffered histograms as above.  The
+// emit pass ranks one batch at a time: per-(key slot, wave) counts scanned in
+// position order within the batch, on top of running totals of the batches
+// before it.
+constexpr int kStreamU = 16;
+
+__global__ __launch_bounds__(kThreads) void topk_stream_kernel(
+    const float* __restrict__ score, int n, Forced forced, int c_star, int n_forced,
+    uint8_t* __restrict__ keep_mask, int32_t* __restrict__ keep_idx, int64_t* __restrict__ n_kept) {
+  constexpr int U = kStreamU;
+  __shared__ uint32_t hist[2][kWaves][256];
+  __shared__ uint32_t wred[kWaves][2];
+  __shared__ uint32_t state[2];
+  __shared__ uint32_t cnt[2][U][kWaves];   // [kept-by-value | ties][u][wave] of the current batch
+  __shared__ uint32_t ubase[2][U];
+  __shared__ uint32_t btotal[2];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  constexpr int kBatch = kThreads * U;
+
+  // keys of positions b0 + 1024u + tid, u < U, classed as in topk_reg_kernel
+  // (positions in 64 bits: a batch may reach past 2^31 - 1)
+  auto load_keys = [&](int64_t b0, uint32_t* key) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = score[min(b0 + u * kThreads + tid, (int64_t)n - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = b0 + u * kThreads + tid;
+      key[u] = j >= n ? kKeyOut : (forced((int)j) ? kKeyForced : cand_key(v[u]));
+    }
+  };
+  auto is_cand = [](uint32_t k) -> bool { return (k != kKeyOut) & (k != kKeyForced); };
+
+  uint32_t kT = 0xfffffffeu, k_tie = 0;   // c_star == 0 keeps the forced set only
+  if (c_star > 0) {
+    for (int i = tid; i < kWaves * 256; i += kThreads) (&hist[0][0][0])[i] = 0u;
+    uint32_t mn = 0xffffffffu, mx = 0u;
+    for (int64_t b0 = 0; b0 < n; b0 += kBatch) {
+      uint32_t key[U];
+      load_keys(b0, key);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool c = is_cand(key[u]);
+        mn = min(mn, c ? key[u] : 0xffffffffu);
+        mx = max(mx, c ? key[u] : 0u);
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
+      mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
+    }
+    if (lane == 0) { wred[wave][0] = mn; wred[wave][1] = mx; }
+    __syncthreads();
+    mn = wred[0][0]; mx = wred[0][1];
+    for (int w = 1; w < kWaves; ++w) { mn = min(mn, wred[w][0]); mx = max(mx, wred[w][1]); }
+    const uint32_t range = mx - mn;
+    const int bits = range ? 32 - __clz(range) : 0;
+    const int ndig = (bits + 7) / 8;
+    uint32_t prefix = 0, k = (uint32_t)c_star;
+    int buf = 0;
+    for (int p = 0; p < ndig; ++p) {
+      const int sh = max(bits - 8 * (p + 1), 0), wd = bits - 8 * p - sh;
+      uint32_t* h = &hist[buf][wave][0];
+      for (int64_t b0 = 0; b0 < n; b0 += kBatch) {
+        uint32_t key[U];
+        load_keys(b0, key);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint32_t rel = key[u] - mn;
+          const uint32_t hi = (uint32_t)((uint64_t)rel >> (sh + wd));
+          if (is_cand(key[u]) & (hi == prefix)) atomicAdd(h + ((rel >> sh) & ((1u << wd) - 1u)), 1u);
+        }
+      }
+      for (int i = tid; i < kWaves * 256; i += kThreads) (&hist[buf ^ 1][0][0])[i] = 0u;
+      __syncthreads();
+      if (wave == 0) {
+        uint32_t c[4] = {0u, 0u, 0u, 0u};
+        for (int w = 0; w < kWaves; ++w) {
+          const u32x4 hv = *reinterpret_cast<const u32x4*>(&hist[buf][w][4 * lane]);
+          c[0] += hv[0]; c[1] += hv[1]; c[2] += hv[2]; c[3] += hv[3];
+        }
+        const uint32_t lsum = c[0] + c[1] + c[2] + c[3];
+        uint32_t incl = lsum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t t = (uint32_t)__shfl_down((int)incl, o, kWave);
+          if (lane + o < 64) incl += t;
+        }
+        const uint32_t above = incl - lsum;
+        if (above < k && k <= incl) {
+          uint32_t a = above;
+          for (int i = 3; i >= 0; --i) {
+            if (a + c[i] >= k) {
+              state[0] = (prefix << wd) | (uint32_t)(4 * lane + i);
+              state[1] = k - a;
+              break;
+            }
+            a += c[i];
+          }
+        }
+      }
+      __syncthreads();
+      prefix = state[0];
+      k = state[1];
+      buf ^= 1;
+    }
+    kT = mn + prefix;
+    k_tie = k;
+  }
+
+  // Emit, one batch at a time, ranks continuing from the batches before.
+  uint32_t run_def = 0, run_tie = 0;
+  for (int64_t b0 = 0; b0 < n; b0 += kBatch) {
+    uint32_t key[U];
+    load_keys(b0, key);
+    uint32_t cv0 = 0u, cv1 = 0u;                 // lane u: this wave's counts of key slot u
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t nd = (uint32_t)__popcll(__ballot(key[u] > kT));
+      const uint32_t nt = (uint32_t)__popcll(__ballot(key[u] == kT));
+      if (lane == u) { cv0 = nd; cv1 = nt; }
+    }
+    if (lane < U) { cnt[0][lane][wave] = cv0; cnt[1][lane][wave] = cv1; }
+    __syncthreads();
+    if (tid < 2 * U) {
+      const int which = tid / U, u = tid - which * U;
+      uint32_t run = 0;
+      for (int w = 0; w < kWaves; ++w) {
+        const uint32_t c = cnt[which][u][w];
+        cnt[which][u][w] = run;
+        run += c;
+      }
+      ubase[which][u] = run;
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int which = 0; which < 2; ++which) {
+        const uint32_t a = lane < U ? ubase[which][lane] : 0u;
+        uint32_t incl = a;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t t = (uint32_t)__shfl_up((int)incl, o, kWave);
+          if (lane >= o) incl += t;
+        }
+        if (lane < U) ubase[which][lane] = incl - a;
+        if (lane == 63) btotal[which] = incl;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = b0 + u * kThreads + tid;
+      const bool tie = key[u] == kT;
+      const uint64_t bt = __ballot(tie);
+      const uint32_t def_before = run_def + ubase[0][u] + cnt[0][u][wave];
+      const uint32_t tie_before = run_tie + ubase[1][u] + cnt[1][u][wave];
+      const bool keep = (key[u] > kT) | (tie & (tie_before + rank_below(bt, lane) < k_tie));
+      const uint64_t bk = __ballot(keep);
+      if (j < n) keep_mask[j] = keep ? 1 : 0;
+      if (keep) keep_idx[def_before + min(tie_before, k_tie) + rank_below(bk, lane)] = (int32_t)j;
+    }
+    run_def += btotal[0];
+    run_tie += btotal[1];
+    __syncthreads();   // the next batch rewrites cnt, ubase and btotal
+  }
+  if (tid == 0) *n_kept = (int64_t)n_forced + c_star;
+}
+
 // C* >= |H|: everything is kept.
 __global__ __launch_bounds__(256) void keep_all_kernel(int n, uint8_t* __restrict__ keep_mask,
                                                        int32_t* __restrict__ keep_idx,
@@ -411,7 +437,7 @@ hipError_t kvs_launch_topk(const float* score, int64_t n, int64_t f0b, int64_t f
   else if (n <= 32 * kThreads) TOPK_REG(32);
 #undef TOPK_REG
   else
-    hipLaunchKernelGGL(topk_select_kernel, dim3(1), dim3(kThreads), 0, st, score, (int)n, f,
+    hipLaunchKernelGGL(topk_stream_kernel, dim3(1), dim3(kThreads), 0, st, score, (int)n, f,
                        (int)c_star, (int)n_forced, keep_mask, keep_idx, n_kept);
   return hipGetLastError();
 }
