@@ -135,7 +135,9 @@ kvs_status kvs_topk_select(const float* score, int64_t n, int64_t f0_begin, int6
   if (n < 0 || C < 0 || f0_end < f0_begin || f1_end < f1_begin) return KVS_ERR_ARG;
   if (n > kMaxIndex) return KVS_ERR_SHAPE;
   const size_t need = kvs_topk_ws_bytes(n);
-  if (need && (!ws || ws_bytes < need)) return KVS_ERR_WORKSPACE;
+  if (need && ws && ws_bytes < need) return KVS_ERR_WORKSPACE;   // no workspace: one-workgroup path
+  if (need && ((uintptr_t)ws & 3)) return KVS_ERR_ARG;
+  if (!need) ws = nullptr;
   clip_range(n, f0_begin, f0_end);
   clip_range(n, f1_begin, f1_end);
   const int64_t lo = f0_begin > f1_begin ? f0_begin : f1_begin;

@@ -399,6 +399,235 @@ __global__ __launch_bounds__(kThreads) void topk_stream_kernel(
   if (tid == 0) *n_kept = (int64_t)n_forced + c_star;
 }
 
+// Multi-workgroup selection for n > 32768: one workgroup of 256 threads per
+// 2048-position slice, each thread holding 8 classed keys, and a few short
+// launches instead of one workgroup's long passes (whose LDS-atomic
+// histograms over every key are what limits them).  State lives in the
+// workspace: candidate key min/max, the radix prefix and the count k still to
+// place, an arrival ticket, a 256-bin histogram and per-slice counts.
+//   topk_mw_init     state <- (min = ~0, max = 0, prefix 0, k = C*), histogram 0
+//   topk_mw_minmax   per-slice min/max of the candidate keys -> atomicMin/Max
+//   topk_mw_pass<p>  digit p of the range, top-aligned: each slice adds its
+//                    histogram of the prefix-matching keys with integer atomics
+//                    (sums independent of order); the last slice to arrive
+//                    picks the bin, advances prefix and k, clears the histogram
+//   topk_mw_count    per-slice counts of kept-by-value and tie positions
+//   topk_mw_emit     each slice ranks its positions from the counts before it
+constexpr int kMwThreads = 256;
+constexpr int kMwKeys = 8;                          // keys per thread
+constexpr int kMwSlice = kMwThreads * kMwKeys;      // positions per workgroup
+constexpr int kMwWaves = kMwThreads / 64;
+enum { kMwMin = 0, kMwMax, kMwPrefix, kMwK, kMwTicket, kMwHist = 16, kMwCounts = kMwHist + 256 };
+
+struct MwArgs {
+  const float* score;
+  int n;
+  Forced forced;
+  int c_star;
+  uint32_t* ws;
+};
+
+// Keys of positions slice0 + 256u + tid, classed as in topk_reg_kernel.
+__device__ __forceinline__ void mw_keys(const MwArgs& a, uint32_t* key) {
+  const int64_t slice0 = (int64_t)blockIdx.x * kMwSlice;
+  float v[kMwKeys];
+#pragma unroll
+  for (int u = 0; u < kMwKeys; ++u) v[u] = a.score[min(slice0 + u * kMwThreads + threadIdx.x, (int64_t)a.n - 1)];
+#pragma unroll
+  for (int u = 0; u < kMwKeys; ++u) {
+    const int64_t j = slice0 + u * kMwThreads + threadIdx.x;
+    key[u] = j >= a.n ? kKeyOut : (a.forced((int)j) ? kKeyForced : cand_key(v[u]));
+  }
+}
+__device__ __forceinline__ bool mw_cand(uint32_t k) { return (k != kKeyOut) & (k != kKeyForced); }
+
+__device__ __forceinline__ uint32_t mw_load(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ __launch_bounds__(kMwThreads) void topk_mw_init(MwArgs a, int64_t n_kept_value, int64_t* n_kept) {
+  uint32_t* ws = a.ws;
+  const int t = threadIdx.x;
+  if (t == 0) {
+    ws[kMwMin] = 0xffffffffu;
+    ws[kMwMax] = 0u;
+    ws[kMwPrefix] = 0u;
+    ws[kMwK] = (uint32_t)a.c_star;
+    ws[kMwTicket] = 0u;
+    *n_kept = n_kept_value;
+  }
+  ws[kMwHist + t] = 0u;
+}
+
+__global__ __launch_bounds__(kMwThreads) void topk_mw_minmax(MwArgs a) {
+  uint32_t key[kMwKeys];
+  mw_keys(a, key);
+  uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+  for (int u = 0; u < kMwKeys; ++u) {
+    const bool c = mw_cand(key[u]);
+    mn = min(mn, c ? key[u] : 0xffffffffu);
+    mx = max(mx, c ? key[u] : 0u);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    if (mn != 0xffffffffu) atomicMin(a.ws + kMwMin, mn);
+    if (mx != 0u) atomicMax(a.ws + kMwMax, mx);
+  }
+}
+
+__global__ __launch_bounds__(kMwThreads) void topk_mw_pass(MwArgs a, int p) {
+  __shared__ uint32_t hist[kMwWaves][256];
+  __shared__ uint32_t s_last;
+  uint32_t* ws = a.ws;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const uint32_t mn = mw_load(ws + kMwMin), mx = mw_load(ws + kMwMax);
+  const uint32_t range = mx - mn;
+  const int bits = range ? 32 - __clz(range) : 0;
+  if (p >= (bits + 7) / 8) return;                   // every workgroup alike: this digit does not exist
+  const int sh = max(bits - 8 * (p + 1), 0), wd = bits - 8 * p - sh;
+  const uint32_t prefix = mw_load(ws + kMwPrefix);
+  for (int i = t; i < kMwWaves * 256; i += kMwThreads) (&hist[0][0])[i] = 0u;
+  uint32_t key[kMwKeys];
+  mw_keys(a, key);
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kMwKeys; ++u) {
+    const uint32_t rel = key[u] - mn;
+    const uint32_t hi = (uint32_t)((uint64_t)rel >> (sh + wd));
+    if (mw_cand(key[u]) & (hi == prefix)) atomicAdd(&hist[wave][(rel >> sh) & ((1u << wd) - 1u)], 1u);
+  }
+  __syncthreads();
+  {
+    uint32_t c = 0;
+#pragma unroll
+    for (int w = 0; w < kMwWaves; ++w) c += hist[w][t];
+    if (c) atomicAdd(ws + kMwHist + t, c);
+  }
+  __threadfence();                                   // the bins are added before this slice arrives
+  __syncthreads();
+  if (t == 0) s_last = atomicAdd(ws + kMwTicket, 1u) == gridDim.x - 1;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  if (wave == 0) {
+    // suffix scan over the 256 bins: lane l holds bins 4l..4l+3
+    uint32_t c[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = mw_load(ws + kMwHist + 4 * lane + i);
+    const uint32_t lsum = c[0] + c[1] + c[2] + c[3];
+    uint32_t incl = lsum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t v = (uint32_t)__shfl_down((int)incl, o, kWave);
+      if (lane + o < 64) incl += v;
+    }
+    const uint32_t above = incl - lsum;
+    const uint32_t k = mw_load(ws + kMwK);
+    if (above < k && k <= incl) {
+      uint32_t acc = above;
+      for (int i = 3; i >= 0; --i) {
+        if (acc + c[i] >= k) {
+          ws[kMwPrefix] = (prefix << wd) | (uint32_t)(4 * lane + i);
+          ws[kMwK] = k - acc;
+          break;
+        }
+        acc += c[i];
+      }
+    }
+  }
+  __syncthreads();                                   // wave 0 has read every bin before any is cleared
+  ws[kMwHist + t] = 0u;                              // clean for the next digit
+  if (t == 0) ws[kMwTicket] = 0u;
+}
+
+// threshold key T and ties to keep, from the state the passes left
+__device__ __forceinline__ void mw_threshold(const MwArgs& a, uint32_t& kT, uint32_t& k_tie) {
+  if (a.c_star == 0) { kT = 0xfffffffeu; k_tie = 0u; return; }
+  kT = mw_load(a.ws + kMwMin) + mw_load(a.ws + kMwPrefix);
+  k_tie = mw_load(a.ws + kMwK);
+}
+
+__global__ __launch_bounds__(kMwThreads) void topk_mw_count(MwArgs a) {
+  __shared__ uint32_t part[kMwWaves][2];
+  uint32_t kT, k_tie;
+  mw_threshold(a, kT, k_tie);
+  uint32_t key[kMwKeys];
+  mw_keys(a, key);
+  uint32_t nd = 0, nt = 0;
+#pragma unroll
+  for (int u = 0; u < kMwKeys; ++u) {
+    nd += (uint32_t)__popcll(__ballot(key[u] > kT));
+    nt += (uint32_t)__popcll(__ballot(key[u] == kT));
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { part[wave][0] = nd; part[wave][1] = nt; }
+  __syncthreads();
+  if (threadIdx.x < 2) {
+    uint32_t c = 0;
+    for (int w = 0; w < kMwWaves; ++w) c += part[w][threadIdx.x];
+    a.ws[kMwCounts + 2 * blockIdx.x + threadIdx.x] = c;
+  }
+}
+
+__global__ __launch_bounds__(kMwThreads) void topk_mw_emit(MwArgs a, uint8_t* __restrict__ keep_mask,
+                                                           int32_t* __restrict__ keep_idx) {
+  __shared__ uint32_t cnt[2][kMwKeys][kMwWaves];
+  __shared__ uint32_t base[2];
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  uint32_t kT, k_tie;
+  mw_threshold(a, kT, k_tie);
+  uint32_t key[kMwKeys];
+  mw_keys(a, key);
+  // counts of the slices before this one, summed in slice order by wave 0
+  if (wave == 0) {
+    uint32_t d = 0, e = 0;
+    for (int w = lane; w < (int)blockIdx.x; w += 64) {
+      d += a.ws[kMwCounts + 2 * w];
+      e += a.ws[kMwCounts + 2 * w + 1];
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      d += (uint32_t)__shfl_xor((int)d, o, kWave);
+      e += (uint32_t)__shfl_xor((int)e, o, kWave);
+    }
+    if (lane == 0) { base[0] = d; base[1] = e; }
+  }
+#pragma unroll
+  for (int u = 0; u < kMwKeys; ++u) {
+    const uint32_t nd = (uint32_t)__popcll(__ballot(key[u] > kT));
+    const uint32_t nt = (uint32_t)__popcll(__ballot(key[u] == kT));
+    if (lane == 0) { cnt[0][u][wave] = nd; cnt[1][u][wave] = nt; }
+  }
+  __syncthreads();
+  if (t < 2) {                                       // exclusive prefix over (u, wave) in position order
+    uint32_t run = base[t];
+    for (int u = 0; u < kMwKeys; ++u)
+      for (int w = 0; w < kMwWaves; ++w) {
+        const uint32_t c = cnt[t][u][w];
+        cnt[t][u][w] = run;
+        run += c;
+      }
+  }
+  __syncthreads();
+  const int64_t slice0 = (int64_t)blockIdx.x * kMwSlice;
+#pragma unroll
+  for (int u = 0; u < kMwKeys; ++u) {
+    const int64_t j = slice0 + u * kMwThreads + t;
+    const bool tie = key[u] == kT;
+    const uint64_t bt = __ballot(tie);
+    const uint32_t def_before = cnt[0][u][wave], tie_before = cnt[1][u][wave];
+    const bool keep = (key[u] > kT) | (tie & (tie_before + rank_below(bt, lane) < k_tie));
+    const uint64_t bk = __ballot(keep);
+    if (j < a.n) keep_mask[j] = keep ? 1 : 0;
+    if (keep) keep_idx[def_before + min(tie_before, k_tie) + rank_below(bk, lane)] = (int32_t)j;
+  }
+}
+
 // C* >= |H|: everything is kept.
 __global__ __launch_bounds__(256) void keep_all_kernel(int n, uint8_t* __restrict__ keep_mask,
                                                        int32_t* __restrict__ keep_idx,
@@ -418,11 +647,17 @@ __global__ __launch_bounds__(256) void slotmap_kernel(const int64_t* __restrict_
 
 }  // namespace
 
-size_t kvs_topk_ws_bytes(int64_t) { return 0; }
+// n > 32768 takes the multi-workgroup path: state words, a histogram and two
+// counts per 2048-position slice.
+size_t kvs_topk_ws_bytes(int64_t n) {
+  if (n <= 32 * kThreads) return 0;
+  const int64_t slices = (n + kMwSlice - 1) / kMwSlice;
+  return (size_t)(kMwCounts + 2 * slices) * 4;
+}
 
 hipError_t kvs_launch_topk(const float* score, int64_t n, int64_t f0b, int64_t f0e, int64_t f1b,
                            int64_t f1e, int64_t n_forced, int64_t c_star, uint8_t* keep_mask,
-                           int32_t* keep_idx, int64_t* n_kept, void*, hipStream_t st) {
+                           int32_t* keep_idx, int64_t* n_kept, void* ws, hipStream_t st) {
   if (c_star >= n - n_forced) {   // includes n == 0: still writes n_kept
     const unsigned blocks = n > 0 ? ceil_div(n, 256) : 1u;
     hipLaunchKernelGGL(keep_all_kernel, dim3(blocks), dim3(256), 0, st, (int)n, keep_mask, keep_idx,
@@ -436,9 +671,20 @@ hipError_t kvs_launch_topk(const float* score, int64_t n, int64_t f0b, int64_t f
   if (n <= 8 * kThreads) TOPK_REG(8);
   else if (n <= 32 * kThreads) TOPK_REG(32);
 #undef TOPK_REG
-  else
+  else if (ws == nullptr)
     hipLaunchKernelGGL(topk_stream_kernel, dim3(1), dim3(kThreads), 0, st, score, (int)n, f,
                        (int)c_star, (int)n_forced, keep_mask, keep_idx, n_kept);
+  else {
+    MwArgs a{score, (int)n, f, (int)c_star, static_cast<uint32_t*>(ws)};
+    const dim3 grid((unsigned)((n + kMwSlice - 1) / kMwSlice)), block(kMwThreads);
+    hipLaunchKernelGGL(topk_mw_init, dim3(1), block, 0, st, a, (int64_t)n_forced + c_star, n_kept);
+    if (c_star > 0) {
+      hipLaunchKernelGGL(topk_mw_minmax, grid, block, 0, st, a);
+      for (int p = 0; p < 4; ++p) hipLaunchKernelGGL(topk_mw_pass, grid, block, 0, st, a, p);
+    }
+    hipLaunchKernelGGL(topk_mw_count, grid, block, 0, st, a);
+    hipLaunchKernelGGL(topk_mw_emit, grid, block, 0, st, a, keep_mask, keep_idx);
+  }
   return hipGetLastError();
 }
 

@@ -199,8 +199,12 @@ def kvs_topk_workspace(n):
     return load().kvs_topk_workspace(n)
 
 
-def kvs_topk_select(score, f0, f1, C, keep_mask=None, keep_idx=None, n_kept=None, ws=None):
-    """Returns (keep_mask uint8 [n], keep_idx int32 [n], n_kept int64 [1]) on the device."""
+def kvs_topk_select(score, f0, f1, C, keep_mask=None, keep_idx=None, n_kept=None, ws=None,
+                    single_workgroup=False):
+    """Returns (keep_mask uint8 [n], keep_idx int32 [n], n_kept int64 [1]) on the device.
+
+    Above 32768 scores the library selects with several workgroups through a
+    small workspace; single_workgroup=True passes none (the slower path)."""
     _dev(score, keep_mask, keep_idx, n_kept, ws)
     if score.dtype != torch.float32:
         raise TypeError("score must be float32")
@@ -213,7 +217,9 @@ def kvs_topk_select(score, f0, f1, C, keep_mask=None, keep_idx=None, n_kept=None
     _need(keep_idx.dtype == torch.int32 and keep_idx.numel() >= n, "keep_idx must be int32 [n]")
     _need(n_kept.dtype == torch.int64 and n_kept.numel() >= 1, "n_kept must be int64 [1]")
     need = kvs_topk_workspace(n)
-    if need:
+    if single_workgroup:
+        ws = None
+    elif need:
         ws = _workspace(need, dev, ws)
     _check("kvs_topk_select", load().kvs_topk_select(
         _ptr(score), n, f0[0], f0[1], f1[0], f1[1], C, _ptr(keep_mask), _ptr(keep_idx),

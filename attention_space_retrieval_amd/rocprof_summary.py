@@ -31,7 +31,9 @@ KERNEL_SOURCES = {
     "qmem_kernel": "qmem.hip",
     "rule_logits_mfma": "rule_score.hip", "rule_logits_f32": "rule_score.hip",
     "rule_lse_merge": "rule_score.hip", "rule_colsum": "rule_score.hip",
-    "topk_select_kernel": "topk.hip", "topk_reg_kernel": "topk.hip", "keep_all_kernel": "topk.hip",
+    "topk_reg_kernel": "topk.hip", "topk_stream_kernel": "topk.hip", "topk_mw_init": "topk.hip",
+    "topk_mw_minmax": "topk.hip", "topk_mw_pass": "topk.hip", "topk_mw_count": "topk.hip",
+    "topk_mw_emit": "topk.hip", "keep_all_kernel": "topk.hip",
     "slotmap_kernel": "topk.hip",
     "meank_build_raw": "meank_build.hip", "meank_build_derope": "meank_build.hip",
     "meank_append_kernel": "meank_build.hip",

@@ -81,6 +81,7 @@ class Setup:
         self.ws_rule = torch.empty(kvs.kvs_rule_score_workspace(c["L"], c["H_q"], c["H_kv"], c["N"]),
                                    dtype=torch.uint8, device=dev)
         self.keep_r = torch.empty(c["N"], dtype=torch.uint8, device=dev)
+        self.ws_topk_r = torch.empty(max(1, kvs.kvs_topk_workspace(c["N"])), dtype=torch.uint8, device=dev)
         self.idx_r = torch.empty(c["N"], dtype=torch.int32, device=dev)
         self.nk_r = torch.empty(1, dtype=torch.int64, device=dev)
         self.slots_out = torch.empty_like(self.slots)
@@ -106,6 +107,7 @@ class Setup:
         self.ws_mk = torch.empty(kvs.kvs_meank_score_workspace(m["L"], m["H_q"], m["H_kv"], m["Mq"], self.nB),
                                  dtype=torch.uint8, device=dev)
         self.keep_m = torch.empty(self.nB, dtype=torch.uint8, device=dev)
+        self.ws_topk_m = torch.empty(max(1, kvs.kvs_topk_workspace(self.nB)), dtype=torch.uint8, device=dev)
         self.idx_m = torch.empty(self.nB, dtype=torch.int32, device=dev)
         self.nk_m = torch.empty(1, dtype=torch.int64, device=dev)
         pool = (m["L"], m["H_kv"], 32 * self.n_sel, m["D"])
@@ -124,7 +126,8 @@ class Setup:
             ("kvs_rule_score", lambda: kvs.kvs_rule_score(self.K, self.M, c["pi"], c["q_s"], c["q_e"],
                                                           rule=self.rule, ws=self.ws_rule)),
             ("kvs_topk_select[rule]", lambda: kvs.kvs_topk_select(
-                self.rule, (0, c["pi"]), (c["q_s"], c["q_e"]), c["C"], self.keep_r, self.idx_r, self.nk_r)),
+                self.rule, (0, c["pi"]), (c["q_s"], c["q_e"]), c["C"], self.keep_r, self.idx_r, self.nk_r,
+                ws=self.ws_topk_r)),
             ("kvs_slotmap_redirect", lambda: kvs.kvs_slotmap_redirect(self.slots, self.keep_r, c["dead_slot"],
                                                                       self.slots_out)),
             ("kvs_meank_build", lambda: kvs.kvs_meank_build(self.Kraw, index=self.index)),
@@ -132,7 +135,7 @@ class Setup:
                                                             R=self.R, ws=self.ws_mk)),
             ("kvs_topk_select[meank]", lambda: kvs.kvs_topk_select(
                 self.R, (0, m["n_sink"]), (nB - m["n_recent"], nB), m["budget"], self.keep_m, self.idx_m,
-                self.nk_m)),
+                self.nk_m, ws=self.ws_topk_m)),
             ("kvs_rerope_scatter", lambda: kvs.kvs_rerope_scatter(
                 self.k_src, self.v_src, src, self.page_table, self.n_sel, m["pos_base"], m["theta"],
                 self.k_pool, self.v_pool, self.err)),

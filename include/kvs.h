@@ -142,7 +142,9 @@ kvs_status kvs_window_score(const void* K, const void* Qw, int32_t L, int32_t H_
                             int32_t D, int64_t N, int64_t W, int64_t pi, int64_t q_s, int64_t q_e,
                             float* score, void* ws, size_t ws_bytes, void* stream);
 
-/* Workspace bytes kvs_topk_select needs for n scores. */
+/* Workspace bytes kvs_topk_select uses for n scores: 0 up to 32768 scores;
+ * beyond that a few KB that select the multi-workgroup path (ws may also be
+ * NULL there, for a slower single-workgroup selection that needs none). */
 size_t kvs_topk_workspace(int64_t n);
 
 /*
@@ -159,7 +161,9 @@ size_t kvs_topk_workspace(int64_t n);
  * Order among candidates: larger score first; equal scores -> lower index
  * first (Eq. 1's argmax is not unique under ties); NaN below every number;
  * -0.0 equal to +0.0.  C >= n keeps everything; C < |F| keeps F only.
- * Errors: KVS_ERR_ARG, KVS_ERR_SHAPE (n > 2^31-1), KVS_ERR_WORKSPACE.
+ *   ws        device workspace of kvs_topk_workspace(n) bytes, or NULL (see there).
+ * Errors: KVS_ERR_ARG, KVS_ERR_SHAPE (n > 2^31-1), KVS_ERR_WORKSPACE (ws given
+ * but smaller than kvs_topk_workspace(n)).
  */
 kvs_status kvs_topk_select(const float* score, int64_t n, int64_t f0_begin, int64_t f0_end,
                            int64_t f1_begin, int64_t f1_end, int64_t C, uint8_t* keep_mask,

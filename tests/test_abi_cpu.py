@@ -82,6 +82,12 @@ def test_topk_slot_meank_rerope_rejections(lib):
     assert lib.kvs_topk_select(FAKE, 10, 3, 1, 5, 6, 3, FAKE, FAKE, FAKE, None, 0, None) == 1
     assert lib.kvs_topk_select(FAKE, 10, 0, 1, 5, 6, -1, FAKE, FAKE, FAKE, None, 0, None) == 1
     assert lib.kvs_topk_select(FAKE, 1 << 31, 0, 1, 5, 6, 3, FAKE, FAKE, FAKE, None, 0, None) == 2
+    # up to 32768 scores no workspace; beyond, an optional one (too small is an error)
+    assert lib.kvs_topk_workspace(32768) == 0
+    need = lib.kvs_topk_workspace(92160)
+    assert need >= 4 * (256 + 2 * 45)
+    assert lib.kvs_topk_select(FAKE, 92160, 0, 64, 92096, 92160, 8192, FAKE, FAKE, FAKE, FAKE, need - 1,
+                               None) == 5
     assert lib.kvs_slotmap_redirect(None, FAKE, 10, -1, FAKE, None) == 1
     assert lib.kvs_slotmap_redirect(FAKE, FAKE, -1, -1, FAKE, None) == 1
     assert lib.kvs_meank_build(FAKE, 2, 2, 128, 64, 16, 0, 0, 1e6, None, FAKE, None) == 4

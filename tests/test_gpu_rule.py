@@ -267,8 +267,8 @@ def test_window_score_full_size_sampled():
 
 # ---------------------------------------------------------------- top-k
 
-def check_topk(score, f0, f1, C):
-    keep, idx, nk = kvs.kvs_topk_select(score, f0, f1, C)
+def check_topk(score, f0, f1, C, single_workgroup=False):
+    keep, idx, nk = kvs.kvs_topk_select(score, f0, f1, C, single_workgroup=single_workgroup)
     torch.cuda.synchronize()
     ok, oidx, onk = oracle.topk_select(score.cpu().numpy(), f0, f1, C)
     nk = int(nk.item())
@@ -299,6 +299,20 @@ def check_topk(score, f0, f1, C):
 def test_topk_bit_exact(n, levels, f0, f1, C):
     score = W.scores_with_ties(n, n + 1, levels).to(DEV)
     check_topk(score, f0, f1, C)
+    if n > 32768:   # the no-workspace single-workgroup path as well
+        check_topk(score, f0, f1, C, single_workgroup=True)
+
+
+@pytest.mark.parametrize("n,levels,C,f0,f1", [
+    (65537, None, 1, (0, 0), (0, 0)),                 # one kept, ragged last slice
+    (200000, 9, 150000, (10, 100000), (99990, 100010)),  # heavy ties, overlapping forced ranges
+    (100000, None, 30, (0, 64), (99936, 100000)),     # C < |F| -> forced only
+    (70000, 1, 40000, (0, 5), (69990, 70000)),        # every candidate ties
+])
+def test_topk_multi_workgroup(n, levels, C, f0, f1):
+    score = W.scores_with_ties(n, n + 7, levels).to(DEV)
+    check_topk(score, f0, f1, C)
+    check_topk(score, f0, f1, C, single_workgroup=True)
 
 
 @pytest.mark.parametrize("n,C", [(32768, 8192), (92160, 8192), (8192, 2048)])
@@ -308,6 +322,8 @@ def test_topk_concentrated_scores(n, C):
     x = W.scores_with_ties(n, 4242)
     score = (0.0353 * (1.0 + 0.0026 * x)).float().to(DEV)
     check_topk(score, (0, 64), (n - 64, n), C)
+    if n > 32768:
+        check_topk(score, (0, 64), (n - 64, n), C, single_workgroup=True)
 
 
 def test_topk_special_values():
