@@ -315,6 +315,20 @@ def test_topk_multi_workgroup(n, levels, C, f0, f1):
     check_topk(score, f0, f1, C, single_workgroup=True)
 
 
+def test_topk_multi_workgroup_repeatable():
+    """Slices add their histograms with atomics in whatever order they arrive:
+    the selection must not depend on it (integer sums), call after call."""
+    n = 150000
+    score = W.scores_with_ties(n, 31, 40).to(DEV)
+    first = [t.clone() for t in kvs.kvs_topk_select(score, (0, 10), (n - 10, n), 20000)]
+    for _ in range(5):
+        again = kvs.kvs_topk_select(score, (0, 10), (n - 10, n), 20000)
+        torch.cuda.synchronize()
+        for a, b in zip(first, again):
+            assert torch.equal(a[: int(first[2].item())] if a.dtype == torch.int32 else a,
+                               b[: int(first[2].item())] if b.dtype == torch.int32 else b)
+
+
 @pytest.mark.parametrize("n,C", [(32768, 8192), (92160, 8192), (8192, 2048)])
 def test_topk_concentrated_scores(n, C):
     """Rule-score-like keys: every value within a few 1e-3 of the mean, so the
