@@ -29,6 +29,8 @@
 // XCD and share its L2 copy of the streamed operand.
 // Operand k-slots: lane half h = lane/32 carries k-slots 8h..8h+7 of every
 // k-step; k-step s of half h is dims [64h + 8s, +8) for both operands.
+#include <type_traits>
+
 #include "kvs_internal.h"
 
 using namespace kvs;
@@ -260,18 +262,21 @@ __global__ __launch_bounds__(256, 2) void meank_pass(const uint16_t* __restrict_
   const int nt = (int)((s_end - s_begin + kTile - 1) / kTile);
 
   // Tiles reach LDS two at a time (double buffer); global loads run ahead of
-  // them in a ring of two register stages, so a tile's load is issued two
-  // iterations before its LDS store and an L2 miss has ~two tiles of MFMA
-  // work to hide behind.
+  // them in a ring of PF register stages, so a tile's load is issued PF - 1
+  // iterations before its LDS store.  R_b's pass 1 streams index blocks from
+  // HBM and takes the deeper ring (about 1% faster); pass 2 streams L2-resident
+  // query tiles, and the window score's pass 1 gains nothing from it.
+  constexpr int PF = (PASS1 && !SPAN) ? 4 : 2;
   // streamed rows [s_begin, s_end) and, in pass 2, their lse2 (tile k = rows 32k..)
   const __amdgpu_buffer_rsrc_t srows = buf_rsrc(sbase + (size_t)s_begin * D, (int)((s_end - s_begin) * kRowBytes));
   const __amdgpu_buffer_rsrc_t slse = buf_rsrc(Lg, PASS1 ? 0 : (int)(rows_pad * 4));
-  Stage st[2];
+  Stage st[PF];
   stage_load<!PASS1>(st[0], srows, 0, slse);
   stage_store<!PASS1>(st[0], tiles[0], lses[0]);
   stage_load<!PASS1>(st[0], srows, 1, slse);
   stage_store<!PASS1>(st[0], tiles[1], lses[1]);
-  stage_load<!PASS1>(st[0], srows, 2, slse);
+#pragma unroll
+  for (int k = 2; k <= PF; ++k) stage_load<!PASS1>(st[k % PF], srows, k, slse);
   __syncthreads();
 
   // A wave whose persistent rows all lie past the end (the window score's
@@ -305,12 +310,12 @@ __global__ __launch_bounds__(256, 2) void meank_pass(const uint16_t* __restrict_
   }
 
   // Process tile t (accumulators cc, lse lc) while issuing tile t+1 into cn;
-  // load tile t+3 into stage sl (t odd: st[0], t even: st[1]) and move tile
-  // t+2, loaded one iteration earlier, from stage ss into LDS.
+  // load tile t+1+PF into stage sl = st[(t+1) % PF] and move tile t+2, loaded
+  // PF-1 iterations earlier, from stage ss = st[(t+2) % PF] into LDS.
   auto body = [&](int t, f32x16& cc0, f32x16& cc1, float* lc, f32x16& cn0, f32x16& cn1, float* ln,
-                  Stage& sl, Stage& ss) {
+                  Stage& sl, Stage& ss) __attribute__((always_inline)) {
     const bool pre = t + 2 < nt;
-    stage_load<!PASS1>(sl, srows, t + 3, slse);   // past the end: reads nothing, returns zeros
+    stage_load<!PASS1>(sl, srows, t + 1 + PF, slse);   // past the end: reads nothing, returns zeros
     read_streamed(tiles[(t + 1) & 1], lane, A);
     if (!PASS1) read_lse16(lses[(t + 1) & 1], h, ln);
     float a0 = 0.f, a1 = 0.f;
@@ -336,20 +341,43 @@ __global__ __launch_bounds__(256, 2) void meank_pass(const uint16_t* __restrict_
     __syncthreads();
   };
 
+  // Even t computes into the B accumulators, odd t into A; the loop runs PF
+  // tiles per trip so every stage index is a constant, then the up to PF - 1
+  // tiles left start at a multiple of PF as well.
+  // kc: t % PF as a type, so every stage index is a constant; always inlined,
+  // since a call would move the accumulators and stages to scratch memory
+  auto body_k = [&](int t, auto kc) __attribute__((always_inline)) {
+    constexpr int k = decltype(kc)::value;
+    if constexpr ((k & 1) != 0) body(t, cB0, cB1, lB, cA0, cA1, lA, st[(k + 1) % PF], st[(k + 2) % PF]);
+    else body(t, cA0, cA1, lA, cB0, cB1, lB, st[(k + 1) % PF], st[(k + 2) % PF]);
+  };
+  using K0 = std::integral_constant<int, 0>;
+  using K1 = std::integral_constant<int, 1>;
+  using K2 = std::integral_constant<int, 2>;
+  using K3 = std::integral_constant<int, 3>;
   int t = 0;
-  for (; t + 2 < nt; t += 2) {
-    body(t, cA0, cA1, lA, cB0, cB1, lB, st[1], st[0]);
-    body(t + 1, cB0, cB1, lB, cA0, cA1, lA, st[0], st[1]);
+  for (; t + PF < nt; t += PF) {
+    body_k(t, K0{});
+    body_k(t + 1, K1{});
+    if constexpr (PF == 4) {
+      body_k(t + 2, K2{});
+      body_k(t + 3, K3{});
+    }
   }
-  f32x16* last0 = &cA0;
-  f32x16* last1 = &cA1;
-  float* llast = lA;
   if (t + 1 < nt) {
-    body(t, cA0, cA1, lA, cB0, cB1, lB, st[1], st[0]);
-    last0 = &cB0;
-    last1 = &cB1;
-    llast = lB;
+    body_k(t, K0{});
+    if constexpr (PF == 4) {
+      if (t + 2 < nt) {
+        body_k(t + 1, K1{});
+        if (t + 3 < nt) body_k(t + 2, K2{});
+      }
+    }
   }
+  // the last tile, nt - 1, was computed by body nt - 2 (B if that is even), or by the prologue
+  const bool last_b = nt >= 2 && (nt & 1) == 0;
+  f32x16* last0 = last_b ? &cB0 : &cA0;
+  f32x16* last1 = last_b ? &cB1 : &cA1;
+  float* llast = last_b ? lB : lA;
   // last tile (the only one that can be partial)
   if (PASS1) {
     const int64_t b0 = s_begin + (int64_t)(nt - 1) * kTile;

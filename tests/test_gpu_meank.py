@@ -165,6 +165,10 @@ def check_score(Q, index, n_sink, n_recent, what):
     (2, 4, 4, 64, 96, 0, 0),         # G = 1, no forced blocks
     (1, 8, 2, 1, 40, 1, 1),          # one query token
     (1, 2, 1, 16, 70, 35, 35),       # no candidates
+    (1, 8, 4, 8, 27, 2, 3),          # 22 candidates: a single partial tile
+    (1, 8, 2, 24, 150, 3, 7),        # 140 candidates: five tiles, one past the unrolled trips
+    (1, 16, 4, 40, 262, 5, 1),       # 256 candidates: eight whole tiles
+    (1, 8, 2, 20, 115, 2, 2),        # 111 candidates: four tiles, the last partial
 ])
 def test_meank_score_shapes(L, H_q, H_kv, Mq, nB, sink, recent):
     Q = W.normal((L, H_q, Mq, 128), 31, W.T_Q, "bf16", DEV)
