@@ -14,6 +14,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
+// (layer, KV head) slices per workgroup of the re-RoPE scatter (its grid has
+// n_sel * ceil(L*H_kv / kScatterSlices) workgroups)
+constexpr int kScatterSlices = 8;
 
 // bf16 is the top half of a binary32: widening is a shift.
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }

@@ -5,11 +5,16 @@
 // page_table[r]; V is copied unchanged.
 //
 // HBM-bound (read K and V once, write them once).  A workgroup owns one
-// selected block for every (layer, KV head): it builds the block's 32 x D/2
-// rotation table once in LDS (float64 angles) and streams the L*H_kv 32-row
-// blocks of K and V through it with 16-byte coalesced loads and stores.
-// Out-of-range block ids or pages skip the block and raise err_flag instead of
-// touching memory outside the buffers.
+// selected block for a chunk of 8 (layer, KV head) slices: it builds the
+// block's 32 x D/2 rotation table in LDS (float64 angles) and streams those
+// slices' 32-row blocks of K and V through it with 16-byte coalesced loads and
+// stores, one slice per wave at a time.  The grid runs the chunks of a block
+// fastest.  Many short-lived workgroups at 4 waves per SIMD keep more
+// independent streams in flight than one long-lived workgroup per block
+// (whose register-resident table allowed 2): 7.0 -> 6.65 ms for 2048 blocks
+// over 512 slices, where a plain copy of the same 8 KB pieces takes 6.5 ms.
+// Out-of-range block ids or pages skip the block and raise err_flag instead
+// of touching memory outside the buffers.
 #include "rope_table.h"
 
 using namespace kvs;
@@ -17,46 +22,63 @@ using namespace kvs;
 namespace {
 
 constexpr int kBlk = 32;
+constexpr int kLgChunk = kScatterSlices;   // (layer, KV head) slices per workgroup, two per wave
 
-template <int D>
-__global__ __launch_bounds__(256) void rerope_scatter_kernel(
+template <int D, bool WITH_V>
+__global__ __launch_bounds__(256, 4) void rerope_scatter_kernel(
     const uint16_t* __restrict__ k_src, const uint16_t* __restrict__ v_src, int64_t src_tokens,
     const int32_t* __restrict__ src_block, const int32_t* __restrict__ page_table, int LG,
     int64_t pos_base, double log2_theta, uint16_t* __restrict__ k_pool,
     uint16_t* __restrict__ v_pool, int64_t pool_pages, int32_t* __restrict__ err_flag) {
   constexpr int LPR = D / 8, RPL = 64 / LPR, LOADS = kBlk / RPL;
   __shared__ float2 tab[kBlk][D / 2];
-  const int r = blockIdx.x;
+  // workgroup -> (selected block r, chunk of slices), chunks fastest: the
+  // workgroups in flight cover every slice of a few neighbouring blocks
+  const int nch = (LG + kLgChunk - 1) / kLgChunk;
+  const int r = blockIdx.x / nch, chunk = blockIdx.x % nch;
   const int64_t sb = src_block[r];
   const int64_t dst = page_table ? (int64_t)page_table[r] : (int64_t)r;
   if (sb < 0 || (sb + 1) * kBlk > src_tokens || dst < 0 || dst >= pool_pages) {
     if (threadIdx.x == 0 && err_flag) *err_flag = 1;
     return;
   }
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int cl = lane % LPR, rr = lane / LPR;
   build_rope_table<D>(tab, pos_base + (int64_t)kBlk * r, log2_theta);
   __syncthreads();
+  // one 32 x D block of one slice through buffer resources: a wave-uniform
+  // base, the lane's byte offset, and each load's row group as a scalar offset
+  constexpr int kBlkBytes = kBlk * D * 2, kGroupBytes = RPL * D * 2;
+  const int lane_off = (rr * D + cl * 8) * 2;
   const int64_t pool_tokens = pool_pages * kBlk;
-  for (int lg = wave; lg < LG; lg += 4) {
-    const size_t s0 = ((size_t)lg * src_tokens + (size_t)sb * kBlk) * D + cl * 8;
-    const size_t d0 = ((size_t)lg * pool_tokens + (size_t)dst * kBlk) * D + cl * 8;
+  const int lg_end = min(LG, (chunk + 1) * kLgChunk);
+  for (int lg = chunk * kLgChunk + wave; lg < lg_end; lg += 4) {
+    const size_t s0 = ((size_t)lg * src_tokens + (size_t)sb * kBlk) * D;
+    const size_t d0 = ((size_t)lg * pool_tokens + (size_t)dst * kBlk) * D;
+    const auto ks = buf_rsrc(k_src + s0, kBlkBytes), kd = buf_rsrc(k_pool + d0, kBlkBytes);
+    // the lane's 64 table entries are the same for every slice, but held in
+    // registers across the loop they would cost 128 VGPRs: re-read them from
+    // LDS per slice (a memory clobber keeps the reads inside the loop)
+    asm volatile("" ::: "memory");
     u32x4 w[LOADS], vv[LOADS];
 #pragma unroll
-    for (int ld = 0; ld < LOADS; ++ld) {
-      const size_t off = (size_t)(ld * RPL + rr) * D;
-      w[ld] = *reinterpret_cast<const u32x4*>(k_src + s0 + off);
-      if (v_src) vv[ld] = *reinterpret_cast<const u32x4*>(v_src + s0 + off);
+    for (int ld = 0; ld < LOADS; ++ld) w[ld] = __builtin_amdgcn_raw_buffer_load_b128(ks, lane_off, ld * kGroupBytes, 0);
+    if constexpr (WITH_V) {
+      const auto vs = buf_rsrc(v_src + s0, kBlkBytes);
+#pragma unroll
+      for (int ld = 0; ld < LOADS; ++ld) vv[ld] = __builtin_amdgcn_raw_buffer_load_b128(vs, lane_off, ld * kGroupBytes, 0);
     }
 #pragma unroll
     for (int ld = 0; ld < LOADS; ++ld) {
-      const int t = ld * RPL + rr;
       float x[8];
       unpack8(w[ld], x);
-      rotate8<D>(x, tab[t], cl, +1);
-      const size_t off = (size_t)t * D;
-      *reinterpret_cast<u32x4*>(k_pool + d0 + off) = pack8(x);
-      if (v_src) *reinterpret_cast<u32x4*>(v_pool + d0 + off) = vv[ld];
+      rotate8<D>(x, tab[ld * RPL + rr], cl, +1);
+      __builtin_amdgcn_raw_buffer_store_b128(pack8(x), kd, lane_off, ld * kGroupBytes, 0);
+    }
+    if constexpr (WITH_V) {
+      const auto vd = buf_rsrc(v_pool + d0, kBlkBytes);
+#pragma unroll
+      for (int ld = 0; ld < LOADS; ++ld) __builtin_amdgcn_raw_buffer_store_b128(vv[ld], vd, lane_off, ld * kGroupBytes, 0);
     }
   }
 }
@@ -70,16 +92,21 @@ hipError_t kvs_launch_rerope(const void* k_src, const void* v_src, int64_t src_t
   if (n_sel == 0) return hipSuccess;
   const int LG = L * H_kv;
   const double l2t = __builtin_log2(theta);
-  dim3 grid((unsigned)n_sel), block(256);
+  dim3 grid((unsigned)(n_sel * ceil_div(LG, kLgChunk))), block(256);
   const uint16_t* ks = static_cast<const uint16_t*>(k_src);
   const uint16_t* vs = static_cast<const uint16_t*>(v_src);
   uint16_t* kp = static_cast<uint16_t*>(k_pool);
   uint16_t* vp = static_cast<uint16_t*>(v_pool);
-  if (D == 128)
-    hipLaunchKernelGGL(rerope_scatter_kernel<128>, grid, block, 0, st, ks, vs, src_tokens, src_block,
-                       page_table, LG, pos_base, l2t, kp, vp, pool_pages, err_flag);
-  else
-    hipLaunchKernelGGL(rerope_scatter_kernel<64>, grid, block, 0, st, ks, vs, src_tokens, src_block,
-                       page_table, LG, pos_base, l2t, kp, vp, pool_pages, err_flag);
+#define KVS_SCATTER(DD, WV)                                                                        \
+  hipLaunchKernelGGL((rerope_scatter_kernel<DD, WV>), grid, block, 0, st, ks, vs, src_tokens, src_block, \
+                     page_table, LG, pos_base, l2t, kp, vp, pool_pages, err_flag)
+  if (D == 128) {
+    if (vs) KVS_SCATTER(128, true);
+    else KVS_SCATTER(128, false);
+  } else {
+    if (vs) KVS_SCATTER(64, true);
+    else KVS_SCATTER(64, false);
+  }
+#undef KVS_SCATTER
   return hipGetLastError();
 }
