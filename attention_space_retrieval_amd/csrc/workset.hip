@@ -16,7 +16,7 @@
 //   outgoing  (G_{t-1} only) releases its page.
 // Two kernels: workset_diff (one workgroup: binary searches, block-wide
 // scans, the new page table) and workset_apply (one workgroup per selected
-// block: in-place rotation, scatter, or nothing).
+// block and chunk of slices: in-place rotation, scatter, or nothing).
 #include "rope_table.h"
 
 using namespace kvs;
@@ -142,15 +142,20 @@ __global__ __launch_bounds__(kThreads) void workset_diff(
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void workset_apply(
+// One workgroup per (selected block, chunk of kScatterSlices slices), chunks
+// fastest, two slices per wave at a time -- the layout of the re-RoPE scatter,
+// whose short-lived workgroups at 4 waves per SIMD stream faster than one
+// workgroup per block over every slice.
+template <int D, bool WITH_V>
+__global__ __launch_bounds__(256, 4) void workset_apply(
     const uint16_t* __restrict__ k_src, const uint16_t* __restrict__ v_src, int64_t src_tokens,
     const int32_t* __restrict__ new_blocks, const int32_t* __restrict__ pages,
     const int32_t* __restrict__ old_rank, int LG, int64_t pos_base, double log2_theta,
     uint16_t* __restrict__ k_pool, uint16_t* __restrict__ v_pool, int64_t pool_pages) {
   constexpr int LPR = D / 8, RPL = 64 / LPR, LOADS = kBlk / RPL;
   __shared__ float2 tab[kBlk][D / 2];
-  const int r = blockIdx.x;
+  const int nch = (LG + kScatterSlices - 1) / kScatterSlices;
+  const int r = blockIdx.x / nch, chunk = blockIdx.x % nch;
   const int32_t rank = old_rank[r];
   const int64_t page = pages[r];
   if (page < 0 || page >= pool_pages || rank == r) return;      // rejected input, or retained in place
@@ -159,29 +164,43 @@ __global__ __launch_bounds__(256) void workset_apply(
   // moved: one row of the table, the angle of the position delta; incoming: the block's positions
   build_rope_table<D>(tab, moved ? (int64_t)kBlk * (r - rank) : pos_base + (int64_t)kBlk * r, log2_theta);
   __syncthreads();
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int cl = lane % LPR, rr = lane / LPR;
+  // one 32 x D block of one slice through buffer resources (wave-uniform base,
+  // the lane's byte offset, each load's row group as a scalar offset)
+  constexpr int kBlkBytes = kBlk * D * 2, kGroupBytes = RPL * D * 2;
+  const int lane_off = (rr * D + cl * 8) * 2;
   const int64_t pool_tokens = pool_pages * kBlk;
-  for (int lg = wave; lg < LG; lg += 4) {
-    const size_t d0 = ((size_t)lg * pool_tokens + (size_t)page * kBlk) * D + cl * 8;
-    const size_t s0 = ((size_t)lg * src_tokens + (size_t)sb * kBlk) * D + cl * 8;
-    const uint16_t* kin = moved ? k_pool + d0 : k_src + s0;
+  const int lg_end = min(LG, (chunk + 1) * kScatterSlices);
+  for (int lg = chunk * kScatterSlices + wave; lg < lg_end; lg += 4) {
+    const size_t d0 = ((size_t)lg * pool_tokens + (size_t)page * kBlk) * D;
+    const size_t s0 = ((size_t)lg * src_tokens + (size_t)sb * kBlk) * D;
+    const auto kin = buf_rsrc(moved ? k_pool + d0 : k_src + s0, kBlkBytes);
+    const auto kd = buf_rsrc(k_pool + d0, kBlkBytes);
+    asm volatile("" ::: "memory");   // table reads stay in the loop (held across it they cost 128 VGPRs)
     u32x4 w[LOADS], vv[LOADS];
 #pragma unroll
-    for (int ld = 0; ld < LOADS; ++ld) {
-      const size_t off = (size_t)(ld * RPL + rr) * D;
-      w[ld] = *reinterpret_cast<const u32x4*>(kin + off);
-      if (!moved && v_src) vv[ld] = *reinterpret_cast<const u32x4*>(v_src + s0 + off);
+    for (int ld = 0; ld < LOADS; ++ld) w[ld] = __builtin_amdgcn_raw_buffer_load_b128(kin, lane_off, ld * kGroupBytes, 0);
+    if constexpr (WITH_V) {
+      if (!moved) {
+        const auto vs = buf_rsrc(v_src + s0, kBlkBytes);
+#pragma unroll
+        for (int ld = 0; ld < LOADS; ++ld) vv[ld] = __builtin_amdgcn_raw_buffer_load_b128(vs, lane_off, ld * kGroupBytes, 0);
+      }
     }
 #pragma unroll
     for (int ld = 0; ld < LOADS; ++ld) {
-      const int t = ld * RPL + rr;
       float x[8];
       unpack8(w[ld], x);
-      rotate8<D>(x, tab[moved ? 0 : t], cl, +1);
-      const size_t off = (size_t)t * D;
-      *reinterpret_cast<u32x4*>(k_pool + d0 + off) = pack8(x);
-      if (!moved && v_src) *reinterpret_cast<u32x4*>(v_pool + d0 + off) = vv[ld];
+      rotate8<D>(x, tab[moved ? 0 : ld * RPL + rr], cl, +1);
+      __builtin_amdgcn_raw_buffer_store_b128(pack8(x), kd, lane_off, ld * kGroupBytes, 0);
+    }
+    if constexpr (WITH_V) {
+      if (!moved) {
+        const auto vd = buf_rsrc(v_pool + d0, kBlkBytes);
+#pragma unroll
+        for (int ld = 0; ld < LOADS; ++ld) __builtin_amdgcn_raw_buffer_store_b128(vv[ld], vd, lane_off, ld * kGroupBytes, 0);
+      }
     }
   }
 }
@@ -210,11 +229,17 @@ hipError_t kvs_launch_workset(const void* k_src, const void* v_src, int64_t src_
   const uint16_t* vs = static_cast<const uint16_t*>(v_src);
   uint16_t* kp = static_cast<uint16_t*>(k_pool);
   uint16_t* vp = static_cast<uint16_t*>(v_pool);
-  if (D == 128)
-    hipLaunchKernelGGL(workset_apply<128>, dim3((unsigned)n_new), dim3(256), 0, st, ks, vs, src_tokens,
-                       new_blocks, pages_out, old_rank_out, LG, pos_base, l2t, kp, vp, pool_pages);
-  else
-    hipLaunchKernelGGL(workset_apply<64>, dim3((unsigned)n_new), dim3(256), 0, st, ks, vs, src_tokens,
-                       new_blocks, pages_out, old_rank_out, LG, pos_base, l2t, kp, vp, pool_pages);
+  const dim3 grid((unsigned)(n_new * ceil_div(LG, kScatterSlices))), block(256);
+#define KVS_APPLY(DD, WV)                                                                          \
+  hipLaunchKernelGGL((workset_apply<DD, WV>), grid, block, 0, st, ks, vs, src_tokens, new_blocks, \
+                     pages_out, old_rank_out, LG, pos_base, l2t, kp, vp, pool_pages)
+  if (D == 128) {
+    if (vs) KVS_APPLY(128, true);
+    else KVS_APPLY(128, false);
+  } else {
+    if (vs) KVS_APPLY(64, true);
+    else KVS_APPLY(64, false);
+  }
+#undef KVS_APPLY
   return hipGetLastError();
 }

@@ -305,8 +305,8 @@ size_t kvs_working_set_workspace(int64_t pool_pages);
  *                  written.  May be NULL.
  *   ws             device workspace of >= kvs_working_set_workspace() bytes.
  * Errors: KVS_ERR_ARG, KVS_ERR_SHAPE (n_new or n_prev > pool_pages, src_tokens
- * not a multiple of 32, overflow), KVS_ERR_UNSUPPORTED (block != 32, D not
- * 64/128), KVS_ERR_WORKSPACE.
+ * not a multiple of 32, n_new * ceil(L*H_kv / 8) >= 2^24, overflow),
+ * KVS_ERR_UNSUPPORTED (block != 32, D not 64/128), KVS_ERR_WORKSPACE.
  */
 kvs_status kvs_working_set_update(const void* k_src, const void* v_src, int64_t src_tokens,
                                   const int32_t* prev_blocks, const int32_t* prev_pages,

@@ -282,10 +282,13 @@ def test_meank_1m_step_full_size():
 
 # ---------------------------------------------------------------- re-RoPE scatter
 
-@pytest.mark.parametrize("D,pos_base,with_v,identity", [(128, 0, True, False), (128, 1000000, True, True),
-                                                        (64, 77, False, False)])
-def test_rerope_scatter(D, pos_base, with_v, identity):
-    L, H_kv, n_src_blocks, pool_pages, n_sel, theta = 2, 3, 20, 12, 7, 1e6
+@pytest.mark.parametrize("D,pos_base,with_v,identity,L,H_kv", [
+    (128, 0, True, False, 2, 3), (128, 1000000, True, True, 2, 3), (64, 77, False, False, 2, 3),
+    (128, 4321, True, False, 4, 5),     # 20 (layer, KV head) slices: chunks of 8, 8 and 4
+    (64, 0, True, True, 2, 8),          # 16 slices: two whole chunks
+])
+def test_rerope_scatter(D, pos_base, with_v, identity, L, H_kv):
+    n_src_blocks, pool_pages, n_sel, theta = 20, 12, 7, 1e6
     k_src = W.normal((L, H_kv, 32 * n_src_blocks, D), 41, W.T_K, "bf16", DEV)
     v_src = W.normal((L, H_kv, 32 * n_src_blocks, D), 41, W.T_V, "bf16", DEV) if with_v else None
     src_block = torch.tensor([0, 3, 4, 9, 10, 17, 19], dtype=torch.int32, device=DEV)
@@ -418,12 +421,13 @@ def _workset_case(L, H_kv, D, src_blocks, pool_pages, prev, prev_pages, new, pos
     return pages_o, rank_o
 
 
-def test_working_set_mixed_classes():
+@pytest.mark.parametrize("L,H_kv", [(2, 3), (3, 6)])       # 6 slices, and 18 (chunks of 8, 8 and 2)
+def test_working_set_mixed_classes(L, H_kv):
     r = np.random.default_rng(60)
     prev = sorted(r.choice(64, 20, replace=False).tolist())
     prev_pages = r.permutation(40)[:20].tolist()
     new = sorted(set(prev[::2]) | set(r.choice(64, 15, replace=False).tolist()))[:30]
-    pages, rank = _workset_case(2, 3, 128, 64, 40, prev, prev_pages, new, 96, True, 61)
+    pages, rank = _workset_case(L, H_kv, 128, 64, 40, prev, prev_pages, new, 96, True, 61)
     assert (rank >= 0).any() and (rank < 0).any() and any(rr not in (-1, i) for i, rr in enumerate(rank))
 
 
