@@ -50,13 +50,6 @@ constexpr float kRebase = 0x1p60f;        // pass 1 rebases its reference past t
 // 8*(v/4) + 4*(l/32) + (v%4) for v = 0..15.
 __device__ __forceinline__ int c_row(int v, int h) { return 8 * (v >> 2) + 4 * h + (v & 3); }
 
-// Persistent operand straight from global memory: row `row` (zero if !ok).
-__device__ __forceinline__ void load_persistent(const uint16_t* base, int64_t row, bool ok, int h, bf16x8* op) {
-  const u32x4* p = reinterpret_cast<const u32x4*>(base + (size_t)(ok ? row : 0) * D + 64 * h);
-#pragma unroll
-  for (int s = 0; s < KS; ++s) op[s] = __builtin_bit_cast(bf16x8, ok ? p[s] : u32x4{0u, 0u, 0u, 0u});
-}
-
 struct Stage {
   u32x4 w[2];
   float4 lse;
@@ -222,8 +215,10 @@ __global__ __launch_bounds__(256, 2) void meank_pass(const uint16_t* __restrict_
                                                      float* __restrict__ lse2,
                                                      float2* __restrict__ part1,
                                                      float* __restrict__ colpart) {
-  __shared__ __attribute__((aligned(16))) char tiles[2][kTile * kLdsRow];
+  // one LDS area: first the workgroup's 256 persistent rows, then the two streamed tiles
+  __shared__ __attribute__((aligned(16))) char smem[kPerWG * kLdsRow];
   __shared__ __attribute__((aligned(16))) float lses[2][kTile];
+  char(*tiles)[kTile * kLdsRow] = reinterpret_cast<char(*)[kTile * kLdsRow]>(smem);
   int lg, tile;
   xcd_map(T, LG, lg, tile);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -232,15 +227,38 @@ __global__ __launch_bounds__(256, 2) void meank_pass(const uint16_t* __restrict_
   const uint16_t* Ig = index + (size_t)lg * nB * D;
   const float* Lg = lse2 + (size_t)lg * rows_pad;
 
-  // persistent operand: pass 1 = query rows, pass 2 = index rows (block columns)
+  // persistent operand: pass 1 = query rows, pass 2 = index rows (block columns).
+  // The workgroup's 256 rows are read whole and coalesced (16 loads of 16 bytes
+  // per thread; rows past the end read as zero), staged in LDS, and each wave
+  // takes its 64 rows in the operand layout from there.  Loaded straight in
+  // that layout, every load instruction would touch 64 rows 16 bytes at a
+  // time, which starves the passes that stream few tiles per workgroup.
   const int64_t p0 = (int64_t)tile * kPerWG + wave * kPerWave;
   bf16x8 B0[KS], B1[KS];
-  if (PASS1) {
-    load_persistent(Qg, p0 + n, p0 + n < rows, h, B0);
-    load_persistent(Qg, p0 + 32 + n, p0 + 32 + n < rows, h, B1);
-  } else {
-    load_persistent(Ig, c0 + p0 + n, c0 + p0 + n < c1, h, B0);
-    load_persistent(Ig, c0 + p0 + 32 + n, c0 + p0 + 32 + n < c1, h, B1);
+  {
+    const int64_t pbase = (PASS1 ? 0 : c0) + (int64_t)tile * kPerWG;
+    const int64_t plim = PASS1 ? rows : c1;
+    const int pcount = (int)(plim <= pbase ? 0 : (plim - pbase > kPerWG ? kPerWG : plim - pbase));
+    const uint16_t* pg = (PASS1 ? Qg : Ig) + (pcount > 0 ? (size_t)pbase * D : 0);
+    const __amdgpu_buffer_rsrc_t prs = buf_rsrc(pg, pcount * kRowBytes);
+    constexpr int kLoads = kPerWG * kRowBytes / 16 / 256;
+    u32x4 v[kLoads];
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i)
+      v[i] = __builtin_amdgcn_raw_buffer_load_b128(prs, (threadIdx.x + 256 * i) * 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int idx = threadIdx.x + 256 * i;
+      *reinterpret_cast<u32x4*>(smem + (idx >> 4) * kLdsRow + (idx & 15) * 16) = v[i];
+    }
+    __syncthreads();
+    const char* r0 = smem + (wave * kPerWave + n) * kLdsRow + h * 128;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      B0[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(r0 + 16 * k));
+      B1[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(r0 + 32 * kLdsRow + 16 * k));
+    }
+    __syncthreads();
   }
   // streamed operand: pass 1 = index tiles over this split of [c0, c1), pass 2 = query tiles over [0, rows)
   const uint16_t* sbase = PASS1 ? Ig : Qg;
