@@ -95,6 +95,10 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def _stream(t):
     return torch.cuda.current_stream(t.device).cuda_stream
 
@@ -146,7 +150,7 @@ def kvs_rule_score(K, M, pi, q_s, q_e, rule=None, ws=None):
     ws = _workspace(need, K.device, ws)
     _check("kvs_rule_score", load().kvs_rule_score(
         _ptr(K), _dtype_code(K), _ptr(M), L, H_q, H_kv, D, N, pi, q_s, q_e, _ptr(rule),
-        _ptr(ws), ws.numel(), _stream(K)))
+        _ptr(ws), _nbytes(ws), _stream(K)))
     return rule
 
 
@@ -167,7 +171,7 @@ def kvs_rule_score_paged(K_pool, slots, M, pi, q_s, q_e, rule=None, ws=None):
                          device=K_pool.device)
     _check("kvs_rule_score_paged", load().kvs_rule_score_paged(
         _ptr(K_pool), _dtype_code(K_pool), _ptr(slots), pool_size, _ptr(M), L, H_q, H_kv, D, N, int(pi),
-        int(q_s), int(q_e), _ptr(rule), _ptr(ws), ws.numel(), _stream(K_pool)))
+        int(q_s), int(q_e), _ptr(rule), _ptr(ws), _nbytes(ws), _stream(K_pool)))
     return rule
 
 
@@ -191,7 +195,7 @@ def kvs_window_score(K, Qw, pi, q_s, q_e, score=None, ws=None):
                          device=K.device)
     _check("kvs_window_score", load().kvs_window_score(
         _ptr(K), _ptr(Qw), L, H_q, H_kv, D, N, W, int(pi), int(q_s), int(q_e), _ptr(score), _ptr(ws),
-        ws.numel(), _stream(K)))
+        _nbytes(ws), _stream(K)))
     return score
 
 
@@ -223,7 +227,7 @@ def kvs_topk_select(score, f0, f1, C, keep_mask=None, keep_idx=None, n_kept=None
         ws = _workspace(need, dev, ws)
     _check("kvs_topk_select", load().kvs_topk_select(
         _ptr(score), n, f0[0], f0[1], f1[0], f1[1], C, _ptr(keep_mask), _ptr(keep_idx),
-        _ptr(n_kept), _ptr(ws), 0 if ws is None else ws.numel(), _stream(score)))
+        _ptr(n_kept), _ptr(ws), _nbytes(ws), _stream(score)))
     return keep_mask, keep_idx, n_kept
 
 
@@ -295,7 +299,7 @@ def kvs_meank_score(Q, index, n_sink, n_recent, R=None, ws=None):
     ws = _workspace(need, Q.device, ws)
     _check("kvs_meank_score", load().kvs_meank_score(
         _ptr(Q), _ptr(index), L, H_q, H_kv, D, Mq, nB, n_sink, n_recent, _ptr(R), _ptr(ws),
-        ws.numel(), _stream(Q)))
+        _nbytes(ws), _stream(Q)))
     return R
 
 
@@ -366,5 +370,5 @@ def kvs_working_set_update(k_src, v_src, prev_blocks, prev_pages, new_blocks, po
         _ptr(k_src), _ptr(v_src), src_tokens, _ptr(prev_blocks), _ptr(prev_pages), n_prev,
         _ptr(new_blocks), n_new, L, H_kv, D, block, int(pos_base), float(theta), _ptr(k_pool),
         _ptr(v_pool), pool_pages, _ptr(pages), _ptr(old_rank), _ptr(outgoing), _ptr(counts),
-        _ptr(err_flag), _ptr(ws), ws.numel(), _stream(k_src)))
+        _ptr(err_flag), _ptr(ws), _nbytes(ws), _stream(k_src)))
     return pages, old_rank, outgoing[:n_prev], counts
