@@ -54,9 +54,11 @@ inline unsigned ceil_div(int64_t a, int64_t b) { return (unsigned)((a + b - 1) /
 // Buffer accesses through a resource over [base, base + bytes): a scalar base
 // and a 32-bit per-lane offset, bounds-checked by the hardware (writes past
 // `bytes` are dropped).  `base` must be wave-uniform.  aux is the cache
-// policy operand: 0 = default, kBufSc1 = write through to memory.
+// policy operand: 0 = default, kBufSc1 = write through to memory, kBufNt =
+// non-temporal.
 constexpr int kBufWord3 = 0x00020000;   // resource word 3 for raw (untyped) access on gfx9
 constexpr int kBufSc1 = 16;
+constexpr int kBufNt = 2;              // non-temporal: data read or written once
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufWord3);

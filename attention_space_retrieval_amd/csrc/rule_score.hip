@@ -35,6 +35,16 @@ __device__ __forceinline__ void online_add(float& m, float& s, float x) {
   m = mn;
 }
 
+// online_add that leaves (m, s) unchanged for x = -inf, by selects rather
+// than a branch (with m = -inf too, the update would read -inf - -inf).
+__device__ __forceinline__ void online_add_live(float& m, float& s, float x) {
+  const float mn = fmaxf(m, x);
+  const float sn = s * __builtin_amdgcn_exp2f(m - mn) + __builtin_amdgcn_exp2f(x - mn);
+  const bool live = x != -INFINITY;
+  s = live ? sn : s;
+  m = live ? mn : m;
+}
+
 // One lane's 8 A-operand values for k-step s: M[head] * log2(e)/sqrt(D) at
 // dims d0..d0+7, high bf16 part (hi) or the bf16 rounding of the remainder,
 // packed two per register so the operand stays in 4 registers.
@@ -84,7 +94,7 @@ __global__ __launch_bounds__(256) void rule_logits_mfma(
   const int chunk = blockIdx.x;
   const int lg = blockIdx.y;
   const int l = lg / H_kv, g = lg - l * H_kv;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
 
   // A operand: row r of the 16x32 tile is head slot r&7 of group hg, high part
@@ -131,12 +141,22 @@ __global__ __launch_bounds__(256) void rule_logits_mfma(
   constexpr int NLD = 16 / RPI;                     // load instructions per 16-row tile
   char* slot = stage[wave];
   const int lr = lane / (D / 8), lc = lane % (D / 8);
+  // Dense keys go through a buffer resource over the chunk's rows, so a row
+  // past the chunk reads as zero with no branch: the loads of the next tile
+  // then stay in flight while this one is transposed and its logits are
+  // written (branchy loads made the compiler wait for every outstanding
+  // memory operation, the spill stores included, before each tile).
+  const __amdgpu_buffer_rsrc_t krs = buf_rsrc(PAGED ? K : Kb + (size_t)row0 * D, PAGED ? 0 : (int)((row1 - row0) * D * 2));
   auto load_tile = [&](int64_t t0, u32x4* w) {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int64_t j = t0 + i * RPI + lr;
-      const uint16_t* p = j < row1 ? row_ptr(j) : nullptr;
-      w[i] = p ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + lc) : u32x4{0u, 0u, 0u, 0u};
+      if constexpr (PAGED) {
+        const uint16_t* p = j < row1 ? row_ptr(j) : nullptr;
+        w[i] = p ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + lc) : u32x4{0u, 0u, 0u, 0u};
+      } else {
+        w[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, (int)(j - row0) * (D * 2) + lc * 16, 0, kBufNt);
+      }
     }
   };
   auto to_operand = [&](const u32x4* w, bf16x8* B) {
@@ -149,12 +169,11 @@ __global__ __launch_bounds__(256) void rule_logits_mfma(
 
   u32x4 W[NLD], Wn[NLD];
   bf16x8 B[KS];
-  int64_t t0 = row0 + wave * 16;
-  if (t0 < row1) load_tile(t0, W);
-  for (; t0 < row1; t0 += 64) {
-    const int64_t tn = t0 + 64;
-    if (tn < row1) load_tile(tn, Wn);
-    to_operand(W, B);
+  // One 16-row tile: issue the loads of the wave's next tile into nxt, move
+  // cur into the operand, and write and fold its logits.
+  auto step = [&](int64_t t0, u32x4* cur, u32x4* nxt) {
+    if (PAGED ? t0 + 64 < row1 : true) load_tile(t0 + 64, nxt);   // dense: past the chunk the loads return zeros
+    to_operand(cur, B);
     const int64_t j = t0 + r;
     const bool vj = j < row1;
     const bool forced = is_forced(j, pi, q_s, q_e) || (PAGED && vj && sslot[j - row0] < 0);
@@ -165,17 +184,44 @@ __global__ __launch_bounds__(256) void rule_logits_mfma(
       for (int s = 0; s < KS; ++s) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[hg][s], B[s], c, 0, 0, 0);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        // C row 4*(lane>>4)+v: lanes 0..31 hold the high rows, lanes 32..63 the low rows.
+        // C row 4*(lane>>4)+v: lanes 0..31 hold the high rows, lanes 32..63 the low rows,
+        // so lanes 0..15 hold head hg*8+v and lanes 16..31 head hg*8+4+v.
         const float t = c[v] + __shfl_xor(c[v], 32, kWave);
         const int hl = hg * 8 + 4 * (q & 1) + v;
-        if (lane < 32 && vj && hl < G) {
-          spill[(head0 + hl) * (size_t)N + j] = forced ? -INFINITY : t;
-          if (!forced) online_add(mx[hg][v], sm[hg][v], t);
+        const bool act = lane < 32 && vj && hl < G;
+        // Branch-free: each head's spill row is a buffer resource (a head past G
+        // gets an empty one) and an inactive lane's offset lies out of range, so
+        // its store is dropped; a -inf logit leaves the online state as it is.
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int hh = hg * 8 + 4 * half + v;
+          const __amdgpu_buffer_rsrc_t srs =
+              buf_rsrc(spill + (head0 + (hh < G ? hh : 0)) * (size_t)N + row0, hh < G ? (int)((row1 - row0) * 4) : 0);
+          const bool mine = act && (q & 1) == half;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(forced ? -INFINITY : t), srs,
+                                                mine ? (int)(j - row0) * 4 : 0x7ffffff0, 0, 0);
         }
+        online_add_live(mx[hg][v], sm[hg][v], act && !forced ? t : -INFINITY);
       }
     }
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) W[i] = Wn[i];
+  };
+  // Tiles alternate between the W and Wn registers (no copies).  The first
+  // pair runs before the loop, so every path into the loop head carries the
+  // same outstanding memory operations (one tile's loads, then the previous
+  // tile's spill stores): the compiler then waits only for the loads a tile
+  // needs, not for the stores issued after them.
+  int64_t t0 = row0 + wave * 16;
+  if (PAGED ? t0 < row1 : true) load_tile(t0, W);
+  if (t0 < row1) {
+    step(t0, W, Wn);
+    if (t0 + 64 < row1) {
+      step(t0 + 64, Wn, W);
+      for (t0 += 128; t0 < row1; t0 += 128) {
+        step(t0, W, Wn);
+        if (t0 + 64 >= row1) break;
+        step(t0 + 64, Wn, W);
+      }
+    }
   }
 
   // Reduce over the 16 lanes that hold the same head, then over the 4 waves.
