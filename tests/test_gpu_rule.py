@@ -94,6 +94,8 @@ def test_rule_tiny_config():
     (1, 24, 2, 128, 2100, 10, 20, 30),         # G = 12: two 8-head groups
     (2, 16, 4, 64, 3000, 5, 2990, 3000),       # D = 64
     (1, 4, 2, 128, 1, 0, 0, 0),                # N = 1
+    (1, 16, 2, 128, 777, 3, 700, 720),         # G = 8: both spill halves of one 8-head group
+    (1, 32, 2, 64, 90, 0, 80, 90),             # G = 16, D = 64, fewer rows than one tile pair per wave
 ])
 def test_rule_bf16_shapes(L, H_q, H_kv, D, N, pi, q_s, q_e):
     K = W.normal((L, H_kv, N, D), 11, W.T_K, "bf16", DEV)
