@@ -1,4 +1,4 @@
-"""The hot path inside a HIP graph.
+"""The hot path inside a HIP graph, and on concurrent streams.
 
 A rule turn (QueryMemory update, rule score, top-k, slot redirect) and a Mean-K
 step (index build, block relevance, top-k, re-RoPE scatter) are captured once
@@ -75,11 +75,17 @@ class Turn:
         self.err.zero_()
 
     def calls(self):
+        self.rule_calls()
+        self.meank_calls()
+
+    def rule_calls(self):
         kvs.kvs_qmem_update(self.span, self.lam, self.M, False)
         kvs.kvs_rule_score(self.K, self.M, self.pi, self.q_s, self.q_e, rule=self.rule, ws=self.ws_rule)
         kvs.kvs_topk_select(self.rule, (0, self.pi), (self.q_s, self.q_e), self.C, self.keep, self.idx, self.nk,
                             ws=self.ws_topk)
         kvs.kvs_slotmap_redirect(self.slots, self.keep, -1, self.slots_out)
+
+    def meank_calls(self):
         kvs.kvs_meank_build(self.Kraw, index=self.index)
         kvs.kvs_meank_score(self.Q, self.index, self.sink, self.recent, R=self.R, ws=self.ws_mk)
         kvs.kvs_topk_select(self.R, (0, self.sink), (self.nB - self.recent, self.nB), self.budget, self.keep_m,
@@ -122,3 +128,27 @@ def test_rule_turn_and_meank_step_replay_in_a_graph():
         assert int(want["err"].item()) == 0
         for name in want:
             assert torch.equal(got[name], want[name]), f"replay {rep}: {name} differs from the eager calls"
+
+
+def test_rule_turn_and_meank_step_on_concurrent_streams():
+    """The two modes on two streams at once give what they give one after the other."""
+    t = Turn()
+    t.fill(200)
+    torch.cuda.synchronize()
+    t.calls()
+    torch.cuda.synchronize()
+    want = t.outputs()
+    t.fill(200)
+    a, b = torch.cuda.Stream(), torch.cuda.Stream()
+    a.wait_stream(torch.cuda.current_stream())
+    b.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(a):
+        t.rule_calls()
+    with torch.cuda.stream(b):
+        t.meank_calls()
+    torch.cuda.current_stream().wait_stream(a)
+    torch.cuda.current_stream().wait_stream(b)
+    torch.cuda.synchronize()
+    got = t.outputs()
+    for name in want:
+        assert torch.equal(got[name], want[name]), f"{name} differs between concurrent and sequential calls"
