@@ -227,7 +227,8 @@ kvs_status kvs_rerope_scatter(const void* k_src, const void* v_src, int64_t src_
   if (block != 32 || !head_dim_ok(D)) return KVS_ERR_UNSUPPORTED;
   if (src_tokens % block != 0 || numel4(L, H_kv, src_tokens, D) < 0 ||
       numel4(L, H_kv, pool_pages, (int64_t)block * D) < 0 ||
-      !grid_ok(n_sel) || !grid_ok(n_sel * cdiv((int64_t)L * H_kv, kvs::kScatterSlices)))
+      !grid_ok(2 * n_sel) || !grid_ok(n_sel * cdiv((int64_t)L * H_kv, kvs::kScatterSlices)) ||
+      (int64_t)L * H_kv > 65535)
     return KVS_ERR_SHAPE;
   return hip_status(kvs_launch_rerope(k_src, v_src, src_tokens, src_block, page_table, n_sel, L,
                                       H_kv, D, pos_base, theta, k_pool, v_pool, pool_pages,

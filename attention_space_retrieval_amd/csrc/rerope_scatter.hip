@@ -24,12 +24,11 @@ namespace {
 constexpr int kBlk = 32;
 constexpr int kLgChunk = kScatterSlices;   // (layer, KV head) slices per workgroup, two per wave
 
-template <int D, bool WITH_V>
+template <int D>
 __global__ __launch_bounds__(256, 4) void rerope_scatter_kernel(
-    const uint16_t* __restrict__ k_src, const uint16_t* __restrict__ v_src, int64_t src_tokens,
-    const int32_t* __restrict__ src_block, const int32_t* __restrict__ page_table, int LG,
-    int64_t pos_base, double log2_theta, uint16_t* __restrict__ k_pool,
-    uint16_t* __restrict__ v_pool, int64_t pool_pages, int32_t* __restrict__ err_flag) {
+    const uint16_t* __restrict__ k_src, int64_t src_tokens, const int32_t* __restrict__ src_block,
+    const int32_t* __restrict__ page_table, int LG, int64_t pos_base, double log2_theta,
+    uint16_t* __restrict__ k_pool, int64_t pool_pages, int32_t* __restrict__ err_flag) {
   constexpr int LPR = D / 8, RPL = 64 / LPR, LOADS = kBlk / RPL;
   __shared__ float2 tab[kBlk][D / 2];
   // workgroup -> (selected block r, chunk of slices), chunks fastest: the
@@ -60,14 +59,9 @@ __global__ __launch_bounds__(256, 4) void rerope_scatter_kernel(
     // registers across the loop they would cost 128 VGPRs: re-read them from
     // LDS per slice (a memory clobber keeps the reads inside the loop)
     asm volatile("" ::: "memory");
-    u32x4 w[LOADS], vv[LOADS];
+    u32x4 w[LOADS];
 #pragma unroll
     for (int ld = 0; ld < LOADS; ++ld) w[ld] = __builtin_amdgcn_raw_buffer_load_b128(ks, lane_off, ld * kGroupBytes, 0);
-    if constexpr (WITH_V) {
-      const auto vs = buf_rsrc(v_src + s0, kBlkBytes);
-#pragma unroll
-      for (int ld = 0; ld < LOADS; ++ld) vv[ld] = __builtin_amdgcn_raw_buffer_load_b128(vs, lane_off, ld * kGroupBytes, 0);
-    }
 #pragma unroll
     for (int ld = 0; ld < LOADS; ++ld) {
       float x[8];
@@ -75,12 +69,31 @@ __global__ __launch_bounds__(256, 4) void rerope_scatter_kernel(
       rotate8<D>(x, tab[ld * RPL + rr], cl, +1);
       __builtin_amdgcn_raw_buffer_store_b128(pack8(x), kd, lane_off, ld * kGroupBytes, 0);
     }
-    if constexpr (WITH_V) {
-      const auto vd = buf_rsrc(v_pool + d0, kBlkBytes);
-#pragma unroll
-      for (int ld = 0; ld < LOADS; ++ld) __builtin_amdgcn_raw_buffer_store_b128(vv[ld], vd, lane_off, ld * kGroupBytes, 0);
-    }
   }
+}
+
+// V carries no position: a plain copy, one 16-byte load and one store per
+// thread, 4 KB per workgroup (half a block at D = 128, a whole one at D = 64).
+// The grid runs the pieces of one block fastest, then the blocks (x), then
+// the slices (y).  Short workgroups that load once and store once move these
+// scattered pieces faster than workgroups that loop over slices, whose every
+// later load also waits for the earlier stores (one counter tracks both).
+template <int D>
+__global__ __launch_bounds__(256) void v_scatter_kernel(const uint16_t* __restrict__ v_src, int64_t src_tokens,
+                                                        const int32_t* __restrict__ src_block,
+                                                        const int32_t* __restrict__ page_table,
+                                                        uint16_t* __restrict__ v_pool, int64_t pool_pages) {
+  constexpr int kPieceBytes = 256 * 16, kPieces = kBlk * D * 2 / kPieceBytes;
+  const int piece = (int)(blockIdx.x % kPieces);
+  const int64_t r = blockIdx.x / kPieces, lg = blockIdx.y;
+  const int64_t sb = src_block[r];
+  const int64_t dst = page_table ? (int64_t)page_table[r] : r;
+  if (sb < 0 || (sb + 1) * kBlk > src_tokens || dst < 0 || dst >= pool_pages) return;   // K's kernel flags it
+  const size_t s0 = ((size_t)lg * src_tokens + (size_t)sb * kBlk) * D;
+  const size_t d0 = ((size_t)lg * pool_pages * kBlk + (size_t)dst * kBlk) * D;
+  const auto vs = buf_rsrc(v_src + s0, kBlk * D * 2), vd = buf_rsrc(v_pool + d0, kBlk * D * 2);
+  const int off = piece * kPieceBytes + threadIdx.x * 16;
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_amdgcn_raw_buffer_load_b128(vs, off, 0, 0), vd, off, 0, 0);
 }
 
 }  // namespace
@@ -97,16 +110,20 @@ hipError_t kvs_launch_rerope(const void* k_src, const void* v_src, int64_t src_t
   const uint16_t* vs = static_cast<const uint16_t*>(v_src);
   uint16_t* kp = static_cast<uint16_t*>(k_pool);
   uint16_t* vp = static_cast<uint16_t*>(v_pool);
-#define KVS_SCATTER(DD, WV)                                                                        \
-  hipLaunchKernelGGL((rerope_scatter_kernel<DD, WV>), grid, block, 0, st, ks, vs, src_tokens, src_block, \
-                     page_table, LG, pos_base, l2t, kp, vp, pool_pages, err_flag)
-  if (D == 128) {
-    if (vs) KVS_SCATTER(128, true);
-    else KVS_SCATTER(128, false);
-  } else {
-    if (vs) KVS_SCATTER(64, true);
-    else KVS_SCATTER(64, false);
-  }
-#undef KVS_SCATTER
+  if (D == 128)
+    hipLaunchKernelGGL(rerope_scatter_kernel<128>, grid, block, 0, st, ks, src_tokens, src_block, page_table, LG,
+                       pos_base, l2t, kp, pool_pages, err_flag);
+  else
+    hipLaunchKernelGGL(rerope_scatter_kernel<64>, grid, block, 0, st, ks, src_tokens, src_block, page_table, LG,
+                       pos_base, l2t, kp, pool_pages, err_flag);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !vs) return e;
+  const dim3 vgrid((unsigned)(n_sel * (kBlk * D * 2 / 4096)), (unsigned)LG);
+  if (D == 128)
+    hipLaunchKernelGGL(v_scatter_kernel<128>, vgrid, block, 0, st, vs, src_tokens, src_block, page_table, vp,
+                       pool_pages);
+  else
+    hipLaunchKernelGGL(v_scatter_kernel<64>, vgrid, block, 0, st, vs, src_tokens, src_block, page_table, vp,
+                       pool_pages);
   return hipGetLastError();
 }

@@ -38,7 +38,7 @@ KERNEL_SOURCES = {
     "meank_build_raw": "meank_build.hip", "meank_build_derope": "meank_build.hip",
     "meank_append_kernel": "meank_build.hip",
     "meank_pass": "meank_score.hip", "meank_reduce": "meank_score.hip", "meank_lse_merge": "meank_score.hip",
-    "rerope_scatter_kernel": "rerope_scatter.hip",
+    "rerope_scatter_kernel": "rerope_scatter.hip", "v_scatter_kernel": "rerope_scatter.hip",
     "workset_diff": "workset.hip", "workset_apply": "workset.hip",
 }
 

@@ -49,7 +49,7 @@ CALL_KERNELS = {
     "kvs_slotmap_redirect": ["slotmap_kernel"],
     "kvs_meank_build": ["meank_build_raw<128>"],
     "kvs_meank_score": ["meank_pass<true, false>", "meank_pass<false, false>", "meank_reduce<false>"],
-    "kvs_rerope_scatter": ["rerope_scatter_kernel<128, true>"],
+    "kvs_rerope_scatter": ["rerope_scatter_kernel<128>", "v_scatter_kernel<128>"],
     # rows beyond the step (timed after it): the paged rule score's merge and column sum are the
     # dense call's kernels on the same sizes
     "kvs_rule_score_paged": ["rule_logits_mfma<128, 1, true>", "rule_lse_merge", "rule_colsum"],

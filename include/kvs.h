@@ -261,8 +261,9 @@ kvs_status kvs_meank_score(const void* Q, const void* index, int32_t L, int32_t 
  *                named keep their contents.  v_src/v_pool may both be NULL.
  *   err_flag     nullable device int32: set to 1 if a src_block or
  *                page_table entry is out of range (that block is skipped).
- * Errors: KVS_ERR_ARG, KVS_ERR_SHAPE (also n_sel * ceil(L*H_kv / 8) >= 2^24, the
- * launch's workgroup count), KVS_ERR_UNSUPPORTED (block != 32, D not 64/128).
+ * Errors: KVS_ERR_ARG, KVS_ERR_SHAPE (also n_sel >= 2^23, n_sel * ceil(L*H_kv / 8)
+ * >= 2^24 or L*H_kv > 65535: the launches' grid limits), KVS_ERR_UNSUPPORTED
+ * (block != 32, D not 64/128).
  */
 kvs_status kvs_rerope_scatter(const void* k_src, const void* v_src, int64_t src_tokens,
                               const int32_t* src_block, const int32_t* page_table, int64_t n_sel,
