@@ -63,6 +63,12 @@ constexpr int kBufNt = 2;              // non-temporal: data read or written onc
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufWord3);
 }
+// A 16-byte store takes its whole offset in the per-lane (vector) offset with
+// a zero scalar offset.  gfx9 needs a wait state between a store of more than
+// 8 bytes and a VALU write of its data registers; the compiler inserts it only
+// when the scalar offset is the constant 0.  With an SGPR scalar offset, a
+// store that reads its data late (under heavy memory traffic) could store a
+// register the next instruction had already rewritten.
 template <int AUX = 0>
 __device__ __forceinline__ void buf_store16(u32x4 v, __amdgpu_buffer_rsrc_t r, int byte_off) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, AUX);

@@ -46,7 +46,8 @@ __global__ __launch_bounds__(256, 4) void rerope_scatter_kernel(
   build_rope_table<D>(tab, pos_base + (int64_t)kBlk * r, log2_theta);
   __syncthreads();
   // one 32 x D block of one slice through buffer resources: a wave-uniform
-  // base, the lane's byte offset, and each load's row group as a scalar offset
+  // base and the lane's byte offset; each load's row group is a scalar offset,
+  // each store's is added to the lane's offset
   constexpr int kBlkBytes = kBlk * D * 2, kGroupBytes = RPL * D * 2;
   const int lane_off = (rr * D + cl * 8) * 2;
   const int64_t pool_tokens = pool_pages * kBlk;
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(256, 4) void rerope_scatter_kernel(
       float x[8];
       unpack8(w[ld], x);
       rotate8<D>(x, tab[ld * RPL + rr], cl, +1);
-      __builtin_amdgcn_raw_buffer_store_b128(pack8(x), kd, lane_off, ld * kGroupBytes, 0);
+      buf_store16(pack8(x), kd, lane_off + ld * kGroupBytes);   // whole offset per lane (see buf_store16)
     }
   }
 }
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(256) void v_scatter_kernel(const uint16_t* __restri
   const size_t d0 = ((size_t)lg * pool_pages * kBlk + (size_t)dst * kBlk) * D;
   const auto vs = buf_rsrc(v_src + s0, kBlk * D * 2), vd = buf_rsrc(v_pool + d0, kBlk * D * 2);
   const int off = piece * kPieceBytes + threadIdx.x * 16;
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_amdgcn_raw_buffer_load_b128(vs, off, 0, 0), vd, off, 0, 0);
+  buf_store16(__builtin_amdgcn_raw_buffer_load_b128(vs, off, 0, 0), vd, off);
 }
 
 }  // namespace

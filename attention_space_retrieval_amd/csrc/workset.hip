@@ -167,7 +167,8 @@ __global__ __launch_bounds__(256, 4) void workset_apply(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int cl = lane % LPR, rr = lane / LPR;
   // one 32 x D block of one slice through buffer resources (wave-uniform base,
-  // the lane's byte offset, each load's row group as a scalar offset)
+  // the lane's byte offset; each load's row group is a scalar offset, each
+  // store's is added to the lane's offset)
   constexpr int kBlkBytes = kBlk * D * 2, kGroupBytes = RPL * D * 2;
   const int lane_off = (rr * D + cl * 8) * 2;
   const int64_t pool_tokens = pool_pages * kBlk;
@@ -193,13 +194,13 @@ __global__ __launch_bounds__(256, 4) void workset_apply(
       float x[8];
       unpack8(w[ld], x);
       rotate8<D>(x, tab[moved ? 0 : ld * RPL + rr], cl, +1);
-      __builtin_amdgcn_raw_buffer_store_b128(pack8(x), kd, lane_off, ld * kGroupBytes, 0);
+      buf_store16(pack8(x), kd, lane_off + ld * kGroupBytes);   // whole offset per lane (see buf_store16)
     }
     if constexpr (WITH_V) {
       if (!moved) {
         const auto vd = buf_rsrc(v_pool + d0, kBlkBytes);
 #pragma unroll
-        for (int ld = 0; ld < LOADS; ++ld) __builtin_amdgcn_raw_buffer_store_b128(vv[ld], vd, lane_off, ld * kGroupBytes, 0);
+        for (int ld = 0; ld < LOADS; ++ld) buf_store16(vv[ld], vd, lane_off + ld * kGroupBytes);
       }
     }
   }

@@ -268,8 +268,11 @@ def test_meank_1m_step_full_size():
     kvs.kvs_rerope_scatter(k_src, v_src, src_block, pt, budget, c["pos_base"], c["theta"], k_pool, v_pool, err)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
+    # every row of both pools (a store that took the wrong data shows up here, wherever it lands)
+    check_copied_rows(v_src, _block_rows(src_block), v_pool, _block_rows(pt), "scattered V at meank-1m")
+    check_rotated_rows(k_src, _block_rows(src_block), k_pool, _block_rows(pt), "scattered K at meank-1m")
     ptn = pt.cpu().numpy()
-    for _ in range(16):
+    for _ in range(64):
         rr, l, g = int(r.integers(budget)), int(r.integers(L)), int(r.integers(H_kv))
         rows = slice(32 * int(ptn[rr]), 32 * int(ptn[rr]) + 32)
         want = oracle.rope_rotate(oracle.bf16_bits_to_f64(host(k_src[l, g, 32 * rr:32 * rr + 32])),
@@ -278,6 +281,41 @@ def test_meank_1m_step_full_size():
         assert np.array_equal(bits(v_pool[l, g, rows]), host(v_src[l, g, 32 * rr:32 * rr + 32]))
     del k_src, v_src, k_pool, v_pool, R
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- whole-pool properties at full size
+
+def _pair_norms(x):
+    """Squared norm of each rotate-half pair (i, i + D/2) of every row, float32 on the device."""
+    x = x.float()
+    h = x.shape[-1] // 2
+    return x[..., :h] ** 2 + x[..., h:] ** 2
+
+
+def check_rotated_rows(src, src_tok, pool, pool_tok, what):
+    """Every pool row pool_tok[k] of every (layer, KV head) holds a rotation of source row src_tok[k]:
+    each rotate-half pair keeps its norm up to the bf16 rounding of the rotated row (a property of any
+    rotation, checked on the device over the whole pool; the oracle checks sampled pages exactly)."""
+    for l in range(src.shape[0]):
+        a = _pair_norms(src[l][:, src_tok])
+        b = _pair_norms(pool[l][:, pool_tok])
+        bad = (a - b).abs() > a * (1.0 / 64) + 1e-6
+        n = int(bad.sum().item())
+        assert n == 0, f"{what}: layer {l}: {n} rotate-half pairs changed norm, first at " \
+                       f"{[int(v) for v in torch.nonzero(bad)[0].tolist()]}"
+
+
+def check_copied_rows(src, src_tok, pool, pool_tok, what):
+    """Every pool row pool_tok[k] equals source row src_tok[k] bit for bit, over the whole pool."""
+    for l in range(src.shape[0]):
+        eq = src[l][:, src_tok].view(torch.int16) == pool[l][:, pool_tok].view(torch.int16)
+        n = int((~eq).sum().item())
+        assert n == 0, f"{what}: layer {l}: {n} elements differ, first at {[int(v) for v in torch.nonzero(~eq)[0].tolist()]}"
+
+
+def _block_rows(blocks):
+    """Token rows of 32-token blocks, in block order."""
+    return (32 * blocks.to(torch.int64)[:, None] + torch.arange(32, device=blocks.device)).reshape(-1)
 
 
 # ---------------------------------------------------------------- re-RoPE scatter
@@ -310,6 +348,38 @@ def test_rerope_scatter(D, pos_base, with_v, identity, L, H_kv):
     assert_within_ulp(kb, ko, "re-RoPE'd K", atol=1e-6)                       # what is met
     if with_v:
         np.testing.assert_array_equal(bits(v_pool), vo)
+
+
+def test_rerope_scatter_full_size_every_row():
+    """meank-256k's scatter shape (2048 of 8192 blocks straight from the raw workspace, into a permuted
+    pool): V equal and every K pair's norm kept over the whole pool, sampled pages against the oracle."""
+    c = W.config("meank-256k")
+    L, H_kv, D, N, n_sel = c["L"], c["H_kv"], c["D"], c["N"], c["budget"]
+    print("[scatter 256k] inputs", flush=True)
+    k_src = W.normal((L, H_kv, N, D), c["seed"], W.T_K, "bf16", DEV)
+    v_src = W.normal((L, H_kv, N, D), c["seed"], W.T_V, "bf16", DEV)
+    r = np.random.default_rng(66)
+    sel = torch.from_numpy(np.sort(r.choice(N // 32, n_sel, replace=False)).astype(np.int32)).to(DEV)
+    pt = W.page_permutation(n_sel, n_sel, c["seed"]).to(DEV)
+    k_pool = torch.empty((L, H_kv, 32 * n_sel, D), dtype=torch.bfloat16, device=DEV)
+    v_pool = torch.empty_like(k_pool)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    print("[scatter 256k] scatter", flush=True)
+    kvs.kvs_rerope_scatter(k_src, v_src, sel, pt, n_sel, c["pos_base"], c["theta"], k_pool, v_pool, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    print("[scatter 256k] whole-pool checks", flush=True)
+    check_copied_rows(v_src, _block_rows(sel), v_pool, _block_rows(pt), "scattered V")
+    check_rotated_rows(k_src, _block_rows(sel), k_pool, _block_rows(pt), "scattered K")
+    seln, ptn = sel.cpu().numpy(), pt.cpu().numpy()
+    for _ in range(48):
+        rr, l, g = int(r.integers(n_sel)), int(r.integers(L)), int(r.integers(H_kv))
+        b, p = int(seln[rr]), int(ptn[rr])
+        want = oracle.rope_rotate(oracle.bf16_bits_to_f64(host(k_src[l, g, 32 * b:32 * b + 32])),
+                                  c["pos_base"] + 32 * rr + np.arange(32), c["theta"])
+        assert_within_ulp(bits(k_pool[l, g, 32 * p:32 * p + 32]), want, f"page {p} (block {b})", atol=1e-6)
+    del k_src, v_src, k_pool, v_pool
+    torch.cuda.empty_cache()
 
 
 def test_rerope_scatter_rejects_bad_indices():
@@ -475,6 +545,12 @@ def test_working_set_full_shape_sampled():
     np.testing.assert_array_equal(pages.cpu().numpy(), pages_o)
     np.testing.assert_array_equal(rank.cpu().numpy(), rank_o)
     np.testing.assert_array_equal(outgoing[:int(counts[2].item())].cpu().numpy(), out_o)
+    # every selected page: moved blocks are their old page rotated, incoming ones raw K rotated
+    inc = torch.from_numpy(np.flatnonzero(rank_o < 0)).to(DEV)
+    mov = torch.from_numpy(np.flatnonzero(rank_o >= 0)).to(DEV)
+    pg = torch.from_numpy(pages_o.astype(np.int64)).to(DEV)
+    check_rotated_rows(k_src, _block_rows(i32(new)[inc]), k_pool, _block_rows(pg[inc]), "incoming blocks")
+    check_rotated_rows(k_init, _block_rows(pg[mov]), k_pool, _block_rows(pg[mov]), "retained blocks")
     for i in r.choice(len(new), 24, replace=False):
         l, g, p = int(r.integers(L)), int(r.integers(H_kv)), int(pages_o[i])
         rows = slice(32 * p, 32 * p + 32)
