@@ -50,8 +50,10 @@ constexpr float kRebase = 0x1p60f;        // pass 1 rebases its reference past t
 // 8*(v/4) + 4*(l/32) + (v%4) for v = 0..15.
 __device__ __forceinline__ int c_row(int v, int h) { return 8 * (v >> 2) + 4 * h + (v & 3); }
 
+// NT = threads per workgroup: an 8 KB tile is 512 16-byte pieces, 512 / NT per thread.
+template <int NT>
 struct Stage {
-  u32x4 w[2];
+  u32x4 w[512 / NT];
   float4 lse;
 };
 
@@ -61,26 +63,26 @@ struct Stage {
 // the partial last one and those past the end alike, issues the same loads,
 // which lets the compiler keep a later tile's loads in flight while it waits
 // for an earlier one.
-template <bool WITH_LSE>
-__device__ __forceinline__ void stage_load(Stage& st, __amdgpu_buffer_rsrc_t rows, int k,
+template <bool WITH_LSE, int NT>
+__device__ __forceinline__ void stage_load(Stage<NT>& st, __amdgpu_buffer_rsrc_t rows, int k,
                                            __amdgpu_buffer_rsrc_t lse) {
   const int t = threadIdx.x;
   const int base = k * kTile * kRowBytes;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-    st.w[i] = __builtin_amdgcn_raw_buffer_load_b128(rows, base + (t + 256 * i) * 16, 0, 0);
+  for (int i = 0; i < 512 / NT; ++i)
+    st.w[i] = __builtin_amdgcn_raw_buffer_load_b128(rows, base + (t + NT * i) * 16, 0, 0);
   if (WITH_LSE) {
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(lse, t < 8 ? (k * kTile + 4 * t) * 4 : 0x7ffffff0, 0, 0);
     st.lse = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
   }
 }
 
-template <bool WITH_LSE>
-__device__ __forceinline__ void stage_store(const Stage& st, char* buf, float* lbuf) {
+template <bool WITH_LSE, int NT>
+__device__ __forceinline__ void stage_store(const Stage<NT>& st, char* buf, float* lbuf) {
   const int t = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int idx = t + 256 * i, row = idx >> 4, chunk = idx & 15;
+  for (int i = 0; i < 512 / NT; ++i) {
+    const int idx = t + NT * i, row = idx >> 4, chunk = idx & 15;
     *reinterpret_cast<u32x4*>(buf + row * kLdsRow + chunk * 16) = st.w[i];
   }
   if (WITH_LSE && t < 8) *reinterpret_cast<float4*>(lbuf + 4 * t) = st.lse;
@@ -206,8 +208,8 @@ __device__ __forceinline__ void xcd_map(int T, int LG, int& lg, int& tile) {
 // pass 1 may split the candidate range over n_split workgroups (gridDim.y);
 // each then writes a (max, sum) partial per row to part1 and meank_lse_merge
 // combines them.  R_b instantiates SPAN = false, which compiles both out.
-template <bool PASS1, bool SPAN>
-__global__ __launch_bounds__(256, 2) void meank_pass(const uint16_t* __restrict__ Q,
+template <bool PASS1, bool SPAN, int NW = 4>
+__global__ __launch_bounds__(64 * NW, 2) void meank_pass(const uint16_t* __restrict__ Q,
                                                      const uint16_t* __restrict__ index, int LG,
                                                      int64_t rows, int64_t rows_pad, int64_t nB,
                                                      int64_t c0, int64_t c1, int64_t h0, int64_t h1,
@@ -215,8 +217,9 @@ __global__ __launch_bounds__(256, 2) void meank_pass(const uint16_t* __restrict_
                                                      float* __restrict__ lse2,
                                                      float2* __restrict__ part1,
                                                      float* __restrict__ colpart) {
-  // one LDS area: first the workgroup's 256 persistent rows, then the two streamed tiles
-  __shared__ __attribute__((aligned(16))) char smem[kPerWG * kLdsRow];
+  constexpr int NT = 64 * NW, PER_WG = NW * kPerWave;   // threads and persistent rows per workgroup
+  // one LDS area: first the workgroup's persistent rows, then the two streamed tiles
+  __shared__ __attribute__((aligned(16))) char smem[PER_WG * kLdsRow];
   __shared__ __attribute__((aligned(16))) float lses[2][kTile];
   char(*tiles)[kTile * kLdsRow] = reinterpret_cast<char(*)[kTile * kLdsRow]>(smem);
   int lg, tile;
@@ -233,22 +236,22 @@ __global__ __launch_bounds__(256, 2) void meank_pass(const uint16_t* __restrict_
   // takes its 64 rows in the operand layout from there.  Loaded straight in
   // that layout, every load instruction would touch 64 rows 16 bytes at a
   // time, which starves the passes that stream few tiles per workgroup.
-  const int64_t p0 = (int64_t)tile * kPerWG + wave * kPerWave;
+  const int64_t p0 = (int64_t)tile * PER_WG + wave * kPerWave;
   bf16x8 B0[KS], B1[KS];
   {
-    const int64_t pbase = (PASS1 ? 0 : c0) + (int64_t)tile * kPerWG;
+    const int64_t pbase = (PASS1 ? 0 : c0) + (int64_t)tile * PER_WG;
     const int64_t plim = PASS1 ? rows : c1;
-    const int pcount = (int)(plim <= pbase ? 0 : (plim - pbase > kPerWG ? kPerWG : plim - pbase));
+    const int pcount = (int)(plim <= pbase ? 0 : (plim - pbase > PER_WG ? PER_WG : plim - pbase));
     const uint16_t* pg = (PASS1 ? Qg : Ig) + (pcount > 0 ? (size_t)pbase * D : 0);
     const __amdgpu_buffer_rsrc_t prs = buf_rsrc(pg, pcount * kRowBytes);
-    constexpr int kLoads = kPerWG * kRowBytes / 16 / 256;
+    constexpr int kLoads = PER_WG * kRowBytes / 16 / NT;
     u32x4 v[kLoads];
 #pragma unroll
     for (int i = 0; i < kLoads; ++i)
-      v[i] = __builtin_amdgcn_raw_buffer_load_b128(prs, (threadIdx.x + 256 * i) * 16, 0, 0);
+      v[i] = __builtin_amdgcn_raw_buffer_load_b128(prs, (threadIdx.x + NT * i) * 16, 0, 0);
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int idx = threadIdx.x + 256 * i;
+      const int idx = threadIdx.x + NT * i;
       *reinterpret_cast<u32x4*>(smem + (idx >> 4) * kLdsRow + (idx & 15) * 16) = v[i];
     }
     __syncthreads();
@@ -288,7 +291,7 @@ __global__ __launch_bounds__(256, 2) void meank_pass(const uint16_t* __restrict_
   // streamed rows [s_begin, s_end) and, in pass 2, their lse2 (tile k = rows 32k..)
   const __amdgpu_buffer_rsrc_t srows = buf_rsrc(sbase + (size_t)s_begin * D, (int)((s_end - s_begin) * kRowBytes));
   const __amdgpu_buffer_rsrc_t slse = buf_rsrc(Lg, PASS1 ? 0 : (int)(rows_pad * 4));
-  Stage st[PF];
+  Stage<NT> st[PF];
   stage_load<!PASS1>(st[0], srows, 0, slse);
   stage_store<!PASS1>(st[0], tiles[0], lses[0]);
   stage_load<!PASS1>(st[0], srows, 1, slse);
@@ -331,7 +334,7 @@ __global__ __launch_bounds__(256, 2) void meank_pass(const uint16_t* __restrict_
   // load tile t+1+PF into stage sl = st[(t+1) % PF] and move tile t+2, loaded
   // PF-1 iterations earlier, from stage ss = st[(t+2) % PF] into LDS.
   auto body = [&](int t, f32x16& cc0, f32x16& cc1, float* lc, f32x16& cn0, f32x16& cn1, float* ln,
-                  Stage& sl, Stage& ss) __attribute__((always_inline)) {
+                  Stage<NT>& sl, Stage<NT>& ss) __attribute__((always_inline)) {
     const bool pre = t + 2 < nt;
     stage_load<!PASS1>(sl, srows, t + 1 + PF, slse);   // past the end: reads nothing, returns zeros
     read_streamed(tiles[(t + 1) & 1], lane, A);
@@ -527,7 +530,7 @@ namespace {
 
 struct WindowPlan {
   int64_t rows, rows_pad, c0, c1, h0, h1;
-  int T1, T2, n_split;
+  int T1, T2, n_split, nw1;
 };
 
 WindowPlan window_plan(int L, int H_q, int H_kv, int64_t W, int64_t N, int64_t pi, int64_t q_s, int64_t q_e) {
@@ -540,7 +543,11 @@ WindowPlan window_plan(int L, int H_q, int H_kv, int64_t W, int64_t N, int64_t p
   p.h0 = q_s > p.c0 ? q_s : p.c0;
   p.h1 = q_e < N ? q_e : N;
   if (p.h1 < p.h0) p.h1 = p.h0;
-  p.T1 = (int)ceil_div(p.rows_pad, kPerWG);
+  // pass 1 with two waves per workgroup when the window has at most 128 rows
+  // (a 256-row workgroup would leave half its waves without rows): twice the
+  // workgroups per CU, each streaming its own keys
+  p.nw1 = p.rows_pad <= 2 * kPerWave ? 2 : 4;
+  p.T1 = (int)ceil_div(p.rows_pad, p.nw1 * kPerWave);
   p.T2 = (int)ceil_div(p.c1 - p.c0 > 0 ? p.c1 - p.c0 : 1, kPerWG);
   // at least ~2048 workgroups in pass 1, and at least 8 tiles per split
   const int64_t want = ceil_div(2048, (int64_t)p.T1 * LG);
@@ -578,9 +585,13 @@ hipError_t kvs_launch_window(const void* K, const void* Qw, int L, int H_q, int 
   int64_t c0 = p.c0, c1 = p.c1;
   const bool any = c1 > c0 && !(p.h0 <= c0 && p.h1 >= c1) && p.rows > 0;
   if (any) {
-    hipLaunchKernelGGL((meank_pass<true, true>), dim3((unsigned)p.T1 * LG, (unsigned)p.n_split), dim3(256), 0, st, Qb,
-                       Kb, LG, p.rows, p.rows_pad, N, c0, c1, p.h0, p.h1, p.T1, scale, p.n_split, lse2, part1,
-                       colpart);
+    const dim3 grid1((unsigned)p.T1 * LG, (unsigned)p.n_split);
+    if (p.nw1 == 2)
+      hipLaunchKernelGGL((meank_pass<true, true, 2>), grid1, dim3(128), 0, st, Qb, Kb, LG, p.rows, p.rows_pad, N, c0,
+                         c1, p.h0, p.h1, p.T1, scale, p.n_split, lse2, part1, colpart);
+    else
+      hipLaunchKernelGGL((meank_pass<true, true>), grid1, dim3(256), 0, st, Qb, Kb, LG, p.rows, p.rows_pad, N, c0, c1,
+                         p.h0, p.h1, p.T1, scale, p.n_split, lse2, part1, colpart);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (p.n_split > 1) {

@@ -221,6 +221,8 @@ def test_rule_paged_full_size_equals_dense(name):
     (2, 8, 2, 3000, 16, 10, 1000, 1100),       # span in the middle: a hole in the candidates
     (1, 40, 8, 777, 7, 0, 0, 0),               # G = 5, odd W, no forced positions, ragged N
     (1, 4, 4, 300, 1, 299, 0, 0),              # one candidate
+    (1, 16, 2, 2500, 32, 5, 2400, 2450),       # G*W = 256 rows: pass 1 with four-wave workgroups
+    (1, 20, 4, 1800, 40, 0, 1700, 1800),       # G*W = 200 rows (padded to 224): four waves, a partial one
 ])
 def test_window_score_against_oracle(L, H_q, H_kv, N, W, pi, q_s, q_e):
     K = W_.normal((L, H_kv, N, 128), 17, W_.T_K, "bf16", DEV)
