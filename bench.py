@@ -40,7 +40,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 WORKLOADS = {"rule-8b+meank-256k": ("rule-8b", "meank-256k"),
              "rule-14b+meank-1m": ("rule-14b", "meank-1m")}
-# kernels each call launches (rocprofv3 short names)
+# kernels each call launches (rocprofv3 short names); a tuple lists alternatives of which the
+# call launches one, chosen by the sizes (the window score's first pass runs two-wave workgroups
+# for windows of at most 128 rows per KV group)
 CALL_KERNELS = {
     "kvs_qmem_update": ["qmem_kernel<128, true>"],
     "kvs_rule_score": ["rule_logits_mfma<128, 1, false>", "rule_lse_merge", "rule_colsum"],
@@ -48,12 +50,13 @@ CALL_KERNELS = {
     "kvs_topk_select[meank]": ["topk_reg_kernel<8>"],
     "kvs_slotmap_redirect": ["slotmap_kernel"],
     "kvs_meank_build": ["meank_build_raw<128>"],
-    "kvs_meank_score": ["meank_pass<true, false>", "meank_pass<false, false>", "meank_reduce<false>"],
+    "kvs_meank_score": ["meank_pass<true, false, 4>", "meank_pass<false, false, 4>", "meank_reduce<false>"],
     "kvs_rerope_scatter": ["rerope_scatter_kernel<128>", "v_scatter_kernel<128>"],
     # rows beyond the step (timed after it): the paged rule score's merge and column sum are the
     # dense call's kernels on the same sizes
     "kvs_rule_score_paged": ["rule_logits_mfma<128, 1, true>", "rule_lse_merge", "rule_colsum"],
-    "kvs_window_score": ["meank_pass<true, true>", "meank_lse_merge", "meank_pass<false, true>",
+    "kvs_window_score": [("meank_pass<true, true, 2>", "meank_pass<true, true, 4>"), "meank_lse_merge",
+                         "meank_pass<false, true, 4>",
                          "meank_reduce<true>"],
     "kvs_meank_append": ["meank_append_kernel<128>"],
     "kvs_working_set_update": ["workset_diff", "workset_apply<128, true>"],
@@ -254,8 +257,9 @@ def measured_traffic(workload):
     for call, kernels in CALL_KERNELS.items():
         total = 0.0
         for k in kernels:
-            e = summ.get(k)
-            if e is None or e["source_sha256"] != rs.source_hash(rs.base_name(k)):
+            alts = k if isinstance(k, tuple) else (k,)   # alternatives share one source file
+            e = next((summ[n] for n in alts if n in summ), None)
+            if e is None or e["source_sha256"] != rs.source_hash(rs.base_name(alts[0])):
                 total = None
                 break
             total += e["read_bytes_mean"] + e["write_bytes_mean"]
@@ -457,7 +461,8 @@ def main():
         "config": {"workload": a.workload, "rule": {k: c[k] for k in ("L", "H_q", "H_kv", "D", "N", "pi", "q_s", "q_e", "C", "lam")},
                    "meank": {k: m[k] for k in ("L", "H_q", "H_kv", "D", "N", "Mq", "n_sink", "n_recent", "budget", "theta")},
                    "tokens_per_step": tokens},
-        "roofline": {"call": dom, "kernels": " + ".join(CALL_KERNELS.get(dom, [dom])), "bound": d["bound"],
+        "roofline": {"call": dom, "kernels": " + ".join(k if isinstance(k, str) else " | ".join(k)
+                                                         for k in CALL_KERNELS.get(dom, [dom])), "bound": d["bound"],
                      "achieved": d["achieved"], "peak": d["peak"], "unit": d["unit"], "frac": d["frac"],
                      "per_launch": d["per_launch"], "traffic": d["traffic"]},
         "rule_turn": {"ms": round(rule_ms, 4), "tokens_per_s": c["N"] / (rule_ms * 1e-3),
