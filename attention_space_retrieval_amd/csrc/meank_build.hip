@@ -16,6 +16,11 @@ using namespace kvs;
 namespace {
 
 constexpr int kBlk = 32;
+// Sums start from -0 and absent rows read as -0: -0 is the additive identity
+// (x + -0 = x for every x, -0 included), so each sum is exactly the float32
+// sum of the block's rows, and a block of -0 keys averages to -0.
+constexpr float kNegZero = -0.0f;
+constexpr u32x4 kNegZeroRows = {0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
 
 // The index rows are a thin write stream inside a saturated read stream.
 // Written through to memory at once (the sc1 cache policy) they cost about
@@ -52,8 +57,8 @@ __global__ __launch_bounds__(256) void meank_build_raw(const uint16_t* __restric
 #pragma unroll
     for (int i = 0; i < LOADS; ++i)
       w[i] = i * RPL + rr < nb ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t)i * RPL * D))
-                               : u32x4{0u, 0u, 0u, 0u};
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                               : kNegZeroRows;
+    float acc[8] = {kNegZero, kNegZero, kNegZero, kNegZero, kNegZero, kNegZero, kNegZero, kNegZero};
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       float x[8];
@@ -95,9 +100,9 @@ __global__ __launch_bounds__(256) void meank_build_derope(const uint16_t* __rest
 #pragma unroll
     for (int ld = 0; ld < LOADS; ++ld) {
       const int t = ld * RPL + rr;
-      w[ld] = t < nb ? *reinterpret_cast<const u32x4*>(src + (size_t)t * D) : u32x4{0u, 0u, 0u, 0u};
+      w[ld] = t < nb ? *reinterpret_cast<const u32x4*>(src + (size_t)t * D) : kNegZeroRows;
     }
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float acc[8] = {kNegZero, kNegZero, kNegZero, kNegZero, kNegZero, kNegZero, kNegZero, kNegZero};
 #pragma unroll
     for (int ld = 0; ld < LOADS; ++ld) {
       const int t = ld * RPL + rr;
@@ -157,11 +162,11 @@ __global__ __launch_bounds__(256) void meank_append_kernel(const uint16_t* __res
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int64_t t = tb + i * RPL + rr;
-      w[i] = u32x4{0u, 0u, 0u, 0u};
+      w[i] = kNegZeroRows;
       if (t < t0) w[i] = *reinterpret_cast<const u32x4*>(st + (size_t)t * D);
       else if (t < t1) w[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t)(t - t0) * D));
     }
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float acc[8] = {kNegZero, kNegZero, kNegZero, kNegZero, kNegZero, kNegZero, kNegZero, kNegZero};
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int r = i * RPL + rr;
@@ -174,7 +179,7 @@ __global__ __launch_bounds__(256) void meank_append_kernel(const uint16_t* __res
         *reinterpret_cast<u32x4*>(st + (size_t)t * D) = y;
         w[i] = y;
       }
-      unpack8(w[i], x);                     // staged (rounded) raw K, zero past the end
+      unpack8(w[i], x);                     // staged (rounded) raw K, -0 past the end
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] += x[e];
     }

@@ -39,7 +39,12 @@ __device__ __forceinline__ void rotate8(float* x, const float2* row_tab, int cl,
   constexpr int LPR = D / 8;
   float p[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) p[e] = __shfl_xor(x[e], LPR / 2, kWave);
+  for (int e = 0; e < 8; ++e) {
+    if constexpr (LPR == 16)   // partner lane = lane ^ 8: a rotation by 8 within each 16-lane row (DPP)
+      p[e] = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x[e]), 0x128, 0xf, 0xf, false));
+    else
+      p[e] = __shfl_xor(x[e], LPR / 2, kWave);
+  }
   const bool first = cl < LPR / 2;
   // first half: y = x c - dir * xp s ; second half: y = x c + dir * xp s
   const float sg = (first ? -1.f : 1.f) * (float)dir;

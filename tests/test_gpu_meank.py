@@ -31,6 +31,56 @@ def test_meank_build_raw(L, H_kv, N, D):
     assert_within_ulp(bits(idx), want, "index", atol=1e-5)
 
 
+def _bf16_pairs():
+    """(a, c) bf16 bit pairs whose mean is exact in float32: ties at both parities, in normal and
+    subnormal range, across a binade edge, signed zeros, infinities and NaNs."""
+    pairs = []
+    for base in (0x3F80, 0x0080, 0x4300, 0x7B00, 0x3A00, 0xBF80, 0xC300):
+        for off in (0, 1, 2, 3, 0x7E):
+            pairs.append((base + off, base + off + 1))              # half-ulp tie
+    pairs += [(0x0000, 0x0001), (0x0001, 0x0002), (0x0002, 0x0003), (0x007E, 0x007F), (0x007F, 0x0080),
+              (0x8001, 0x8002), (0x8000, 0x8001)]                   # subnormal ties
+    pairs += [(0x3F7F, 0x3F80), (0x3F80, 0x3F83), (0x3F81, 0x3F84), (0x3F80, 0x3F82)]
+    pairs += [(v, v) for v in (0x0001, 0x8001, 0x7F80, 0xFF80, 0x8000, 0x0000, 0x3F80)]
+    pairs += [(0x8000, 0x0000), (0x7FC0, 0x7FC0), (0x7F80, 0xFF80), (0xFFC1, 0x3F80)]
+    r = np.random.default_rng(31)
+    while len(pairs) < 128:
+        a = int(r.integers(0x0080, 0x7B00)) | (0x8000 if r.integers(2) else 0)
+        pairs.append((a, a + 1))
+    return np.array(pairs[:128], dtype=np.uint16)
+
+
+def test_meank_build_bf16_rounding_special_values():
+    """Each dimension's block holds 16 rows of a and 16 of c, so the float32 mean (a + c) / 2 is
+    exact and the index must be its round-to-nearest-even bf16, bit for bit (NaN: any NaN)."""
+    p = _bf16_pairs()
+    rows = np.concatenate([np.repeat(p[None, :, 0], 16, 0), np.repeat(p[None, :, 1], 16, 0)])
+    K = torch.from_numpy(rows.view(np.int16).reshape(1, 1, 32, 128)).view(torch.bfloat16).to(DEV)
+    idx = kvs.kvs_meank_build(K)
+    torch.cuda.synchronize()
+    got = bits(idx).reshape(128)
+    a = torch.from_numpy(p[:, 0].view(np.int16)).view(torch.bfloat16).double()
+    c = torch.from_numpy(p[:, 1].view(np.int16)).view(torch.bfloat16).double()
+    mean = (a + c) / 2
+    finite = torch.isfinite(mean)
+    assert torch.equal(mean[finite].float().double(), mean[finite])      # the float32 mean is exact
+    want = mean.float().to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    nan = mean.isnan().numpy()
+    got_nan = ((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0)
+    assert np.array_equal(got_nan, nan), "NaN lanes differ"
+    bad = np.nonzero((got != want) & ~nan)[0]
+    assert bad.size == 0, [(hex(p[i, 0]), hex(p[i, 1]), hex(got[i]), hex(want[i])) for i in bad[:8]]
+    # a partial block of 20 equal rows averages to that value exactly (-0, subnormals, infinities too)
+    rows = np.repeat(p[None, :, 0], 20, 0)
+    K = torch.from_numpy(rows.view(np.int16).reshape(1, 1, 20, 128)).view(torch.bfloat16).to(DEV)
+    got = bits(kvs.kvs_meank_build(K)).reshape(128)
+    torch.cuda.synchronize()
+    v = p[:, 0]
+    v_nan = ((v & 0x7F80) == 0x7F80) & ((v & 0x7F) != 0)
+    got_nan = ((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0)
+    assert np.array_equal(got_nan, v_nan) and np.array_equal(got[~v_nan], v[~v_nan])
+
+
 @pytest.mark.parametrize("D,pos0", [(128, 0), (128, 1000000 - 640), (64, 12345)])
 def test_meank_build_derope(D, pos0):
     L, H_kv, N, theta = 2, 2, 640 + 17, 1e6
