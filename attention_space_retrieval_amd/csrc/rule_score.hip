@@ -186,7 +186,10 @@ __global__ __launch_bounds__(256) void rule_logits_mfma(
       for (int v = 0; v < 4; ++v) {
         // C row 4*(lane>>4)+v: lanes 0..31 hold the high rows, lanes 32..63 the low rows,
         // so lanes 0..15 hold head hg*8+v and lanes 16..31 head hg*8+4+v.
-        const float t = c[v] + __shfl_xor(c[v], 32, kWave);
+        // lanes 0..31 add the low part held by lane + 32 (v_permlane32_swap hands
+        // the upper half-wave's values to the lower half); lanes 32..63 are inactive below
+        const uint32_t cu = __float_as_uint(c[v]);
+        const float t = c[v] + __uint_as_float(__builtin_amdgcn_permlane32_swap(cu, cu, false, false)[1]);
         const int hl = hg * 8 + 4 * (q & 1) + v;
         const bool act = lane < 32 && vj && hl < G;
         // Branch-free: each head's spill row is a buffer resource (a head past G
