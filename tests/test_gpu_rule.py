@@ -45,7 +45,9 @@ def check_rule(K, M, pi, q_s, q_e, what, M_oracle=None):
 
 # ---------------------------------------------------------------- QueryMemory
 
-@pytest.mark.parametrize("dtype,D,S", [("f32", 64, 32), ("bf16", 128, 64), ("bf16", 64, 5)])
+@pytest.mark.parametrize("dtype,D,S", [("f32", 64, 32), ("bf16", 128, 64), ("bf16", 64, 5),
+                                       # spans over several load batches with a ragged last one
+                                       ("f32", 128, 70), ("bf16", 128, 200), ("f32", 64, 97), ("bf16", 64, 300)])
 def test_qmem_turns(dtype, D, S):
     L, H_q, T, lam = 3, 8, 4, 0.3
     spans = [W.normal((L, H_q, S, D), 77, 100 + t, dtype, DEV) for t in range(T)]
