@@ -387,7 +387,7 @@ def main():
                     help="after the timed steps, run one 4 GiB device copy (for HBM counter scaling)")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the scoring path has no multi-GPU mode in this build "
+        print("bench.py measures one GPU: the library runs on one device and has no multi-GPU mode "
               "(sharding by (layer, KV head) is a design note). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     dev = "cuda:0"
