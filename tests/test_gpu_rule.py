@@ -203,7 +203,7 @@ def test_rule_paged_against_oracle(dtype, L, H_q, H_kv, D, N, pool_size, dead):
     assert_rel(got[~out], want[~out], RULE_RTOL, f"paged rule {dtype} D{D}")
 
 
-@pytest.mark.parametrize("name", ["rule-8b"])
+@pytest.mark.parametrize("name", ["rule-8b", "rule-14b"])
 def test_rule_paged_full_size_equals_dense(name):
     """At full size, the pool read through a permuted slot map gives the dense scores bit for bit."""
     c = W.config(name)
@@ -252,9 +252,11 @@ def test_window_one_row_matches_rule_score():
     assert_rel(win.cpu().numpy()[~F], rule.cpu().numpy()[~F], RULE_RTOL, "window(W=1) vs rule")
 
 
-def test_window_score_full_size_sampled():
-    """rule-8b's cache with a 32-row window: sampled layers' contribution checked against the oracle."""
-    c = W_.config("rule-8b")
+@pytest.mark.parametrize("name", ["rule-8b", "rule-14b"])
+def test_window_score_full_size_sampled(name):
+    """The cache with a 32-row window (128 rows per KV group at rule-8b, 160 at rule-14b): two
+    layers' contribution checked against the oracle, the whole call by its invariants."""
+    c = W_.config(name)
     L, H_q, H_kv, D, N = c["L"], c["H_q"], c["H_kv"], c["D"], c["N"]
     K = W_.normal((L, H_kv, N, D), c["seed"], W_.T_K, "bf16", DEV)
     Qw = W_.normal((L, H_q, 32, D), c["seed"], W_.T_Q, "bf16", DEV)
@@ -264,7 +266,7 @@ def test_window_score_full_size_sampled():
     torch.cuda.synchronize()
     F = oracle.forced_mask(N, c["pi"], c["q_s"], c["q_e"])
     want = oracle.window_score(host(K[:2]), host(Qw[:2]), c["pi"], c["q_s"], c["q_e"])
-    assert_rel(two.cpu().numpy()[~F], want[~F], RULE_RTOL, "window score, 2 layers of rule-8b")
+    assert_rel(two.cpu().numpy()[~F], want[~F], RULE_RTOL, f"window score, 2 layers of {name}")
     g = got.cpu().numpy()
     assert np.all(g[F] == 0.0) and np.all(g[~F] > 0.0)
     assert abs(g.sum(dtype=np.float64) - L * H_q * 32) <= 1e-4 * L * H_q * 32
