@@ -14,9 +14,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
-// (layer, KV head) slices per workgroup of the re-RoPE scatter (its grid has
-// n_sel * ceil(L*H_kv / kScatterSlices) workgroups)
-constexpr int kScatterSlices = 8;
+// (layer, KV head) slices per workgroup: the re-RoPE scatter runs one wave per
+// slice (n_sel * ceil(L*H_kv / kScatterSlices) workgroups of kScatterThreads),
+// the working-set update two slices per wave of a 256-thread workgroup
+// (n_new * ceil(L*H_kv / kWorksetSlices) workgroups)
+constexpr int kScatterSlices = 16;
+constexpr int kScatterThreads = 64 * kScatterSlices;
+constexpr int kWorksetSlices = 8;
 
 // bf16 is the top half of a binary32: widening is a shift.
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }

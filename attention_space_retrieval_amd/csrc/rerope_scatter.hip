@@ -5,14 +5,15 @@
 // page_table[r]; V is copied unchanged.
 //
 // HBM-bound (read K and V once, write them once).  A workgroup owns one
-// selected block for a chunk of 8 (layer, KV head) slices: it builds the
-// block's 32 x D/2 rotation table in LDS (float64 angles) and streams those
-// slices' 32-row blocks of K and V through it with 16-byte coalesced loads and
-// stores, one slice per wave at a time.  The grid runs the chunks of a block
-// fastest.  Many short-lived workgroups at 4 waves per SIMD keep more
-// independent streams in flight than one long-lived workgroup per block
-// (whose register-resident table allowed 2): 7.0 -> 6.65 ms for 2048 blocks
-// over 512 slices, where a plain copy of the same 8 KB pieces takes 6.5 ms.
+// selected block for a chunk of 16 (layer, KV head) slices: it builds the
+// block's 32 x D/2 rotation table in LDS (float64 angles), then each of its
+// 16 waves streams one slice's 32-row block of K through it with 16-byte
+// coalesced loads and stores.  The grid runs the chunks of a block fastest.
+// One slice per wave matters: a wave that loops over two slices waits for its
+// first slice's stores before it can use its second slice's loads (gfx9 counts
+// both on one counter).  Same-process A/B for 2048 blocks over 512 slices:
+// 6.50 ms with 8 slices per workgroup at two per wave, 6.46 ms at one per wave,
+// 6.42 ms with 16 slices at one per wave (4 slices: 6.55 ms).
 // Out-of-range block ids or pages skip the block and raise err_flag instead
 // of touching memory outside the buffers.
 #include "rope_table.h"
@@ -22,10 +23,10 @@ using namespace kvs;
 namespace {
 
 constexpr int kBlk = 32;
-constexpr int kLgChunk = kScatterSlices;   // (layer, KV head) slices per workgroup, two per wave
+constexpr int kLgChunk = kScatterSlices;   // (layer, KV head) slices per workgroup, one per wave
 
 template <int D>
-__global__ __launch_bounds__(256, 4) void rerope_scatter_kernel(
+__global__ __launch_bounds__(kScatterThreads, 1) void rerope_scatter_kernel(
     const uint16_t* __restrict__ k_src, int64_t src_tokens, const int32_t* __restrict__ src_block,
     const int32_t* __restrict__ page_table, int LG, int64_t pos_base, double log2_theta,
     uint16_t* __restrict__ k_pool, int64_t pool_pages, int32_t* __restrict__ err_flag) {
@@ -52,7 +53,7 @@ __global__ __launch_bounds__(256, 4) void rerope_scatter_kernel(
   const int lane_off = (rr * D + cl * 8) * 2;
   const int64_t pool_tokens = pool_pages * kBlk;
   const int lg_end = min(LG, (chunk + 1) * kLgChunk);
-  for (int lg = chunk * kLgChunk + wave; lg < lg_end; lg += 4) {
+  for (int lg = chunk * kLgChunk + wave; lg < lg_end; lg += kScatterThreads / 64) {
     const size_t s0 = ((size_t)lg * src_tokens + (size_t)sb * kBlk) * D;
     const size_t d0 = ((size_t)lg * pool_tokens + (size_t)dst * kBlk) * D;
     const auto ks = buf_rsrc(k_src + s0, kBlkBytes), kd = buf_rsrc(k_pool + d0, kBlkBytes);
@@ -106,7 +107,7 @@ hipError_t kvs_launch_rerope(const void* k_src, const void* v_src, int64_t src_t
   if (n_sel == 0) return hipSuccess;
   const int LG = L * H_kv;
   const double l2t = __builtin_log2(theta);
-  dim3 grid((unsigned)(n_sel * ceil_div(LG, kLgChunk))), block(256);
+  dim3 grid((unsigned)(n_sel * ceil_div(LG, kLgChunk))), block(kScatterThreads);
   const uint16_t* ks = static_cast<const uint16_t*>(k_src);
   const uint16_t* vs = static_cast<const uint16_t*>(v_src);
   uint16_t* kp = static_cast<uint16_t*>(k_pool);
@@ -121,10 +122,10 @@ hipError_t kvs_launch_rerope(const void* k_src, const void* v_src, int64_t src_t
   if (e != hipSuccess || !vs) return e;
   const dim3 vgrid((unsigned)(n_sel * (kBlk * D * 2 / 4096)), (unsigned)LG);
   if (D == 128)
-    hipLaunchKernelGGL(v_scatter_kernel<128>, vgrid, block, 0, st, vs, src_tokens, src_block, page_table, vp,
+    hipLaunchKernelGGL(v_scatter_kernel<128>, vgrid, dim3(256), 0, st, vs, src_tokens, src_block, page_table, vp,
                        pool_pages);
   else
-    hipLaunchKernelGGL(v_scatter_kernel<64>, vgrid, block, 0, st, vs, src_tokens, src_block, page_table, vp,
+    hipLaunchKernelGGL(v_scatter_kernel<64>, vgrid, dim3(256), 0, st, vs, src_tokens, src_block, page_table, vp,
                        pool_pages);
   return hipGetLastError();
 }

@@ -142,10 +142,12 @@ __global__ __launch_bounds__(kThreads) void workset_diff(
   }
 }
 
-// One workgroup per (selected block, chunk of kScatterSlices slices), chunks
-// fastest, two slices per wave at a time -- the layout of the re-RoPE scatter,
-// whose short-lived workgroups at 4 waves per SIMD stream faster than one
-// workgroup per block over every slice.
+// One workgroup per (selected block, chunk of kWorksetSlices slices), chunks
+// fastest, two slices per wave: short-lived workgroups stream faster than one
+// workgroup per block over every slice.  The scatter's shape (16 slices, one
+// per wave of a 1024-thread workgroup) was 4% slower here: most workgroups
+// belong to blocks retained in place, which exit at once, and large
+// workgroups cost more to launch and retire.
 template <int D, bool WITH_V>
 __global__ __launch_bounds__(256, 4) void workset_apply(
     const uint16_t* __restrict__ k_src, const uint16_t* __restrict__ v_src, int64_t src_tokens,
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(256, 4) void workset_apply(
     uint16_t* __restrict__ k_pool, uint16_t* __restrict__ v_pool, int64_t pool_pages) {
   constexpr int LPR = D / 8, RPL = 64 / LPR, LOADS = kBlk / RPL;
   __shared__ float2 tab[kBlk][D / 2];
-  const int nch = (LG + kScatterSlices - 1) / kScatterSlices;
+  const int nch = (LG + kWorksetSlices - 1) / kWorksetSlices;
   const int r = blockIdx.x / nch, chunk = blockIdx.x % nch;
   const int32_t rank = old_rank[r];
   const int64_t page = pages[r];
@@ -172,8 +174,8 @@ __global__ __launch_bounds__(256, 4) void workset_apply(
   constexpr int kBlkBytes = kBlk * D * 2, kGroupBytes = RPL * D * 2;
   const int lane_off = (rr * D + cl * 8) * 2;
   const int64_t pool_tokens = pool_pages * kBlk;
-  const int lg_end = min(LG, (chunk + 1) * kScatterSlices);
-  for (int lg = chunk * kScatterSlices + wave; lg < lg_end; lg += 4) {
+  const int lg_end = min(LG, (chunk + 1) * kWorksetSlices);
+  for (int lg = chunk * kWorksetSlices + wave; lg < lg_end; lg += 4) {
     const size_t d0 = ((size_t)lg * pool_tokens + (size_t)page * kBlk) * D;
     const size_t s0 = ((size_t)lg * src_tokens + (size_t)sb * kBlk) * D;
     const auto kin = buf_rsrc(moved ? k_pool + d0 : k_src + s0, kBlkBytes);
@@ -230,7 +232,7 @@ hipError_t kvs_launch_workset(const void* k_src, const void* v_src, int64_t src_
   const uint16_t* vs = static_cast<const uint16_t*>(v_src);
   uint16_t* kp = static_cast<uint16_t*>(k_pool);
   uint16_t* vp = static_cast<uint16_t*>(v_pool);
-  const dim3 grid((unsigned)(n_new * ceil_div(LG, kScatterSlices))), block(256);
+  const dim3 grid((unsigned)(n_new * ceil_div(LG, kWorksetSlices))), block(256);
 #define KVS_APPLY(DD, WV)                                                                          \
   hipLaunchKernelGGL((workset_apply<DD, WV>), grid, block, 0, st, ks, vs, src_tokens, new_blocks, \
                      pages_out, old_rank_out, LG, pos_base, l2t, kp, vp, pool_pages)

@@ -31,8 +31,8 @@
  *     dimension, N tokens.
  *   - bf16 means IEEE binary32 with the low 16 bits dropped (uint16 storage).
  *   - A data pointer may be NULL only where its tensor holds no elements.
- *   - Sizes that would need a launch of 2^24 or more 256-thread workgroups
- *     (far beyond any single-GPU cache) return KVS_ERR_SHAPE.
+ *   - Sizes that would need a launch of 2^24 or more workgroups (far beyond
+ *     any single-GPU cache) return KVS_ERR_SHAPE.
  */
 #ifndef KVS_H_
 #define KVS_H_
@@ -261,7 +261,7 @@ kvs_status kvs_meank_score(const void* Q, const void* index, int32_t L, int32_t 
  *                named keep their contents.  v_src/v_pool may both be NULL.
  *   err_flag     nullable device int32: set to 1 if a src_block or
  *                page_table entry is out of range (that block is skipped).
- * Errors: KVS_ERR_ARG, KVS_ERR_SHAPE (also n_sel >= 2^23, n_sel * ceil(L*H_kv / 8)
+ * Errors: KVS_ERR_ARG, KVS_ERR_SHAPE (also n_sel >= 2^23, n_sel * ceil(L*H_kv / 16)
  * >= 2^24 or L*H_kv > 65535: the launches' grid limits), KVS_ERR_UNSUPPORTED
  * (block != 32, D not 64/128).
  */

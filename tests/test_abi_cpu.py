@@ -171,8 +171,8 @@ def test_working_set_rejections(lib):
 def test_oversized_launches_are_rejected(lib):
     r = lib.kvs_rerope_scatter
     assert r(FAKE, None, 640, FAKE, None, 1 << 24, 2, 2, 128, 32, 0, 1e6, FAKE, None, 8, None, None) == 2
-    # one workgroup per (block, 8 slices): 2^21 blocks over 64 slices is 2^24 workgroups
-    assert r(FAKE, None, 640, FAKE, None, 1 << 21, 8, 8, 128, 32, 0, 1e6, FAKE, None, 8, None, None) == 2
+    # one workgroup per (block, 16 slices): 2^22 blocks over 64 slices is 2^24 workgroups
+    assert r(FAKE, None, 640, FAKE, None, 1 << 22, 8, 8, 128, 32, 0, 1e6, FAKE, None, 8, None, None) == 2
     ws = 1 << 30
     assert lib.kvs_meank_score(FAKE, FAKE, 4, 8, 2, 128, 50, (1 << 31) - 1, 4, 7, FAKE, FAKE, ws, None) == 2
     # streamed operands past 2^23 - 128 rows (32-bit buffer offsets): index blocks, query rows, keys, window rows
