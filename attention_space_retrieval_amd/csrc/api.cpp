@@ -163,7 +163,9 @@ kvs_status kvs_meank_build(const void* K, int32_t L, int32_t H_kv, int32_t D, in
   if (L < 1 || H_kv < 1 || N < 0 || pos0 < 0) return KVS_ERR_ARG;
   if (k_is_rope && !(std::isfinite(theta) && theta > 0.0)) return KVS_ERR_ARG;
   if (block != 32 || !head_dim_ok(D)) return KVS_ERR_UNSUPPORTED;
-  if (numel4(L, H_kv, N, D) < 0 || (N + 31) / 32 > kMaxIndex || !grid_ok(cdiv(N, 32))) return KVS_ERR_SHAPE;
+  if (numel4(L, H_kv, N, D) < 0 || (N + 31) / 32 > kMaxIndex || !grid_ok(cdiv(N, 32)) ||
+      (k_is_rope && raw_k_out && !grid_ok(cdiv(N, 32) * cdiv((int64_t)L * H_kv, kvs::kScatterSlices))))
+    return KVS_ERR_SHAPE;
   return hip_status(kvs_launch_meank_build(K, L, H_kv, D, N, k_is_rope ? 1 : 0, pos0, theta,
                                            k_is_rope ? raw_k_out : nullptr, index,
                                            as_stream(stream)));

@@ -193,7 +193,9 @@ kvs_status kvs_slotmap_redirect(const int64_t* slot_in, const uint8_t* keep_mask
  *            back; raw_k_out (nullable, [L,H_kv,N,D] bf16) then receives k~.
  *   index    [L, H_kv, ceil(N/block), D] bf16 output.
  * Errors: KVS_ERR_ARG (null, pos0 < 0, theta not finite/positive),
- * KVS_ERR_UNSUPPORTED (block != 32, D not 64/128), KVS_ERR_SHAPE.
+ * KVS_ERR_UNSUPPORTED (block != 32, D not 64/128), KVS_ERR_SHAPE (also, in
+ * de-RoPE mode with raw_k_out, ceil(N/32) * ceil(L*H_kv / 16) >= 2^24: the
+ * launch's grid limit).
  */
 kvs_status kvs_meank_build(const void* K, int32_t L, int32_t H_kv, int32_t D, int64_t N,
                            int32_t block, int32_t k_is_rope, int64_t pos0, double theta,

@@ -81,18 +81,22 @@ def test_meank_build_bf16_rounding_special_values():
     assert np.array_equal(got_nan, v_nan) and np.array_equal(got[~v_nan], v[~v_nan])
 
 
-@pytest.mark.parametrize("D,pos0", [(128, 0), (128, 1000000 - 640), (64, 12345)])
-def test_meank_build_derope(D, pos0):
-    L, H_kv, N, theta = 2, 2, 640 + 17, 1e6
+@pytest.mark.parametrize("D,pos0,L,H_kv,with_raw", [
+    (128, 0, 2, 2, True), (128, 1000000 - 640, 2, 2, True), (64, 12345, 2, 2, True),
+    (128, 777, 3, 7, True), (64, 777, 3, 7, False),      # 21 slices: two chunks of 16, the second ragged
+])
+def test_meank_build_derope(D, pos0, L, H_kv, with_raw):
+    N, theta = 640 + 17, 1e6
     raw = host(W.normal((L, H_kv, N, D), 22, W.T_K, "bf16", "cpu"))
     post = oracle.f64_to_bf16_bits(oracle.rope_rotate(oracle.bf16_bits_to_f64(raw),
                                                       pos0 + np.arange(N), theta))
     Kt = torch.from_numpy(post.view(np.int16)).view(torch.bfloat16).to(DEV)
-    raw_out = torch.empty_like(Kt)
+    raw_out = torch.empty_like(Kt) if with_raw else None
     idx = kvs.kvs_meank_build(Kt, k_is_rope=True, pos0=pos0, theta=theta, raw_k_out=raw_out)
     torch.cuda.synchronize()
     want_idx, want_raw = oracle.meank_build(post, k_is_rope=True, pos0=pos0, theta=theta)
-    assert_within_ulp(bits(raw_out), want_raw, "de-RoPE'd K", atol=1e-6)
+    if with_raw:
+        assert_within_ulp(bits(raw_out), want_raw, "de-RoPE'd K", atol=1e-6)
     assert_within_ulp(bits(idx), want_idx, "index (de-RoPE mode)", atol=1e-5)
 
 
