@@ -185,8 +185,8 @@ kvs_status kvs_slotmap_redirect(const int64_t* slot_in, const uint8_t* keep_mask
  * Mean-K index build -- KVMEM, section "Design and trade-offs ... Mean-K":
  * one mean of position-free K per block of `block` tokens, per layer and KV
  * head.  index[l,g,b,:] = bf16( (1/n_b) sum_{i in block b} k~[l,g,i,:] ),
- * summed in float32, rounded to nearest-even; a partial last block averages
- * its n_b < block tokens.
+ * summed in float32 from -0 (so a block of -0 keys averages to -0), rounded
+ * to nearest-even; a partial last block averages its n_b < block tokens.
  *   K        [L, H_kv, N, D] bf16.  k_is_rope = 0: K is raw (pre-RoPE) and k~ = K.
  *            k_is_rope = 1: K carries RoPE at positions pos0 + i (rotate-half
  *            pairs (i, i+D/2), omega_i = theta^(-2i/D)) and k~ is K rotated
