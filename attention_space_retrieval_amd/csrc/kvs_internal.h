@@ -14,10 +14,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
-// (layer, KV head) slices per workgroup: the re-RoPE scatter runs one wave per
-// slice (n_sel * ceil(L*H_kv / kScatterSlices) workgroups of kScatterThreads),
-// the working-set update two slices per wave of a 256-thread workgroup
-// (n_new * ceil(L*H_kv / kWorksetSlices) workgroups)
+// (layer, KV head) slices per workgroup, one wave per slice: the re-RoPE
+// scatter launches n_sel * ceil(L*H_kv / kScatterSlices) workgroups of
+// kScatterThreads, the working-set update n_new * ceil(L*H_kv / kWorksetSlices)
+// workgroups of 64 * kWorksetSlices threads
 constexpr int kScatterSlices = 16;
 constexpr int kScatterThreads = 64 * kScatterSlices;
 constexpr int kWorksetSlices = 8;
