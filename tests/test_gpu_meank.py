@@ -376,8 +376,9 @@ def _block_rows(blocks):
 
 @pytest.mark.parametrize("D,pos_base,with_v,identity,L,H_kv", [
     (128, 0, True, False, 2, 3), (128, 1000000, True, True, 2, 3), (64, 77, False, False, 2, 3),
-    (128, 4321, True, False, 4, 5),     # 20 (layer, KV head) slices: chunks of 8, 8 and 4
-    (64, 0, True, True, 2, 8),          # 16 slices: two whole chunks
+    (128, 4321, True, False, 4, 5),     # 20 (layer, KV head) slices: chunks of 16 and 4
+    (64, 0, True, True, 2, 8),          # 16 slices: one whole chunk
+    (64, 999, True, False, 3, 11),      # 33 slices: chunks of 16, 16 and 1
 ])
 def test_rerope_scatter(D, pos_base, with_v, identity, L, H_kv):
     n_src_blocks, pool_pages, n_sel, theta = 20, 12, 7, 1e6
