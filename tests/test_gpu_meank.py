@@ -83,7 +83,8 @@ def test_meank_build_bf16_rounding_special_values():
 
 @pytest.mark.parametrize("D,pos0,L,H_kv,with_raw", [
     (128, 0, 2, 2, True), (128, 1000000 - 640, 2, 2, True), (64, 12345, 2, 2, True),
-    (128, 777, 3, 7, True), (64, 777, 3, 7, False),      # 21 slices: two chunks of 16, the second ragged
+    # 21 slices: with raw K out, two chunks of 16 (the second ragged); index only, one workgroup per block
+    (128, 777, 3, 7, True), (64, 777, 3, 7, False),
 ])
 def test_meank_build_derope(D, pos0, L, H_kv, with_raw):
     N, theta = 640 + 17, 1e6
