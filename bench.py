@@ -42,7 +42,7 @@ WORKLOADS = {"rule-8b+meank-256k": ("rule-8b", "meank-256k"),
              "rule-14b+meank-1m": ("rule-14b", "meank-1m")}
 # kernels each call launches (rocprofv3 short names); a tuple lists alternatives of which the
 # call launches one, chosen by the sizes (the window score's first pass runs two-wave workgroups
-# for windows of at most 128 rows per KV group)
+# for windows of at most 128 rows per KV group; its second pass always does)
 CALL_KERNELS = {
     "kvs_qmem_update": ["qmem_kernel<128, true>"],
     "kvs_rule_score": ["rule_logits_mfma<128, 1, false>", "rule_lse_merge", "rule_colsum"],
@@ -56,7 +56,7 @@ CALL_KERNELS = {
     # dense call's kernels on the same sizes
     "kvs_rule_score_paged": ["rule_logits_mfma<128, 1, true>", "rule_lse_merge", "rule_colsum"],
     "kvs_window_score": [("meank_pass<true, true, 2>", "meank_pass<true, true, 4>"), "meank_lse_merge",
-                         "meank_pass<false, true, 4>",
+                         "meank_pass<false, true, 2>",
                          "meank_reduce<true>"],
     "kvs_meank_append": ["meank_append_kernel<128>"],
     "kvs_working_set_update": ["workset_diff", "workset_apply<128, true>"],
