@@ -117,6 +117,29 @@ def test_meank_build_full_size_sampled():
     del K
 
 
+def test_meank_build_derope_full_size_sampled():
+    """meank-256k read as post-RoPE keys, in both de-RoPE launch layouts: sampled blocks against the
+    oracle (index and RoPE-free keys), and the index-only layout equal to the written-out one bit
+    for bit (both sum each block in the same order)."""
+    c = W.config("meank-256k")
+    K = W.normal((c["L"], c["H_kv"], c["N"], c["D"]), c["seed"], W.T_K, "bf16", DEV)
+    raw = torch.empty_like(K)
+    idx = kvs.kvs_meank_build(K, k_is_rope=True, pos0=0, theta=1e6, raw_k_out=raw)
+    idx_only = kvs.kvs_meank_build(K, k_is_rope=True, pos0=0, theta=1e6)
+    torch.cuda.synchronize()
+    assert torch.equal(idx.view(torch.int16), idx_only.view(torch.int16))
+    r = np.random.default_rng(6)
+    nB = c["N"] // 32
+    for _ in range(32):
+        l, g, b = int(r.integers(c["L"])), int(r.integers(c["H_kv"])), int(r.integers(nB))
+        blk = host(K[l, g, 32 * b:32 * b + 32])[None, None]
+        want_idx, want_raw = oracle.meank_build(blk, k_is_rope=True, pos0=32 * b, theta=1e6)
+        assert_within_ulp(bits(idx[l, g, b])[None, None, None], want_idx, f"index block {(l, g, b)}", atol=1e-5)
+        assert_within_ulp(bits(raw[l, g, 32 * b:32 * b + 32])[None, None], want_raw, f"raw block {(l, g, b)}",
+                          atol=1e-6)
+    del K, raw
+
+
 # ---------------------------------------------------------------- incremental append (stage-out)
 
 def _append_case(L, H_kv, D, cap, chunks, pos0, seed):
