@@ -5,10 +5,12 @@
 //
 // W_t (new_blocks) and G_{t-1} (prev_blocks, with their pages) are ascending
 // block ids; a block's compact index is its rank.  Classes:
-//   retained  (in both)      keeps its page; if its rank moved by dr its K,
-//                            RoPE'd at the old positions, is rotated in place by
-//                            the position delta 32 dr (RoPE(p+d) = RoPE(d) RoPE(p)),
-//                            so it needs no raw-K transfer; V is untouched.
+//   retained  (in both)      keeps its page; if its rank moved, its K is rebuilt
+//                            from raw K (the reconstruction authority) at the new
+//                            positions, like an incoming block; V is untouched.
+//                            This moves the same bytes as rotating the pool's copy
+//                            by the position delta, without rounding the block to
+//                            bf16 once more per move (no drift over many steps).
 //   incoming  (W_t only)     takes a free page -- one no retained block holds,
 //                            free pages in ascending order to incoming blocks in
 //                            ascending rank -- and is written like the re-RoPE
@@ -16,7 +18,8 @@
 //   outgoing  (G_{t-1} only) releases its page.
 // Two kernels: workset_diff (one workgroup: binary searches, block-wide
 // scans, the new page table) and workset_apply (one workgroup per selected
-// block and chunk of slices: in-place rotation, scatter, or nothing).
+// block and chunk of slices: re-RoPE from raw K, V copy for incoming blocks,
+// or nothing for a block retained at the same rank).
 #include "rope_table.h"
 
 using namespace kvs;
@@ -163,10 +166,9 @@ __global__ __launch_bounds__(64 * kWorksetSlices, 2) void workset_apply(
   const int32_t rank = old_rank[r];
   const int64_t page = pages[r];
   if (page < 0 || page >= pool_pages || rank == r) return;      // rejected input, or retained in place
-  const bool moved = rank >= 0;
+  const bool moved = rank >= 0;                                 // retained, rank changed: V stays
   const int64_t sb = new_blocks[r];
-  // moved: one row of the table, the angle of the position delta; incoming: the block's positions
-  build_rope_table<D>(tab, moved ? (int64_t)kBlk * (r - rank) : pos_base + (int64_t)kBlk * r, log2_theta);
+  build_rope_table<D>(tab, pos_base + (int64_t)kBlk * r, log2_theta);
   __syncthreads();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int cl = lane % LPR, rr = lane / LPR;
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(64 * kWorksetSlices, 2) void workset_apply(
   for (int lg = chunk * kWorksetSlices + wave; lg < lg_end; lg += kWorksetSlices) {
     const size_t d0 = ((size_t)lg * pool_tokens + (size_t)page * kBlk) * D;
     const size_t s0 = ((size_t)lg * src_tokens + (size_t)sb * kBlk) * D;
-    const auto kin = buf_rsrc(moved ? k_pool + d0 : k_src + s0, kBlkBytes);
+    const auto kin = buf_rsrc(k_src + s0, kBlkBytes);
     const auto kd = buf_rsrc(k_pool + d0, kBlkBytes);
     asm volatile("" ::: "memory");   // table reads stay in the loop (held across it they cost 128 VGPRs)
     u32x4 w[LOADS], vv[LOADS];
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(64 * kWorksetSlices, 2) void workset_apply(
     for (int ld = 0; ld < LOADS; ++ld) {
       float x[8];
       unpack8(w[ld], x);
-      rotate8<D>(x, tab[moved ? 0 : ld * RPL + rr], cl, +1);
+      rotate8<D>(x, tab[ld * RPL + rr], cl, +1);
       buf_store16(pack8(x), kd, lane_off + ld * kGroupBytes);   // whole offset per lane (see buf_store16)
     }
     if constexpr (WITH_V) {

@@ -286,9 +286,12 @@ size_t kvs_working_set_workspace(int64_t pool_pages);
  * prev_blocks (G_{t-1}, the blocks the pool holds, with their pages) and
  * new_blocks (W_t) are strictly ascending block ids; a block's compact index
  * r is its rank, so it sits at positions pos_base + 32r .. +31.
- *   retained  keeps its page.  If its rank moved from r_old to r, its K
- *             (RoPE'd at the old positions) is rotated in place by the
- *             position delta 32 (r - r_old); V is untouched.
+ *   retained  keeps its page.  If its rank moved, its K is rebuilt from raw
+ *             K (the reconstruction authority) at its new positions, exactly
+ *             as kvs_rerope_scatter writes it; V is untouched.  A retained
+ *             block whose rank did not move is not touched at all, so pos_base
+ *             must be the value the pool was last written with (a caller that
+ *             shifts pos_base re-scatters the whole selection instead).
  *   incoming  takes a free page (one no retained block holds; free pages in
  *             ascending order go to incoming blocks in ascending rank) and is
  *             written like kvs_rerope_scatter: raw K rotated to its compact

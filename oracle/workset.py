@@ -13,9 +13,13 @@ Readings (the difference equation itself was lost in extraction):
   previous step) are ascending block ids; a block's compact index is its rank
   in that list, so block r of the view sits at positions pos_base + 32 r ... +31.
 * retained = W_t and G_{t-1}: the block keeps its physical page.  If its
-  compact index moved by dr, its pool K (RoPE'd at the old positions) is
-  rotated in place by the position delta 32 dr (RoPE(p + d) = RoPE(d) RoPE(p)),
-  which needs no raw K transfer; V is untouched.
+  compact index moved, its K is rebuilt from raw K (the page's reconstruction
+  authority) at the new positions pos_base + 32 r ... +31, exactly as the
+  re-RoPE scatter writes it; V carries no position and is untouched.  (Rotating
+  the pool's bf16 copy by the position delta instead would round once more per
+  move, so a block that moves over many steps would drift away from raw K.)
+  pos_base is the same in consecutive steps: a retained block whose compact
+  index did not move is left as it is.
 * incoming = W_t minus G_{t-1}: takes a free page (a page no retained block
   holds), the free pages handed out in ascending page order to the incoming
   blocks in ascending compact order, and is written like the re-RoPE scatter:
@@ -69,13 +73,11 @@ def working_set_update(k_src, v_src, prev_blocks, prev_pages, new_blocks, pos_ba
     v_out = np.array(v_pool, copy=True)
     for r, b in enumerate(new_blocks):
         rows = slice(int(pages[r]) * block, (int(pages[r]) + 1) * block)
-        if old_rank[r] >= 0:
-            delta = block * (r - int(old_rank[r]))
-            if delta != 0:
-                k_out[:, :, rows, :] = rope_rotate(as_f64(k_pool[:, :, rows, :]), np.full(block, delta), theta)
-        else:
-            src = slice(int(b) * block, (int(b) + 1) * block)
-            pos = pos_base + block * r + np.arange(block)
-            k_out[:, :, rows, :] = rope_rotate(as_f64(k_src[:, :, src, :]), pos, theta)
+        if old_rank[r] == r:
+            continue                                  # retained at the same compact index
+        src = slice(int(b) * block, (int(b) + 1) * block)
+        pos = pos_base + block * r + np.arange(block)
+        k_out[:, :, rows, :] = rope_rotate(as_f64(k_src[:, :, src, :]), pos, theta)
+        if old_rank[r] < 0:                           # incoming: V copied; a moved block's V stays
             v_out[:, :, rows, :] = v_src[:, :, src, :]
     return k_out, v_out, pages, old_rank, outgoing

@@ -624,21 +624,57 @@ def test_working_set_full_shape_sampled():
     np.testing.assert_array_equal(pages.cpu().numpy(), pages_o)
     np.testing.assert_array_equal(rank.cpu().numpy(), rank_o)
     np.testing.assert_array_equal(outgoing[:int(counts[2].item())].cpu().numpy(), out_o)
-    # every selected page: moved blocks are their old page rotated, incoming ones raw K rotated
-    inc = torch.from_numpy(np.flatnonzero(rank_o < 0)).to(DEV)
-    mov = torch.from_numpy(np.flatnonzero(rank_o >= 0)).to(DEV)
+    # every selected page: incoming and moved blocks are raw K rotated to the new rank's positions,
+    # blocks retained at their rank keep their page bit for bit
+    ranks = np.arange(len(new))
+    fresh_r = torch.from_numpy(np.flatnonzero(rank_o != ranks)).to(DEV)
+    same_r = torch.from_numpy(np.flatnonzero(rank_o == ranks)).to(DEV)
     pg = torch.from_numpy(pages_o.astype(np.int64)).to(DEV)
-    check_rotated_rows(k_src, _block_rows(i32(new)[inc]), k_pool, _block_rows(pg[inc]), "incoming blocks")
-    check_rotated_rows(k_init, _block_rows(pg[mov]), k_pool, _block_rows(pg[mov]), "retained blocks")
-    for i in r.choice(len(new), 24, replace=False):
-        l, g, p = int(r.integers(L)), int(r.integers(H_kv)), int(pages_o[i])
+    assert (rank_o >= 0).sum() > len(same_r) > 0
+    check_rotated_rows(k_src, _block_rows(i32(new)[fresh_r]), k_pool, _block_rows(pg[fresh_r]),
+                       "incoming and moved blocks")
+    check_copied_rows(k_init, _block_rows(pg[same_r]), k_pool, _block_rows(pg[same_r]), "blocks retained at their rank")
+    for i in r.choice(np.flatnonzero(rank_o != ranks), 24, replace=False):
+        l, g, p, b = int(r.integers(L)), int(r.integers(H_kv)), int(pages_o[i]), int(new[i])
         rows = slice(32 * p, 32 * p + 32)
-        if rank_o[i] >= 0:
-            want = oracle.rope_rotate(oracle.bf16_bits_to_f64(host(k_init[l, g, rows])),
-                                      np.full(32, 32 * (i - rank_o[i])), 1e6)
-        else:
-            b = int(new[i])
-            want = oracle.rope_rotate(oracle.bf16_bits_to_f64(host(k_src[l, g, 32 * b:32 * b + 32])),
-                                      32 * i + np.arange(32), 1e6)
-        assert_within_ulp(bits(k_pool[l, g, rows]), want, f"page {p} (rank {i})", atol=1e-6)
+        want = oracle.rope_rotate(oracle.bf16_bits_to_f64(host(k_src[l, g, 32 * b:32 * b + 32])),
+                                  32 * i + np.arange(32), 1e6)
+        assert_within_ulp(bits(k_pool[l, g, rows]), want, f"page {p} (rank {i}, old rank {rank_o[i]})", atol=1e-6)
     del k_src, k_pool, k_init
+
+
+def test_working_set_chain_of_updates():
+    """Eight updates in a row on one pool: every page of the final selection holds what one re-RoPE
+    scatter of that selection from raw K writes (bit for bit against the library's scatter, within
+    1 ulp + 1e-6 of the oracle), however often its block moved; nothing drifts."""
+    L, H_kv, D, src_blocks, pool, pos_base, theta = 2, 5, 128, 200, 64, 32 * 7, 1e6
+    r = np.random.default_rng(66)
+    k_src = W.normal((L, H_kv, 32 * src_blocks, D), 67, W.T_K, "bf16", DEV, scale=4.0)
+    v_src = W.normal((L, H_kv, 32 * src_blocks, D), 67, W.T_V, "bf16", DEV)
+    k_pool = torch.zeros((L, H_kv, 32 * pool, D), dtype=torch.bfloat16, device=DEV)
+    v_pool = torch.zeros_like(k_pool)
+    i32 = lambda a: torch.tensor(np.asarray(a), dtype=torch.int32, device=DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    prev, prev_pages, n_moved = [], [], 0
+    for step in range(8):
+        keep = [b for b in prev if r.random() < 0.75]
+        new = sorted(set(keep) | set(r.choice(src_blocks, 20, replace=False).tolist()))[:48]
+        pages, rank, _, _ = kvs.kvs_working_set_update(k_src, v_src, i32(prev), i32(prev_pages), i32(new), pos_base,
+                                                       theta, k_pool, v_pool, err_flag=err)
+        torch.cuda.synchronize()
+        rk = rank.cpu().numpy()
+        n_moved += int(((rk >= 0) & (rk != np.arange(len(new)))).sum())
+        prev, prev_pages = new, pages.cpu().numpy().tolist()
+    assert int(err.item()) == 0 and n_moved >= 16
+    k_ref, v_ref = torch.zeros_like(k_pool), torch.zeros_like(v_pool)
+    kvs.kvs_rerope_scatter(k_src, v_src, i32(prev), i32(prev_pages), len(prev), pos_base, theta, k_ref, v_ref)
+    torch.cuda.synchronize()
+    rows = _block_rows(i32(prev_pages))
+    check_copied_rows(k_ref, rows, k_pool, rows, "K after a chain of updates vs one scatter")
+    check_copied_rows(v_ref, rows, v_pool, rows, "V after a chain of updates vs one scatter")
+    ko, _ = oracle.rerope_scatter(host(k_src), host(v_src), prev, prev_pages, pos_base, theta,
+                                  np.zeros(k_pool.shape), np.zeros(k_pool.shape, dtype=np.uint16))
+    kp = bits(k_pool)
+    for p in prev_pages:
+        sl = slice(32 * p, 32 * p + 32)
+        assert_within_ulp(kp[:, :, sl], ko[:, :, sl], f"page {p} after the chain", atol=1e-6)

@@ -487,8 +487,10 @@ def test_workset_empty_previous_is_the_scatter():
 
 
 def test_workset_moved_blocks_match_rope_at_new_position():
-    # A retained block rotated by its position delta must equal raw K RoPE'd at the new
-    # compact position: catches a wrong sign of the delta or a delta in blocks, not tokens.
+    # A retained block whose compact index moved must equal raw K RoPE'd at the new compact
+    # position (KVMEM, "Engineering and cost ...": raw K is the reconstruction authority):
+    # catches a block left at its old positions, a rotation by the delta in blocks rather
+    # than tokens, or the wrong sign.
     r = rng(511)
     raw_k, raw_v = r.standard_normal((1, 2, 32 * 30, 32)), r.standard_normal((1, 2, 32 * 30, 32))
     prev, prev_pages = [2, 3, 7, 10, 15, 21], [5, 0, 7, 2, 9, 4]
@@ -500,6 +502,38 @@ def test_workset_moved_blocks_match_rope_at_new_position():
         rows = slice(32 * p, 32 * p + 32)
         np.testing.assert_allclose(k[:, :, rows], want_k[:, :, rows], atol=1e-10)
         np.testing.assert_array_equal(v[:, :, rows], want_v[:, :, rows])
+
+
+def test_workset_chain_of_updates_has_no_drift():
+    # Several steps in a row, the pool rounded to bf16 after each one as the library stores it:
+    # the final pool equals one re-RoPE scatter of the final selection from raw K onto the final
+    # pages, bit for bit.  Rotating a moved block's stored bf16 copy by its position delta would
+    # round once more per move and fail this.
+    r = rng(513)
+    L, H, D, src_blocks, pool, pos_base, theta = 1, 2, 16, 60, 24, 0, 1e6
+    raw_k = oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(r.standard_normal((L, H, 32 * src_blocks, D)) * 4))
+    raw_v = oracle.f64_to_bf16_bits(r.standard_normal((L, H, 32 * src_blocks, D)))
+    prev = sorted(r.choice(src_blocks, 12, replace=False).tolist())
+    prev_pages = r.permutation(pool)[:12].tolist()
+    k, v = oracle.rerope_scatter(raw_k, raw_v, prev, prev_pages, pos_base, theta, np.zeros((L, H, 32 * pool, D)),
+                                 np.zeros((L, H, 32 * pool, D), np.uint16))
+    k = oracle.f64_to_bf16_bits(k)
+    n_moved = 0
+    for step in range(8):
+        keep = [b for b in prev if r.random() < 0.7]
+        new = sorted(set(keep) | set(r.choice(src_blocks, 6, replace=False).tolist()))[:16]
+        kf, v, pages, old_rank, _ = oracle.working_set_update(raw_k, raw_v, prev, prev_pages, new, pos_base, theta,
+                                                              k, v)
+        k = oracle.f64_to_bf16_bits(kf)
+        n_moved += sum(1 for i, rr in enumerate(old_rank) if rr >= 0 and rr != i)
+        prev, prev_pages = new, pages.tolist()
+    assert n_moved >= 8
+    ks, vs = oracle.rerope_scatter(raw_k, raw_v, prev, prev_pages, pos_base, theta, np.zeros((L, H, 32 * pool, D)),
+                                   np.zeros((L, H, 32 * pool, D), np.uint16))
+    for p in prev_pages:
+        rows = slice(32 * p, 32 * p + 32)
+        np.testing.assert_array_equal(k[:, :, rows], oracle.f64_to_bf16_bits(ks[:, :, rows]))
+        np.testing.assert_array_equal(v[:, :, rows], vs[:, :, rows])
 
 
 def test_workset_classes_pages_and_untouched_rows():
