@@ -5,7 +5,12 @@ score, top-k with the forced set, slot redirect) followed by a KVMEM agent step
 on the Mean-K workspace (index build from raw K, block scoring, sink/recent +
 budget selection, re-RoPE scatter of the selected K/V blocks into the pool).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload rule-8b+meank-256k]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload rule-14b+meank-1m]
+
+The default workload is the largest that fits one GPU: the 14B-shaped rule
+cache (N = 92160, IntentKV's worst case) and the 1M-token Mean-K workspace
+(32768 blocks, budget 4096, scatter from a packed staging buffer through a page
+table).  rule-8b+meank-256k is the smaller pair.
 
 Prints one JSON line.  `value` counts K-cache tokens scored per second over the
 whole step (the rule cache's N plus the Mean-K workspace's N).  Per-call times
@@ -38,11 +43,18 @@ from attention_space_retrieval_amd import kvs, workloads as W  # noqa: E402
 METRIC = "K-cache tokens scored/s + HBM GB/s (rule+top-k); Mean-K scoring TFLOP/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+# Sustained rate of R_b's instruction mix (bf16 MFMA 32x32x16 with one fma + exp2 + add per logit
+# interleaved) in a register-only loop over all 256 CUs at 4-16 waves per SIMD: 1.51-1.57 PFLOP/s,
+# against ~1.96 PFLOP/s for the MFMAs alone (the clock does not hold 2.4 GHz under either load).
+MIX_CEILING_TFLOPS = 1570.0
 WORKLOADS = {"rule-8b+meank-256k": ("rule-8b", "meank-256k"),
              "rule-14b+meank-1m": ("rule-14b", "meank-1m")}
 # kernels each call launches (rocprofv3 short names); a tuple lists alternatives of which the
 # call launches one, chosen by the sizes (the window score's first pass runs two-wave workgroups
-# for windows of at most 128 rows per KV group; its second pass always does)
+# for windows of at most 128 rows per KV group; its second pass always does); "name*k" is a kernel
+# the call launches k times.  Top-k runs one register-resident workgroup up to 8192 or 32768
+# scores and the multi-workgroup path above that (rule-14b's 92160).
+TOPK_MW = ["topk_mw_init", "topk_mw_minmax", "topk_mw_pass*4", "topk_mw_count", "topk_mw_emit"]
 CALL_KERNELS = {
     "kvs_qmem_update": ["qmem_kernel<128, true>"],
     "kvs_rule_score": ["rule_logits_mfma<128, 1, false>", "rule_lse_merge", "rule_colsum"],
@@ -61,6 +73,18 @@ CALL_KERNELS = {
     "kvs_meank_append": ["meank_append_kernel<128>"],
     "kvs_working_set_update": ["workset_diff", "workset_apply<128, true>"],
 }
+
+
+def call_kernels(workload):
+    """CALL_KERNELS with the top-k kernels the workload's sizes select."""
+    ck = dict(CALL_KERNELS)
+    if workload == "rule-14b+meank-1m":
+        ck["kvs_topk_select[rule]"] = TOPK_MW                       # n = 92160
+        ck["kvs_topk_select[meank]"] = ["topk_reg_kernel<32>"]      # n = 32768 blocks
+        # the 1M workspace keeps no V beside raw K (the scatter reads the packed staging buffers), so
+        # the working-set update there moves K only
+        ck["kvs_working_set_update"] = ["workset_diff", "workset_apply<128, false>"]
+    return ck
 
 
 def log(*a):
@@ -254,15 +278,19 @@ def measured_traffic(workload):
     with open(path) as f:
         summ = json.load(f)["kernels"]
     out = {}
-    for call, kernels in CALL_KERNELS.items():
+    for call, kernels in call_kernels(workload).items():
         total = 0.0
         for k in kernels:
             alts = k if isinstance(k, tuple) else (k,)   # alternatives share one source file
+            times = 1
+            if len(alts) == 1 and "*" in alts[0]:
+                name, n = alts[0].rsplit("*", 1)
+                alts, times = (name,), int(n)
             e = next((summ[n] for n in alts if n in summ), None)
             if e is None or e["source_sha256"] != rs.source_hash(rs.base_name(alts[0])):
                 total = None
                 break
-            total += e["read_bytes_mean"] + e["write_bytes_mean"]
+            total += times * (e["read_bytes_mean"] + e["write_bytes_mean"])
         out[call] = total
     return out
 
@@ -300,23 +328,50 @@ def run_gpu(s, steps, warmup, only=None):
     return wall, per_call, spread
 
 
+def host_info():
+    """Host cores, CPU model and the NumPy / BLAS build the oracle runs on."""
+    info = {"os_cpu_count": os.cpu_count()}
+    try:
+        info["affinity_cpus"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):                    # pragma: no cover
+        info["affinity_cpus"] = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            info["cpu_model"] = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:                                      # pragma: no cover
+        info["cpu_model"] = None
+    info["numpy"] = np.__version__
+    info["blas"] = None
+    info["blas_threads"] = 1
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if libs:
+            b = max(libs, key=lambda p: p.get("num_threads", 1))
+            info["blas"] = f"{b.get('internal_api')} {b.get('version')} ({os.path.basename(b.get('filepath', ''))})"
+            info["blas_threads"] = int(b.get("num_threads", 1))
+    except Exception:                                    # pragma: no cover
+        pass
+    return info
+
+
 def cpu_baseline(s):
     """The float64 oracle on a bounded sample of the same inputs, scaled to one step."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"), default=1)
-    except Exception:                                    # pragma: no cover
-        blas = 1
+    hi = host_info()
+    blas = hi["blas_threads"]
 
     def bits(t):
         return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
     c, m = s.rc, s.mc
+    # about 15-30 s of oracle work on a 16-core host at either workload
+    big = m["N"] > (1 << 19)
     L_r = min(8, c["L"])
-    lg_m = 48
+    lg_m = 16 if big else 48
     blocks = 256
     t = {}
+    t_sample = time.perf_counter()
     K = bits(s.K[:L_r])
     Mo = None
     for q in s.spans[:-1]:                               # the oracle's own session state
@@ -363,7 +418,9 @@ def cpu_baseline(s):
         "sample": (f"float64 oracle on the same input bits: rule score over {L_r} of {c['L']} layers, "
                    f"Mean-K build and score over {lg_m} of {LG} (layer, KV head) pairs, re-RoPE scatter of "
                    f"{blocks} of {s.n_sel} blocks on {lg_m} pairs; each part scaled linearly to the full step "
-                   f"({step:.1f} s extrapolated). BLAS threads = cores; elementwise numpy is single-threaded."),
+                   f"({step:.1f} s extrapolated from {time.perf_counter() - t_sample:.1f} s of sampling). "
+                   f"cores = the BLAS threads the float64 products use; elementwise numpy is single-threaded."),
+        "host": hi,
         "seconds_per_step_extrapolated": step,
         "parts_s": {k: round(v, 3) for k, v in t.items()},
     }
@@ -374,7 +431,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="rule-8b+meank-256k", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="rule-14b+meank-1m", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
                     help="comma-separated call names to time alone (profiling; not a headline figure). "
@@ -462,13 +519,22 @@ def main():
                    "meank": {k: m[k] for k in ("L", "H_q", "H_kv", "D", "N", "Mq", "n_sink", "n_recent", "budget", "theta")},
                    "tokens_per_step": tokens},
         "roofline": {"call": dom, "kernels": " + ".join(k if isinstance(k, str) else " | ".join(k)
-                                                         for k in CALL_KERNELS.get(dom, [dom])), "bound": d["bound"],
+                                                         for k in call_kernels(a.workload).get(dom, [dom])),
+                     "bound": d["bound"],
                      "achieved": d["achieved"], "peak": d["peak"], "unit": d["unit"], "frac": d["frac"],
                      "per_launch": d["per_launch"], "traffic": d["traffic"]},
         "rule_turn": {"ms": round(rule_ms, 4), "tokens_per_s": c["N"] / (rule_ms * 1e-3),
                       "hbm_gbps": rule_bytes / (rule_ms * 1e-3) / 1e9,
                       "frac_hbm_peak": rule_bytes / (rule_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "meank_score_tflops": rows["kvs_meank_score"]["achieved"],
+        # the exact R_b runs two passes over the same tiles (row normalisers, then column sums), so
+        # it executes twice the algorithmic flops; the mix ceiling is the rate a register-only loop
+        # of the same MFMA 32x32x16 + exp2 epilogue mix sustains on all 256 CUs
+        "meank_score_executed": {
+            "tflop_per_call": 2 * work["kvs_meank_score"][1] / 1e12,
+            "tflops": round(2 * rows["kvs_meank_score"]["achieved"], 2),
+            "mix_ceiling_tflops": MIX_CEILING_TFLOPS,
+            "frac_of_mix_ceiling": round(2 * rows["kvs_meank_score"]["achieved"] / MIX_CEILING_TFLOPS, 4)},
         "calls": rows,
         "next_rows": next_rows,
     }

@@ -569,6 +569,76 @@ def test_workset_classes_pages_and_untouched_rows():
     assert out.tolist() == [0] and pages.tolist() == [3, 1, 0]
 
 
+def _meank_select_brute(R, n_sink, n_recent, budget, free_pages, pos_base):
+    """KVMEM, "Design and trade-offs ... Mean-K": the sink and recent blocks are always kept and the
+    rest of the budget goes to the blocks of largest R_b; the selection is laid out in ascending block
+    order ("Engineering and cost ...": compact logical order), logical block r on the r-th free page
+    (page r when there is no free list) at positions pos_base + 32 r ... +31.  Written as an exhaustive
+    search: among all candidate subsets of the remaining budget, the one of largest R sum, the
+    lexicographically smallest among equals."""
+    nB = len(R)
+    forced = [b for b in range(nB) if b < n_sink or b >= nB - n_recent]
+    cand = [b for b in range(nB) if b not in forced]
+    k = min(max(0, budget - len(forced)), len(cand))
+    best = None
+    for comb in itertools.combinations(cand, k):
+        key = (-sum(R[b] for b in comb), comb)
+        if best is None or key < best:
+            best = key
+    keep = sorted(forced + list(best[1]))
+    dst = [free_pages[r] if free_pages is not None else r for r in range(len(keep))]
+    return keep, dst, [pos_base + 32 * r for r in range(len(keep))]
+
+
+def _meank_select_cases():
+    r = rng(520)
+    for trial in range(60):
+        nB = int(r.integers(1, 15))
+        R = (r.integers(0, 5, size=nB) / 4.0).tolist()             # exact ties
+        n_sink, n_recent = int(r.integers(0, 4)), int(r.integers(0, 5))  # sink and recent may overlap
+        budget = int(r.integers(0, nB + 3))
+        free = r.permutation(nB + 6).tolist() if trial % 2 else None
+        yield R, n_sink, n_recent, budget, free, int(r.integers(0, 5000))
+
+
+def _check_meank_select(select):
+    """Every case against the brute force, plus the properties the page fixes."""
+    for R, n_sink, n_recent, budget, free, pos_base in _meank_select_cases():
+        keep, dst, pos = select(np.array(R), n_sink, n_recent, budget, free, pos_base)
+        want = _meank_select_brute(R, n_sink, n_recent, budget, free, pos_base)
+        assert [list(map(int, keep)), list(map(int, dst)), list(map(int, pos))] == [list(w) for w in want], \
+            (R, n_sink, n_recent, budget, free, pos_base)
+        nB = len(R)
+        forced = {b for b in range(nB) if b < n_sink or b >= nB - n_recent}
+        assert forced <= set(int(b) for b in keep)
+        assert len(keep) == len(forced) + min(max(0, budget - len(forced)), nB - len(forced))
+        assert all(a < b for a, b in zip(keep, keep[1:]))
+
+
+def test_meank_select_brute_force_page_table_and_positions():
+    _check_meank_select(lambda R, s, rc, b, fp, pb: oracle.meank_select(R, s, rc, b, fp, pb))
+
+
+def _select_variant(R, n_sink, n_recent, budget, free, pos_base, recent=True, inclusive=True, pages=True,
+                    shift=0):
+    """meank_select with one deliberate mistake (for the test below)."""
+    nB = len(R)
+    f1 = (nB - n_recent, nB) if recent else (nB, nB)
+    n_forced = len(set(range(min(n_sink, nB))) | set(range(max(0, nB - n_recent), nB)))
+    _, keep, nk = oracle.topk_select(R, (0, n_sink), f1, budget if inclusive else budget + n_forced)
+    dst = np.asarray(free)[:nk] if (free is not None and pages) else np.arange(nk)
+    return keep, dst, pos_base + 32 * (np.arange(nk) + shift)
+
+
+@pytest.mark.parametrize("mistake", [dict(recent=False), dict(inclusive=False), dict(pages=False), dict(shift=1)])
+def test_meank_select_pin_catches_planted_mistakes(mistake):
+    # recent blocks not forced; budget read as excluding the sink and recent blocks; the free list
+    # ignored; positions one block off.  The pin must reject each, and accept the unchanged variant.
+    _check_meank_select(lambda *a: _select_variant(*a))
+    with pytest.raises(AssertionError):
+        _check_meank_select(lambda *a: _select_variant(*a, **mistake))
+
+
 def test_meank_planted_evidence_is_selected():
     # Blocks whose raw K is shifted along a direction the queries share must win.
     r = rng(506)
