@@ -43,6 +43,24 @@ void clip_range(int64_t n, int64_t& b, int64_t& e) {
   e = e < b ? b : (e > n ? n : e);
 }
 
+// Argument checks shared by the two top-k entry points; clips the forced
+// ranges and gives |F| and C*.
+kvs_status topk_args(const float* score, int64_t n, int64_t& f0_begin, int64_t& f0_end, int64_t& f1_begin,
+                     int64_t& f1_end, int64_t C, const uint8_t* keep_mask, const int32_t* keep_idx,
+                     const int64_t* n_kept, int64_t* n_forced, int64_t* c_star) {
+  if (!n_kept || (n > 0 && (!score || !keep_mask || !keep_idx))) return KVS_ERR_ARG;
+  if (n < 0 || C < 0 || f0_end < f0_begin || f1_end < f1_begin) return KVS_ERR_ARG;
+  if (n > kMaxIndex) return KVS_ERR_SHAPE;
+  clip_range(n, f0_begin, f0_end);
+  clip_range(n, f1_begin, f1_end);
+  const int64_t lo = f0_begin > f1_begin ? f0_begin : f1_begin;
+  const int64_t hi = f0_end < f1_end ? f0_end : f1_end;
+  const int64_t overlap = hi > lo ? hi - lo : 0;
+  *n_forced = (f0_end - f0_begin) + (f1_end - f1_begin) - overlap;
+  *c_star = C > *n_forced ? C - *n_forced : 0;
+  return KVS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -56,6 +74,7 @@ const char* kvs_status_string(kvs_status s) {
     case KVS_ERR_UNSUPPORTED: return "unsupported configuration";
     case KVS_ERR_WORKSPACE: return "workspace missing or too small";
     case KVS_ERR_HIP: return "HIP launch failed";
+    case KVS_ERR_LIMIT: return "size above the fixed limit of a no-allocation entry point";
     default: return "unknown status";
   }
 }
@@ -131,22 +150,30 @@ kvs_status kvs_topk_select(const float* score, int64_t n, int64_t f0_begin, int6
                            int64_t f1_begin, int64_t f1_end, int64_t C, uint8_t* keep_mask,
                            int32_t* keep_idx, int64_t* n_kept, void* ws, size_t ws_bytes,
                            void* stream) {
-  if (!n_kept || (n > 0 && (!score || !keep_mask || !keep_idx))) return KVS_ERR_ARG;
-  if (n < 0 || C < 0 || f0_end < f0_begin || f1_end < f1_begin) return KVS_ERR_ARG;
-  if (n > kMaxIndex) return KVS_ERR_SHAPE;
+  int64_t n_forced = 0, c_star = 0;
+  const kvs_status a = topk_args(score, n, f0_begin, f0_end, f1_begin, f1_end, C, keep_mask, keep_idx,
+                                 n_kept, &n_forced, &c_star);
+  if (a != KVS_OK) return a;
   const size_t need = kvs_topk_ws_bytes(n);
   if (need && ws && ws_bytes < need) return KVS_ERR_WORKSPACE;   // no workspace: one-workgroup path
   if (need && ((uintptr_t)ws & 3)) return KVS_ERR_ARG;
   if (!need) ws = nullptr;
-  clip_range(n, f0_begin, f0_end);
-  clip_range(n, f1_begin, f1_end);
-  const int64_t lo = f0_begin > f1_begin ? f0_begin : f1_begin;
-  const int64_t hi = f0_end < f1_end ? f0_end : f1_end;
-  const int64_t overlap = hi > lo ? hi - lo : 0;
-  const int64_t n_forced = (f0_end - f0_begin) + (f1_end - f1_begin) - overlap;
-  const int64_t c_star = C > n_forced ? C - n_forced : 0;
   return hip_status(kvs_launch_topk(score, n, f0_begin, f0_end, f1_begin, f1_end, n_forced, c_star,
                                     keep_mask, keep_idx, n_kept, ws, as_stream(stream)));
+}
+
+int64_t kvs_topk_noalloc_max(void) { return kvs_topk_noalloc_max_n(); }
+
+kvs_status kvs_topk_select_noalloc(const float* score, int64_t n, int64_t f0_begin, int64_t f0_end,
+                                   int64_t f1_begin, int64_t f1_end, int64_t C, uint8_t* keep_mask,
+                                   int32_t* keep_idx, int64_t* n_kept, void* stream) {
+  int64_t n_forced = 0, c_star = 0;
+  const kvs_status a = topk_args(score, n, f0_begin, f0_end, f1_begin, f1_end, C, keep_mask, keep_idx,
+                                 n_kept, &n_forced, &c_star);
+  if (a != KVS_OK) return a;
+  if (n > kvs_topk_noalloc_max_n()) return KVS_ERR_LIMIT;
+  return hip_status(kvs_launch_topk_noalloc(score, n, f0_begin, f0_end, f1_begin, f1_end, n_forced, c_star,
+                                            keep_mask, keep_idx, n_kept, as_stream(stream)));
 }
 
 kvs_status kvs_slotmap_redirect(const int64_t* slot_in, const uint8_t* keep_mask, int64_t N,

@@ -96,6 +96,12 @@ hipError_t kvs_launch_topk(const float* score, int64_t n, int64_t f0b, int64_t f
                            int64_t f1e, int64_t n_forced, int64_t c_star, uint8_t* keep_mask,
                            int32_t* keep_idx, int64_t* n_kept, void* ws, hipStream_t st);
 size_t kvs_topk_ws_bytes(int64_t n);
+// Same selection with the multi-workgroup state in the library's own static
+// device array (no workspace); n <= kvs_topk_noalloc_max_n().
+int64_t kvs_topk_noalloc_max_n();
+hipError_t kvs_launch_topk_noalloc(const float* score, int64_t n, int64_t f0b, int64_t f0e, int64_t f1b,
+                                   int64_t f1e, int64_t n_forced, int64_t c_star, uint8_t* keep_mask,
+                                   int32_t* keep_idx, int64_t* n_kept, hipStream_t st);
 
 hipError_t kvs_launch_slotmap(const int64_t* in, const uint8_t* mask, int64_t N, int64_t dead,
                               int64_t* out, hipStream_t st);

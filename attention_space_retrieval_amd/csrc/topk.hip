@@ -11,6 +11,8 @@
 // output ascending and hand the k ties to the lowest indices.  Up to 32768
 // scores the keys stay in registers for the whole selection; beyond that each
 // pass streams them from L2 in batches with all of a batch's loads in flight.
+#include <mutex>
+
 #include "kvs_internal.h"
 
 using namespace kvs;
@@ -686,6 +688,74 @@ hipError_t kvs_launch_topk(const float* score, int64_t n, int64_t f0b, int64_t f
     hipLaunchKernelGGL(topk_mw_emit, grid, block, 0, st, a, keep_mask, keep_idx);
   }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Top-k that allocates nothing, for callers that cannot allocate (code under
+// HIP graph capture, tight serving loops, harnesses that forbid it).  The
+// multi-workgroup selection keeps its state (key range, radix prefix, arrival
+// ticket, histogram, per-slice counts) in `scratch`, a file-scope device
+// array sized for kvs_topk_noalloc_max_n() scores, instead of a caller
+// workspace.  Each device holds its own copy at its own address from the
+// first call on that device until the process ends, and every call on a
+// device shares it: calls that overlap on one device race.  Nothing carries
+// over between calls -- topk_mw_init rewrites every state word the later
+// kernels read, and each slice writes its counts before any slice reads them.
+constexpr int64_t kNoAllocMaxN = (int64_t)1 << 24;
+constexpr int kNoAllocWords = kMwCounts + 2 * (int)((kNoAllocMaxN + kMwSlice - 1) / kMwSlice);
+
+static __device__ __align__(256) uint32_t scratch[kNoAllocWords];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint32_t* g_scratch[kMaxDevices];   // device address of `scratch` on each device, once resolved
+
+// Device address of `scratch` on the device that runs stream st.  In host code
+// the array's name is only a host-side handle: the address the kernels take
+// comes from hipGetSymbolAddress, resolved once per device with that device
+// current, and kept.
+hipError_t scratch_for(hipStream_t st, uint32_t** out) {
+  int cur = 0, dev = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  dev = cur;
+  if (st != nullptr) {
+    e = hipStreamGetDevice(st, &dev);
+    if (e != hipSuccess) return e;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = static_cast<uint32_t*>(p);
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+int64_t kvs_topk_noalloc_max_n() { return kNoAllocMaxN; }
+
+hipError_t kvs_launch_topk_noalloc(const float* score, int64_t n, int64_t f0b, int64_t f0e, int64_t f1b,
+                                   int64_t f1e, int64_t n_forced, int64_t c_star, uint8_t* keep_mask,
+                                   int32_t* keep_idx, int64_t* n_kept, hipStream_t st) {
+  uint32_t* ws = nullptr;
+  if (kvs_topk_ws_bytes(n) > 0) {                     // the multi-workgroup path needs the state
+    if (kvs_topk_ws_bytes(n) > sizeof(scratch)) return hipErrorInvalidValue;
+    const hipError_t e = scratch_for(st, &ws);
+    if (e != hipSuccess) return e;
+  }
+  return kvs_launch_topk(score, n, f0b, f0e, f1b, f1e, n_forced, c_star, keep_mask, keep_idx, n_kept, ws, st);
 }
 
 hipError_t kvs_launch_slotmap(const int64_t* in, const uint8_t* mask, int64_t N, int64_t dead,

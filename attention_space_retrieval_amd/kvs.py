@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvs.so")
 
 KVS_F32, KVS_BF16 = 0, 1
 STATUS = {0: "KVS_OK", 1: "KVS_ERR_ARG", 2: "KVS_ERR_SHAPE", 3: "KVS_ERR_DTYPE",
-          4: "KVS_ERR_UNSUPPORTED", 5: "KVS_ERR_WORKSPACE", 6: "KVS_ERR_HIP"}
+          4: "KVS_ERR_UNSUPPORTED", 5: "KVS_ERR_WORKSPACE", 6: "KVS_ERR_HIP", 7: "KVS_ERR_LIMIT"}
 
 # (name, restype, argtypes)
 _P, _I32, _I64, _F32, _F64, _SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
@@ -34,6 +34,8 @@ _SIGNATURES = [
     ("kvs_window_score", _I32, [_P, _P, _I32, _I32, _I32, _I32, _I64, _I64, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     ("kvs_topk_workspace", _SZ, [_I64]),
     ("kvs_topk_select", _I32, [_P, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
+    ("kvs_topk_noalloc_max", _I64, []),
+    ("kvs_topk_select_noalloc", _I32, [_P, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P]),
     ("kvs_slotmap_redirect", _I32, [_P, _P, _I64, _I64, _P, _P]),
     ("kvs_meank_build", _I32, [_P, _I32, _I32, _I32, _I64, _I32, _I32, _I64, _F64, _P, _P, _P]),
     ("kvs_meank_append", _I32, [_P, _I32, _I32, _I32, _I64, _I64, _I64, _F64, _P, _I64, _P, _P]),
@@ -228,6 +230,29 @@ def kvs_topk_select(score, f0, f1, C, keep_mask=None, keep_idx=None, n_kept=None
     _check("kvs_topk_select", load().kvs_topk_select(
         _ptr(score), n, f0[0], f0[1], f1[0], f1[1], C, _ptr(keep_mask), _ptr(keep_idx),
         _ptr(n_kept), _ptr(ws), _nbytes(ws), _stream(score)))
+    return keep_mask, keep_idx, n_kept
+
+
+def kvs_topk_noalloc_max():
+    return load().kvs_topk_noalloc_max()
+
+
+def kvs_topk_select_noalloc(score, f0, f1, C, keep_mask, keep_idx, n_kept):
+    """kvs_topk_select without a workspace: the library's own static device array holds the
+    multi-workgroup state (n <= kvs_topk_noalloc_max(); calls overlapping on one device race).
+    The caller passes every output; nothing is allocated."""
+    _dev(score, keep_mask, keep_idx, n_kept)
+    if score.dtype != torch.float32:
+        raise TypeError("score must be float32")
+    n = score.numel()
+    _need(keep_mask.dtype == torch.uint8 and keep_mask.numel() == n, "keep_mask must be uint8 [n]")
+    _need(keep_idx.dtype == torch.int32 and keep_idx.numel() >= n, "keep_idx must be int32 [n]")
+    _need(n_kept.dtype == torch.int64 and n_kept.numel() >= 1, "n_kept must be int64 [1]")
+    if n > kvs_topk_noalloc_max():
+        raise ValueError(f"kvs_topk_select_noalloc takes at most {kvs_topk_noalloc_max()} scores, got {n}")
+    _check("kvs_topk_select_noalloc", load().kvs_topk_select_noalloc(
+        _ptr(score), n, f0[0], f0[1], f1[0], f1[1], C, _ptr(keep_mask), _ptr(keep_idx), _ptr(n_kept),
+        _stream(score)))
     return keep_mask, keep_idx, n_kept
 
 

@@ -18,7 +18,9 @@
  *   - Tensors are caller-owned, contiguous, row-major device buffers in the
  *     layout stated per argument.  The library never allocates, frees or keeps
  *     a pointer after the call returns.  Scratch memory is a caller workspace
- *     whose size comes from the matching *_workspace() query.
+ *     whose size comes from the matching *_workspace() query; the one
+ *     exception, kvs_topk_select_noalloc, uses a fixed static device array of
+ *     the library instead.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *     enqueue work on it and return without synchronising.
  *   - The return value is a kvs_status, decided on the host before any work is
@@ -53,6 +55,7 @@ typedef int32_t kvs_status;
 #define KVS_ERR_UNSUPPORTED 4  /* valid but not built: D outside {64, 128}, block != 32 */
 #define KVS_ERR_WORKSPACE 5    /* workspace missing or smaller than the query says */
 #define KVS_ERR_HIP 6          /* the HIP runtime rejected a launch */
+#define KVS_ERR_LIMIT 7        /* size above the fixed limit of a no-allocation entry point */
 
 #define KVS_F32 0
 #define KVS_BF16 1
@@ -169,6 +172,25 @@ kvs_status kvs_topk_select(const float* score, int64_t n, int64_t f0_begin, int6
                            int64_t f1_begin, int64_t f1_end, int64_t C, uint8_t* keep_mask,
                            int32_t* keep_idx, int64_t* n_kept, void* ws, size_t ws_bytes,
                            void* stream);
+
+/*
+ * Budgeted top-k that allocates nothing -- for callers that cannot allocate:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The same selection as kvs_topk_select, bit for bit, with the
+ * same arguments except the workspace: above 32768 scores the multi-workgroup
+ * state lives in a static device array of the library (about 66 KB, enough
+ * for kvs_topk_noalloc_max() scores), which each device holds from the first
+ * call on it until the process ends.  Every call on a device shares that
+ * array, so calls that overlap on one device (two streams, two host threads)
+ * race and must be ordered by the caller; consecutive calls need nothing, as
+ * each rewrites the state it reads.  The first call on a device also resolves
+ * the array's address there (no allocation).
+ * Errors: as kvs_topk_select, and KVS_ERR_LIMIT when n > kvs_topk_noalloc_max().
+ */
+int64_t kvs_topk_noalloc_max(void);
+kvs_status kvs_topk_select_noalloc(const float* score, int64_t n, int64_t f0_begin, int64_t f0_end,
+                                   int64_t f1_begin, int64_t f1_end, int64_t C, uint8_t* keep_mask,
+                                   int32_t* keep_idx, int64_t* n_kept, void* stream);
 
 /*
  * Slot-map redirect -- IntentKV layout layer (abstract; Sec. 1 contributions;

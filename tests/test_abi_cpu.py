@@ -27,7 +27,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = header_functions()
-    assert len(names) == 18
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(kvs.ENTRY_POINTS) == names
@@ -88,6 +88,15 @@ def test_topk_slot_meank_rerope_rejections(lib):
     assert need >= 4 * (256 + 2 * 45)
     assert lib.kvs_topk_select(FAKE, 92160, 0, 64, 92096, 92160, 8192, FAKE, FAKE, FAKE, FAKE, need - 1,
                                None) == 5
+    # the no-allocation variant: same checks, and a fixed size limit instead of a workspace
+    nmax = lib.kvs_topk_noalloc_max()
+    assert nmax == 1 << 24
+    assert lib.kvs_topk_select_noalloc(FAKE, nmax + 1, 0, 64, nmax - 64, nmax, 8192, FAKE, FAKE, FAKE,
+                                       None) == 7
+    assert lib.kvs_topk_select_noalloc(None, 10, 0, 1, 5, 6, 3, FAKE, FAKE, FAKE, None) == 1
+    assert lib.kvs_topk_select_noalloc(FAKE, 10, 0, 1, 5, 6, -1, FAKE, FAKE, FAKE, None) == 1
+    assert lib.kvs_topk_select_noalloc(FAKE, 1 << 31, 0, 1, 5, 6, 3, FAKE, FAKE, FAKE, None) == 2
+    assert lib.kvs_status_string(7) == b"size above the fixed limit of a no-allocation entry point"
     assert lib.kvs_slotmap_redirect(None, FAKE, 10, -1, FAKE, None) == 1
     assert lib.kvs_slotmap_redirect(FAKE, FAKE, -1, -1, FAKE, None) == 1
     assert lib.kvs_meank_build(FAKE, 2, 2, 128, 64, 16, 0, 0, 1e6, None, FAKE, None) == 4
