@@ -77,6 +77,34 @@ def test_qmem_query_mode_and_zero():
     assert torch.all(Mz == 0)
 
 
+def test_qmem_checkpoint_and_resume_is_bit_exact():
+    """M_t is the whole per-session state of the rule mode (IntentKV Sec. 3.2): t turns, a round trip
+    of M through host memory (a session saved and restored), then the remaining turns equal all
+    turns run at once, bit for bit -- M and the rule scores that read it."""
+    L, H_q, H_kv, S, D, N, T, lam = 3, 8, 2, 40, 128, 3000, 6, 0.3
+    spans = [W.normal((L, H_q, S, D), 79, 200 + t, "bf16", DEV) for t in range(T)]
+    K = W.normal((L, H_kv, N, D), 79, W.T_K, "bf16", DEV)
+    M_all = torch.empty((L, H_q, D), dtype=torch.float32, device=DEV)
+    for t, q in enumerate(spans):
+        kvs.kvs_qmem_update(q, lam, M_all, t == 0)
+    for cut in (1, 3, 5):
+        M = torch.empty((L, H_q, D), dtype=torch.float32, device=DEV)
+        for t in range(cut):
+            kvs.kvs_qmem_update(spans[t], lam, M, t == 0)
+        torch.cuda.synchronize()
+        saved = M.cpu().numpy().copy()                      # checkpoint
+        del M
+        M = torch.from_numpy(saved).to(DEV)                 # resume in a fresh buffer
+        for t in range(cut, T):
+            kvs.kvs_qmem_update(spans[t], lam, M, False)
+        torch.cuda.synchronize()
+        assert torch.equal(M.view(torch.int32), M_all.view(torch.int32)), f"resume after {cut} turns"
+        a = kvs.kvs_rule_score(K, M, 5, N - 64, N).clone()
+        b = kvs.kvs_rule_score(K, M_all, 5, N - 64, N)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
 # ---------------------------------------------------------------- rule score
 
 def test_rule_tiny_config():
