@@ -228,7 +228,7 @@ kvs_status kvs_meank_score(const void* Q, const void* index, int32_t L, int32_t 
   if (H_q % H_kv != 0 || numel4(L, H_q, Mq, D) < 0 || numel4(L, H_kv, nB, D) < 0 ||
       (int64_t)L * H_kv > 65535 || nB > kMaxIndex)
     return KVS_ERR_SHAPE;
-  if (D != 128) return KVS_ERR_UNSUPPORTED;
+  if (!head_dim_ok(D)) return KVS_ERR_UNSUPPORTED;
   if (!grid_ok(cdiv((int64_t)(H_q / H_kv) * Mq, 256) * L * H_kv) || !grid_ok(cdiv(nB, 256) * L * H_kv) ||
       nB > kMaxStreamRows || (int64_t)(H_q / H_kv) * Mq > kMaxStreamRows)
     return KVS_ERR_SHAPE;
@@ -238,7 +238,7 @@ kvs_status kvs_meank_score(const void* Q, const void* index, int32_t L, int32_t 
   const int64_t c0 = n_sink < nB ? n_sink : nB;
   int64_t c1 = nB - n_recent;
   if (c1 < c0) c1 = c0;
-  return hip_status(kvs_launch_meank_score(Q, index, L, H_q, H_kv, Mq, nB, c0, c1, R, ws,
+  return hip_status(kvs_launch_meank_score(Q, index, L, H_q, H_kv, D, Mq, nB, c0, c1, R, ws,
                                            as_stream(stream)));
 }
 
@@ -279,11 +279,11 @@ kvs_status kvs_window_score(const void* K, const void* Qw, int32_t L, int32_t H_
       !grid_ok(cdiv((int64_t)(H_q / H_kv) * W, 256) * L * H_kv) || !grid_ok(cdiv(N, 256) * L * H_kv) ||
       N > kMaxStreamRows || (int64_t)(H_q / H_kv) * W > kMaxStreamRows)
     return KVS_ERR_SHAPE;
-  if (D != 128) return KVS_ERR_UNSUPPORTED;
+  if (!head_dim_ok(D)) return KVS_ERR_UNSUPPORTED;
   if (N == 0) return KVS_OK;
   const size_t need = kvs_window_ws_bytes(L, H_q, H_kv, W, N);
   if (!ws || ws_bytes < need || !a16(ws)) return KVS_ERR_WORKSPACE;
-  return hip_status(kvs_launch_window(K, Qw, L, H_q, H_kv, W, N, pi, q_s, q_e, score, ws, as_stream(stream)));
+  return hip_status(kvs_launch_window(K, Qw, L, H_q, H_kv, D, W, N, pi, q_s, q_e, score, ws, as_stream(stream)));
 }
 
 size_t kvs_working_set_workspace(int64_t pool_pages) {

@@ -114,7 +114,7 @@ hipError_t kvs_launch_meank_append(const void* chunk, int L, int H_kv, int D, in
                                    int64_t pos0, double theta, void* stage, int64_t cap, void* index,
                                    hipStream_t st);
 
-hipError_t kvs_launch_meank_score(const void* Q, const void* index, int L, int H_q, int H_kv,
+hipError_t kvs_launch_meank_score(const void* Q, const void* index, int L, int H_q, int H_kv, int D,
                                   int64_t Mq, int64_t nB, int64_t c0, int64_t c1, float* R,
                                   void* ws, hipStream_t st);
 size_t kvs_meank_ws_bytes(int L, int H_q, int H_kv, int64_t Mq, int64_t nB);
@@ -134,5 +134,5 @@ hipError_t kvs_launch_workset(const void* k_src, const void* v_src, int64_t src_
                               hipStream_t st);
 
 size_t kvs_window_ws_bytes(int L, int H_q, int H_kv, int64_t W, int64_t N);
-hipError_t kvs_launch_window(const void* K, const void* Qw, int L, int H_q, int H_kv, int64_t W, int64_t N,
+hipError_t kvs_launch_window(const void* K, const void* Qw, int L, int H_q, int H_kv, int D, int64_t W, int64_t N,
                              int64_t pi, int64_t q_s, int64_t q_e, float* score, void* ws, hipStream_t st);

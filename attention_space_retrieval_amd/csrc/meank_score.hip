@@ -28,7 +28,9 @@
 // Workgroups are mapped XCD-aware: the tiles of one (l, g) land on the same
 // XCD and share its L2 copy of the streamed operand.
 // Operand k-slots: lane half h = lane/32 carries k-slots 8h..8h+7 of every
-// k-step; k-step s of half h is dims [64h + 8s, +8) for both operands.
+// k-step; k-step s of half h is dims [h*D/2 + 8s, +8) for both operands, so a
+// lane reads one contiguous half row.  The engine is built for D = 128 and
+// D = 64 (D/16 k-steps of the 32x32x16 MFMA per tile).
 #include <type_traits>
 
 #include "kvs_internal.h"
@@ -37,23 +39,33 @@ using namespace kvs;
 
 namespace {
 
-constexpr int D = 128;
-constexpr int KS = D / 16;          // k-steps of the 32x32x16 MFMA
 constexpr int kTile = 32;           // streamed rows per tile
 constexpr int kPerWave = 64;        // persistent rows per wave (two 32-row operands)
 constexpr int kPerWG = 4 * kPerWave;
-constexpr int kRowBytes = D * 2;
-constexpr int kLdsRow = kRowBytes + 16;   // padded LDS row: conflict-free 16-byte reads
 constexpr float kRebase = 0x1p60f;        // pass 1 rebases its reference past this tile sum
+
+// Per head dimension: k-steps of the 32x32x16 MFMA, row bytes, and the padded
+// LDS row (row stride = 16 mod 128 bytes, so the 16-byte operand reads of 16
+// consecutive rows hit 16 distinct bank groups: conflict-free).
+template <int D>
+struct Dims {
+  static_assert(D == 64 || D == 128, "head dimension");
+  static constexpr int KS = D / 16;
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kChunks = kRowBytes / 16;        // 16-byte pieces per row
+  static constexpr int kLdsRow = kRowBytes + 16;
+  static constexpr int kTileBytes = kTile * kRowBytes;
+  static constexpr int EPS = 16 / KS;                   // logits of each C tile per MFMA in the epilogue
+};
 
 // C layout of the 32x32 MFMA: lane l holds column l%32 and rows
 // 8*(v/4) + 4*(l/32) + (v%4) for v = 0..15.
 __device__ __forceinline__ int c_row(int v, int h) { return 8 * (v >> 2) + 4 * h + (v & 3); }
 
-// NT = threads per workgroup: an 8 KB tile is 512 16-byte pieces, 512 / NT per thread.
-template <int NT>
+// NT = threads per workgroup: a tile of 32 rows is kTileBytes / 16 pieces of 16 bytes.
+template <int D, int NT>
 struct Stage {
-  u32x4 w[512 / NT];
+  u32x4 w[Dims<D>::kTileBytes / 16 / NT];
   float4 lse;
 };
 
@@ -63,13 +75,13 @@ struct Stage {
 // the partial last one and those past the end alike, issues the same loads,
 // which lets the compiler keep a later tile's loads in flight while it waits
 // for an earlier one.
-template <bool WITH_LSE, int NT>
-__device__ __forceinline__ void stage_load(Stage<NT>& st, __amdgpu_buffer_rsrc_t rows, int k,
+template <bool WITH_LSE, int D, int NT>
+__device__ __forceinline__ void stage_load(Stage<D, NT>& st, __amdgpu_buffer_rsrc_t rows, int k,
                                            __amdgpu_buffer_rsrc_t lse) {
   const int t = threadIdx.x;
-  const int base = k * kTile * kRowBytes;
+  const int base = k * Dims<D>::kTileBytes;
 #pragma unroll
-  for (int i = 0; i < 512 / NT; ++i)
+  for (int i = 0; i < Dims<D>::kTileBytes / 16 / NT; ++i)
     st.w[i] = __builtin_amdgcn_raw_buffer_load_b128(rows, base + (t + NT * i) * 16, 0, 0);
   if (WITH_LSE) {
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(lse, t < 8 ? (k * kTile + 4 * t) * 4 : 0x7ffffff0, 0, 0);
@@ -77,21 +89,24 @@ __device__ __forceinline__ void stage_load(Stage<NT>& st, __amdgpu_buffer_rsrc_t
   }
 }
 
-template <bool WITH_LSE, int NT>
-__device__ __forceinline__ void stage_store(const Stage<NT>& st, char* buf, float* lbuf) {
+template <bool WITH_LSE, int D, int NT>
+__device__ __forceinline__ void stage_store(const Stage<D, NT>& st, char* buf, float* lbuf) {
+  using Dm = Dims<D>;
   const int t = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < 512 / NT; ++i) {
-    const int idx = t + NT * i, row = idx >> 4, chunk = idx & 15;
-    *reinterpret_cast<u32x4*>(buf + row * kLdsRow + chunk * 16) = st.w[i];
+  for (int i = 0; i < Dm::kTileBytes / 16 / NT; ++i) {
+    const int idx = t + NT * i, row = idx / Dm::kChunks, chunk = idx % Dm::kChunks;
+    *reinterpret_cast<u32x4*>(buf + row * Dm::kLdsRow + chunk * 16) = st.w[i];
   }
   if (WITH_LSE && t < 8) *reinterpret_cast<float4*>(lbuf + 4 * t) = st.lse;
 }
 
+template <int D>
 __device__ __forceinline__ void read_streamed(const char* buf, int lane, bf16x8* A) {
-  const char* p = buf + (lane & 31) * kLdsRow + (lane >> 5) * 128;
+  using Dm = Dims<D>;
+  const char* p = buf + (lane & 31) * Dm::kLdsRow + (lane >> 5) * (Dm::kRowBytes / 2);
 #pragma unroll
-  for (int s = 0; s < KS; ++s) A[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p + 16 * s));
+  for (int s = 0; s < Dm::KS; ++s) A[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p + 16 * s));
 }
 
 __device__ __forceinline__ void read_lse16(const float* lbuf, int h, float* l16) {
@@ -102,12 +117,13 @@ __device__ __forceinline__ void read_lse16(const float* lbuf, int h, float* l16)
   }
 }
 
+template <int D>
 __device__ __forceinline__ void mma2(const bf16x8* A, const bf16x8* B0, const bf16x8* B1, f32x16& c0,
                                      f32x16& c1) {
   c0 = f32x16{};
   c1 = f32x16{};
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
+  for (int s = 0; s < Dims<D>::KS; ++s) {
     c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], B0[s], c0, 0, 0, 0);
     c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], B1[s], c1, 0, 0, 0);
   }
@@ -125,32 +141,40 @@ __device__ __forceinline__ float tile_max(const f32x16& c) {
 // below the MFMAs it is meant to overlap.
 #define KVS_PIN2(a, b) asm volatile("" : "+v"(a), "+v"(b))
 
-// One software-pipelined step: the 16 MFMAs of the next tile (cn = A x B) are
-// issued one at a time, each followed by a slice of the current tile's
-// epilogue (2 logits of each C tile), with scheduling barriers in between so
-// the matrix unit works while the wave's vector ALU runs the exp2 epilogue.
-// ref0/ref1 are the per-lane exponent references (pass 1: the running
-// reference of the lane's query row; pass 2: unused, the row lse2 in l16).
-template <bool PASS1>
+// One software-pipelined step: the 2*D/16 MFMAs of the next tile (cn = A x B)
+// are issued one at a time, each followed by a slice of the current tile's
+// epilogue (EPS = 16/(D/16) logits of each C tile: 2 at D = 128, 4 at D = 64),
+// with scheduling barriers in between so the matrix unit works while the
+// wave's vector ALU runs the exp2 epilogue.  ref0/ref1 are the per-lane
+// exponent references (pass 1: the running reference of the lane's query row;
+// pass 2: unused, the row lse2 in l16).
+template <bool PASS1, int D>
 __device__ __forceinline__ void step_mma_epi(const bf16x8* A, const bf16x8* B0, const bf16x8* B1,
                                              f32x16& cn0, f32x16& cn1, const f32x16& cc0,
                                              const f32x16& cc1, float scale, const float* l16,
                                              float ref0, float ref1, float& sum0, float& sum1) {
+  constexpr int KS = Dims<D>::KS, EPS = Dims<D>::EPS;
   cn0 = f32x16{};
   cn1 = f32x16{};
   float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    const float r00 = PASS1 ? ref0 : l16[2 * s], r01 = PASS1 ? ref0 : l16[2 * s + 1];
-    const float r10 = PASS1 ? ref1 : l16[2 * s], r11 = PASS1 ? ref1 : l16[2 * s + 1];
     cn0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], B0[s], cn0, 0, 0, 0);
-    a0 += __builtin_amdgcn_exp2f(fmaf(cc0[2 * s], scale, -r00));
-    a1 += __builtin_amdgcn_exp2f(fmaf(cc0[2 * s + 1], scale, -r01));
+#pragma unroll
+    for (int e = 0; e < EPS; e += 2) {
+      const int v = EPS * s + e;
+      a0 += __builtin_amdgcn_exp2f(fmaf(cc0[v], scale, -(PASS1 ? ref0 : l16[v])));
+      a1 += __builtin_amdgcn_exp2f(fmaf(cc0[v + 1], scale, -(PASS1 ? ref0 : l16[v + 1])));
+    }
     KVS_PIN2(a0, a1);
     __builtin_amdgcn_sched_barrier(0);
     cn1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[s], B1[s], cn1, 0, 0, 0);
-    b0 += __builtin_amdgcn_exp2f(fmaf(cc1[2 * s], scale, -r10));
-    b1 += __builtin_amdgcn_exp2f(fmaf(cc1[2 * s + 1], scale, -r11));
+#pragma unroll
+    for (int e = 0; e < EPS; e += 2) {
+      const int v = EPS * s + e;
+      b0 += __builtin_amdgcn_exp2f(fmaf(cc1[v], scale, -(PASS1 ? ref1 : l16[v])));
+      b1 += __builtin_amdgcn_exp2f(fmaf(cc1[v + 1], scale, -(PASS1 ? ref1 : l16[v + 1])));
+    }
     KVS_PIN2(b0, b1);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -208,7 +232,7 @@ __device__ __forceinline__ void xcd_map(int T, int LG, int& lg, int& tile) {
 // pass 1 may split the candidate range over n_split workgroups (gridDim.y);
 // each then writes a (max, sum) partial per row to part1 and meank_lse_merge
 // combines them.  R_b instantiates SPAN = false, which compiles both out.
-template <bool PASS1, bool SPAN, int NW = 4>
+template <bool PASS1, bool SPAN, int NW, int D>
 __global__ __launch_bounds__(64 * NW, 2) void meank_pass(const uint16_t* __restrict__ Q,
                                                      const uint16_t* __restrict__ index, int LG,
                                                      int64_t rows, int64_t rows_pad, int64_t nB,
@@ -217,6 +241,8 @@ __global__ __launch_bounds__(64 * NW, 2) void meank_pass(const uint16_t* __restr
                                                      float* __restrict__ lse2,
                                                      float2* __restrict__ part1,
                                                      float* __restrict__ colpart) {
+  using Dm = Dims<D>;
+  constexpr int KS = Dm::KS, kRowBytes = Dm::kRowBytes, kLdsRow = Dm::kLdsRow;
   constexpr int NT = 64 * NW, PER_WG = NW * kPerWave;   // threads and persistent rows per workgroup
   // one LDS area: first the workgroup's persistent rows, then the two streamed tiles
   __shared__ __attribute__((aligned(16))) char smem[PER_WG * kLdsRow];
@@ -232,7 +258,7 @@ __global__ __launch_bounds__(64 * NW, 2) void meank_pass(const uint16_t* __restr
 
   // persistent operand: pass 1 = query rows, pass 2 = index rows (block columns).
   // The workgroup's 256 rows are read whole and coalesced (16 loads of 16 bytes
-  // per thread; rows past the end read as zero), staged in LDS, and each wave
+  // per thread at D = 128; rows past the end read as zero), staged in LDS, and each wave
   // takes its 64 rows in the operand layout from there.  Loaded straight in
   // that layout, every load instruction would touch 64 rows 16 bytes at a
   // time, which starves the passes that stream few tiles per workgroup.
@@ -252,10 +278,10 @@ __global__ __launch_bounds__(64 * NW, 2) void meank_pass(const uint16_t* __restr
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int idx = threadIdx.x + NT * i;
-      *reinterpret_cast<u32x4*>(smem + (idx >> 4) * kLdsRow + (idx & 15) * 16) = v[i];
+      *reinterpret_cast<u32x4*>(smem + (idx / Dm::kChunks) * kLdsRow + (idx % Dm::kChunks) * 16) = v[i];
     }
     __syncthreads();
-    const char* r0 = smem + (wave * kPerWave + n) * kLdsRow + h * 128;
+    const char* r0 = smem + (wave * kPerWave + n) * kLdsRow + h * (kRowBytes / 2);
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
       B0[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(r0 + 16 * k));
@@ -291,7 +317,7 @@ __global__ __launch_bounds__(64 * NW, 2) void meank_pass(const uint16_t* __restr
   // streamed rows [s_begin, s_end) and, in pass 2, their lse2 (tile k = rows 32k..)
   const __amdgpu_buffer_rsrc_t srows = buf_rsrc(sbase + (size_t)s_begin * D, (int)((s_end - s_begin) * kRowBytes));
   const __amdgpu_buffer_rsrc_t slse = buf_rsrc(Lg, PASS1 ? 0 : (int)(rows_pad * 4));
-  Stage<NT> st[PF];
+  Stage<D, NT> st[PF];
   stage_load<!PASS1>(st[0], srows, 0, slse);
   stage_store<!PASS1>(st[0], tiles[0], lses[0]);
   stage_load<!PASS1>(st[0], srows, 1, slse);
@@ -307,9 +333,9 @@ __global__ __launch_bounds__(64 * NW, 2) void meank_pass(const uint16_t* __restr
   bf16x8 A[KS];
   f32x16 cA0 = {}, cA1 = {}, cB0 = {}, cB1 = {};     // ping-pong accumulators (tile t and t+1)
   float lA[16], lB[16];               // pass 2: lse2 of the rows of tile t and t+1
-  read_streamed(tiles[0], lane, A);
+  read_streamed<D>(tiles[0], lane, A);
   if (!PASS1) read_lse16(lses[0], h, lA);
-  if (live) mma2(A, B0, B1, cA0, cA1);
+  if (live) mma2<D>(A, B0, B1, cA0, cA1);
   __syncthreads();
 
   // pass 1: running reference and sum per persistent row; pass 2: column sums
@@ -334,13 +360,13 @@ __global__ __launch_bounds__(64 * NW, 2) void meank_pass(const uint16_t* __restr
   // load tile t+1+PF into stage sl = st[(t+1) % PF] and move tile t+2, loaded
   // PF-1 iterations earlier, from stage ss = st[(t+2) % PF] into LDS.
   auto body = [&](int t, f32x16& cc0, f32x16& cc1, float* lc, f32x16& cn0, f32x16& cn1, float* ln,
-                  Stage<NT>& sl, Stage<NT>& ss) __attribute__((always_inline)) {
+                  Stage<D, NT>& sl, Stage<D, NT>& ss) __attribute__((always_inline)) {
     const bool pre = t + 2 < nt;
     stage_load<!PASS1>(sl, srows, t + 1 + PF, slse);   // past the end: reads nothing, returns zeros
-    read_streamed(tiles[(t + 1) & 1], lane, A);
+    read_streamed<D>(tiles[(t + 1) & 1], lane, A);
     if (!PASS1) read_lse16(lses[(t + 1) & 1], h, ln);
     float a0 = 0.f, a1 = 0.f;
-    if (live) step_mma_epi<PASS1>(A, B0, B1, cn0, cn1, cc0, cc1, scale, lc, m0, m1, a0, a1);
+    if (live) step_mma_epi<PASS1, D>(A, B0, B1, cn0, cn1, cc0, cc1, scale, lc, m0, m1, a0, a1);
     if (PASS1) {
       const int64_t tb = s_begin + (int64_t)t * kTile;
       if (SPAN && tb < h1 && tb + kTile > h0) {    // tile meets the excluded span (wave-uniform)
@@ -489,9 +515,11 @@ size_t kvs_meank_ws_bytes(int L, int H_q, int H_kv, int64_t Mq, int64_t nB) {
   return align256(LG * (size_t)rows_pad * 4) + align256(LG * (size_t)nB * 4);
 }
 
-hipError_t kvs_launch_meank_score(const void* Q, const void* index, int L, int H_q, int H_kv,
-                                  int64_t Mq, int64_t nB, int64_t c0, int64_t c1, float* R,
-                                  void* ws, hipStream_t st) {
+namespace {
+
+template <int D>
+hipError_t launch_meank_score(const uint16_t* Qb, const uint16_t* Ib, int L, int H_q, int H_kv, int64_t Mq,
+                              int64_t nB, int64_t c0, int64_t c1, float* R, void* ws, hipStream_t st) {
   const int LG = L * H_kv;
   const int G = H_q / H_kv;
   const int64_t rows = (int64_t)G * Mq;
@@ -500,16 +528,14 @@ hipError_t kvs_launch_meank_score(const void* Q, const void* index, int L, int H
   float* lse2 = reinterpret_cast<float*>(w);
   float* colpart = reinterpret_cast<float*>(w + align256((size_t)LG * rows_pad * 4));
   const float scale = (float)(1.4426950408889634 / __builtin_sqrt((double)D));
-  const uint16_t* Qb = static_cast<const uint16_t*>(Q);
-  const uint16_t* Ib = static_cast<const uint16_t*>(index);
   if (c1 > c0 && rows > 0) {
     const int T1 = (int)ceil_div(rows_pad, kPerWG);
-    hipLaunchKernelGGL((meank_pass<true, false>), dim3((unsigned)T1 * LG), dim3(256), 0, st, Qb, Ib, LG, rows,
+    hipLaunchKernelGGL((meank_pass<true, false, 4, D>), dim3((unsigned)T1 * LG), dim3(256), 0, st, Qb, Ib, LG, rows,
                        rows_pad, nB, c0, c1, (int64_t)0, (int64_t)0, T1, scale, 1, lse2, nullptr, colpart);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int T2 = (int)ceil_div(c1 - c0, kPerWG);
-    hipLaunchKernelGGL((meank_pass<false, false>), dim3((unsigned)T2 * LG), dim3(256), 0, st, Qb, Ib, LG, rows,
+    hipLaunchKernelGGL((meank_pass<false, false, 4, D>), dim3((unsigned)T2 * LG), dim3(256), 0, st, Qb, Ib, LG, rows,
                        rows_pad, nB, c0, c1, (int64_t)0, (int64_t)0, T2, scale, 1, lse2, nullptr, colpart);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -519,6 +545,17 @@ hipError_t kvs_launch_meank_score(const void* Q, const void* index, int L, int H
   hipLaunchKernelGGL(meank_reduce<false>, dim3(ceil_div(nB, 64)), dim3(256), 0, st, colpart, LG, nB, c0, c1,
                      (int64_t)0, (int64_t)0, (float)(L * H_q), R);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t kvs_launch_meank_score(const void* Q, const void* index, int L, int H_q, int H_kv, int D,
+                                  int64_t Mq, int64_t nB, int64_t c0, int64_t c1, float* R,
+                                  void* ws, hipStream_t st) {
+  const uint16_t* Qb = static_cast<const uint16_t*>(Q);
+  const uint16_t* Ib = static_cast<const uint16_t*>(index);
+  return D == 128 ? launch_meank_score<128>(Qb, Ib, L, H_q, H_kv, Mq, nB, c0, c1, R, ws, st)
+                  : launch_meank_score<64>(Qb, Ib, L, H_q, H_kv, Mq, nB, c0, c1, R, ws, st);
 }
 
 // Window score (the SnapKV query window that IntentKV's Eq. 3 replaces by one
@@ -570,8 +607,11 @@ size_t kvs_window_ws_bytes(int L, int H_q, int H_kv, int64_t W, int64_t N) {
          align256(LG * (size_t)N * 4);
 }
 
-hipError_t kvs_launch_window(const void* K, const void* Qw, int L, int H_q, int H_kv, int64_t W, int64_t N,
-                             int64_t pi, int64_t q_s, int64_t q_e, float* score, void* ws, hipStream_t st) {
+namespace {
+
+template <int D>
+hipError_t launch_window(const uint16_t* Qb, const uint16_t* Kb, int L, int H_q, int H_kv, int64_t W, int64_t N,
+                         int64_t pi, int64_t q_s, int64_t q_e, float* score, void* ws, hipStream_t st) {
   const int LG = L * H_kv;
   WindowPlan p = window_plan(L, H_q, H_kv, W, N, pi, q_s, q_e);
   // the split count (and so the workspace) does not depend on pi or the span
@@ -583,18 +623,16 @@ hipError_t kvs_launch_window(const void* K, const void* Qw, int L, int H_q, int 
   w += align256((size_t)LG * p.rows_pad * p.n_split * 8);
   float* colpart = reinterpret_cast<float*>(w);
   const float scale = (float)(1.4426950408889634 / __builtin_sqrt((double)D));
-  const uint16_t* Qb = static_cast<const uint16_t*>(Qw);
-  const uint16_t* Kb = static_cast<const uint16_t*>(K);
   int64_t c0 = p.c0, c1 = p.c1;
   const bool any = c1 > c0 && !(p.h0 <= c0 && p.h1 >= c1) && p.rows > 0;
   if (any) {
     const dim3 grid1((unsigned)p.T1 * LG, (unsigned)p.n_split);
     if (p.nw1 == 2)
-      hipLaunchKernelGGL((meank_pass<true, true, 2>), grid1, dim3(128), 0, st, Qb, Kb, LG, p.rows, p.rows_pad, N, c0,
-                         c1, p.h0, p.h1, p.T1, scale, p.n_split, lse2, part1, colpart);
+      hipLaunchKernelGGL((meank_pass<true, true, 2, D>), grid1, dim3(128), 0, st, Qb, Kb, LG, p.rows, p.rows_pad, N,
+                         c0, c1, p.h0, p.h1, p.T1, scale, p.n_split, lse2, part1, colpart);
     else
-      hipLaunchKernelGGL((meank_pass<true, true>), grid1, dim3(256), 0, st, Qb, Kb, LG, p.rows, p.rows_pad, N, c0, c1,
-                         p.h0, p.h1, p.T1, scale, p.n_split, lse2, part1, colpart);
+      hipLaunchKernelGGL((meank_pass<true, true, 4, D>), grid1, dim3(256), 0, st, Qb, Kb, LG, p.rows, p.rows_pad, N,
+                         c0, c1, p.h0, p.h1, p.T1, scale, p.n_split, lse2, part1, colpart);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (p.n_split > 1) {
@@ -604,8 +642,8 @@ hipError_t kvs_launch_window(const void* K, const void* Qw, int L, int H_q, int 
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((meank_pass<false, true, 2>), dim3((unsigned)p.T2 * LG), dim3(128), 0, st, Qb, Kb, LG, p.rows,
-                       p.rows_pad, N, c0, c1, p.h0, p.h1, p.T2, scale, 1, lse2, part1, colpart);
+    hipLaunchKernelGGL((meank_pass<false, true, 2, D>), dim3((unsigned)p.T2 * LG), dim3(128), 0, st, Qb, Kb, LG,
+                       p.rows, p.rows_pad, N, c0, c1, p.h0, p.h1, p.T2, scale, 1, lse2, part1, colpart);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   } else {
@@ -614,4 +652,14 @@ hipError_t kvs_launch_window(const void* K, const void* Qw, int L, int H_q, int 
   hipLaunchKernelGGL(meank_reduce<true>, dim3(ceil_div(N, 64)), dim3(256), 0, st, colpart, LG, N, c0, c1, p.h0,
                      p.h1, 1.0f, score);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t kvs_launch_window(const void* K, const void* Qw, int L, int H_q, int H_kv, int D, int64_t W, int64_t N,
+                             int64_t pi, int64_t q_s, int64_t q_e, float* score, void* ws, hipStream_t st) {
+  const uint16_t* Qb = static_cast<const uint16_t*>(Qw);
+  const uint16_t* Kb = static_cast<const uint16_t*>(K);
+  return D == 128 ? launch_window<128>(Qb, Kb, L, H_q, H_kv, W, N, pi, q_s, q_e, score, ws, st)
+                  : launch_window<64>(Qb, Kb, L, H_q, H_kv, W, N, pi, q_s, q_e, score, ws, st);
 }

@@ -62,13 +62,13 @@ CALL_KERNELS = {
     "kvs_topk_select[meank]": ["topk_reg_kernel<8>"],
     "kvs_slotmap_redirect": ["slotmap_kernel"],
     "kvs_meank_build": ["meank_build_raw<128>"],
-    "kvs_meank_score": ["meank_pass<true, false, 4>", "meank_pass<false, false, 4>", "meank_reduce<false>"],
+    "kvs_meank_score": ["meank_pass<true, false, 4, 128>", "meank_pass<false, false, 4, 128>", "meank_reduce<false>"],
     "kvs_rerope_scatter": ["rerope_scatter_kernel<128>", "v_scatter_kernel<128>"],
     # rows beyond the step (timed after it): the paged rule score's merge and column sum are the
     # dense call's kernels on the same sizes
     "kvs_rule_score_paged": ["rule_logits_mfma<128, 1, true>", "rule_lse_merge", "rule_colsum"],
-    "kvs_window_score": [("meank_pass<true, true, 2>", "meank_pass<true, true, 4>"), "meank_lse_merge",
-                         "meank_pass<false, true, 2>",
+    "kvs_window_score": [("meank_pass<true, true, 2, 128>", "meank_pass<true, true, 4, 128>"), "meank_lse_merge",
+                         "meank_pass<false, true, 2, 128>",
                          "meank_reduce<true>"],
     "kvs_meank_append": ["meank_append_kernel<128>"],
     "kvs_working_set_update": ["workset_diff", "workset_apply<128, true>"],

@@ -138,7 +138,7 @@ size_t kvs_window_score_workspace(int32_t L, int32_t H_q, int32_t H_kv, int64_t 
  *   score    [N] float32 output; 0 on F; sum over H = L*H_q*W.
  *   ws       device workspace of >= kvs_window_score_workspace() bytes.
  * Errors: KVS_ERR_ARG (null, W < 1, bad range), KVS_ERR_SHAPE (also N or
- * G*W at or above 2^23 - 128 rows), KVS_ERR_UNSUPPORTED (D != 128),
+ * G*W at or above 2^23 - 128 rows), KVS_ERR_UNSUPPORTED (D not 64/128),
  * KVS_ERR_WORKSPACE.
  */
 kvs_status kvs_window_score(const void* K, const void* Qw, int32_t L, int32_t H_q, int32_t H_kv,
@@ -263,7 +263,7 @@ size_t kvs_meank_score_workspace(int32_t L, int32_t H_q, int32_t H_kv, int64_t M
  *   R        [nB] float32 output; 0 on sink and recent blocks; sum over C = Mq.
  *   ws       device workspace of >= kvs_meank_score_workspace() bytes.
  * Errors: KVS_ERR_ARG, KVS_ERR_SHAPE (also nB or G*Mq above 2^23 - 128),
- * KVS_ERR_UNSUPPORTED (D != 128), KVS_ERR_WORKSPACE.
+ * KVS_ERR_UNSUPPORTED (D not 64/128), KVS_ERR_WORKSPACE.
  */
 kvs_status kvs_meank_score(const void* Q, const void* index, int32_t L, int32_t H_q,
                            int32_t H_kv, int32_t D, int64_t Mq, int64_t nB, int64_t n_sink,

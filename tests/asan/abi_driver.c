@@ -68,6 +68,7 @@ int main(void) {
   CHECK(kvs_window_score(F, F, 2, 8, 2, 128, 1000, 0, 4, 990, 1000, F, F, wws, NULL), KVS_ERR_ARG);
   CHECK(kvs_window_score(F, F, 2, 8, 3, 128, 1000, 16, 4, 990, 1000, F, F, wws, NULL), KVS_ERR_SHAPE);
   CHECK(kvs_window_score(F, F, 2, 8, 2, 128, 1000, 16, 4, 990, 1000, F, F, wws - 1, NULL), KVS_ERR_WORKSPACE);
+  CHECK(kvs_window_score(F, F, 2, 8, 2, 96, 1000, 16, 4, 990, 1000, F, F, wws, NULL), KVS_ERR_UNSUPPORTED);
 
   /* top-k, with and without a workspace, and the no-allocation variant */
   CHECK(kvs_topk_workspace(32768), 0);
@@ -106,6 +107,7 @@ int main(void) {
   CHECK(kvs_meank_score(F, F, 2, 8, 3, 128, 50, 300, 4, 7, F, F, mws, NULL), KVS_ERR_SHAPE);
   CHECK(kvs_meank_score(F, F, 2, 8, 2, 128, 50, 300, 4, 7, F, F, mws - 1, NULL), KVS_ERR_WORKSPACE);
   CHECK(kvs_meank_score(F, F, 2, 8, 2, 128, 50, 300, -1, 7, F, F, mws, NULL), KVS_ERR_ARG);
+  CHECK(kvs_meank_score(F, F, 2, 8, 2, 96, 50, 300, 4, 7, F, F, mws, NULL), KVS_ERR_UNSUPPORTED);
   CHECK(kvs_meank_score(F, F, 4, 8, 2, 128, 50, ((int64_t)1 << 31) - 1, 4, 7, F, F, (size_t)1 << 30, NULL),
         KVS_ERR_SHAPE);
 

@@ -112,7 +112,7 @@ def test_topk_slot_meank_rerope_rejections(lib):
     assert a(None, 2, 2, 128, 10, 0, 0, 1e6, None, 64, None, None) == 0       # empty chunk: no-op
     ws = lib.kvs_meank_score_workspace(2, 8, 2, 50, 300)
     assert ws > 0
-    assert lib.kvs_meank_score(FAKE, FAKE, 2, 8, 2, 64, 50, 300, 4, 7, FAKE, FAKE, ws, None) == 4
+    assert lib.kvs_meank_score(FAKE, FAKE, 2, 8, 2, 96, 50, 300, 4, 7, FAKE, FAKE, ws, None) == 4
     assert lib.kvs_meank_score(FAKE, FAKE, 2, 8, 3, 128, 50, 300, 4, 7, FAKE, FAKE, ws, None) == 2
     assert lib.kvs_meank_score(FAKE, FAKE, 2, 8, 2, 128, 50, 300, 4, 7, FAKE, FAKE, ws - 1, None) == 5
     assert lib.kvs_meank_score(FAKE, FAKE, 2, 8, 2, 128, 50, 300, -1, 7, FAKE, FAKE, ws, None) == 1
@@ -148,7 +148,7 @@ def test_window_rejections(lib):
     assert ws > 0
     assert f(FAKE, FAKE, 2, 8, 2, 128, 1000, 0, 4, 990, 1000, FAKE, FAKE, ws, None) == 1      # W = 0
     assert f(FAKE, FAKE, 2, 8, 3, 128, 1000, 16, 4, 990, 1000, FAKE, FAKE, ws, None) == 2
-    assert f(FAKE, FAKE, 2, 8, 2, 64, 1000, 16, 4, 990, 1000, FAKE, FAKE, ws, None) == 4
+    assert f(FAKE, FAKE, 2, 8, 2, 96, 1000, 16, 4, 990, 1000, FAKE, FAKE, ws, None) == 4
     assert f(FAKE, FAKE, 2, 8, 2, 128, 1000, 16, 4, 990, 1000, FAKE, FAKE, ws - 1, None) == 5
     assert f(None, FAKE, 2, 8, 2, 128, 1000, 16, 4, 990, 1000, FAKE, FAKE, ws, None) == 1
 

@@ -7,6 +7,8 @@ re-RoPE'd K within max(1e-2, 1 bf16 ulp) of the float64 rotation, and within
 bit-exact on identical float32 scores.
 """
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -237,6 +239,7 @@ def check_score(Q, index, n_sink, n_recent, what):
     return got, want
 
 
+@pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("L,H_q,H_kv,Mq,nB,sink,recent", [
     (2, 8, 2, 50, 300, 4, 7),        # ragged rows (200) and columns (289)
     (1, 40, 8, 33, 130, 4, 64),      # G = 5, 62 candidate blocks
@@ -247,11 +250,24 @@ def check_score(Q, index, n_sink, n_recent, what):
     (1, 8, 2, 24, 150, 3, 7),        # 140 candidates: five tiles, one past the unrolled trips
     (1, 16, 4, 40, 262, 5, 1),       # 256 candidates: eight whole tiles
     (1, 8, 2, 20, 115, 2, 2),        # 111 candidates: four tiles, the last partial
+    (1, 8, 2, 300, 700, 4, 64),      # 600 query rows (three workgroups of 256), 632 candidates
 ])
-def test_meank_score_shapes(L, H_q, H_kv, Mq, nB, sink, recent):
-    Q = W.normal((L, H_q, Mq, 128), 31, W.T_Q, "bf16", DEV)
-    index = W.index_like(L, H_kv, nB, 128, 31, DEV)
-    check_score(Q, index, sink, recent, f"R L{L} Hq{H_q} Hkv{H_kv} Mq{Mq} nB{nB}")
+def test_meank_score_shapes(L, H_q, H_kv, Mq, nB, sink, recent, D):
+    Q = W.normal((L, H_q, Mq, D), 31, W.T_Q, "bf16", DEV)
+    index = W.index_like(L, H_kv, nB, D, 31, DEV, scale=0.1767766952966369 * math.sqrt(128 / D))
+    check_score(Q, index, sink, recent, f"R D{D} L{L} Hq{H_q} Hkv{H_kv} Mq{Mq} nB{nB}")
+
+
+def test_meank_score_d64_peaked_and_full_extent():
+    """D = 64 with a peaked softmax (index spread 1.0), and one (layer, KV head) at meank-256k's
+    per-group extent (2560 query rows x 8124 candidate blocks)."""
+    Q = W.normal((2, 8, 40, 64), 32, W.T_Q, "bf16", DEV)
+    index = W.index_like(2, 2, 200, 64, 32, DEV, scale=1.0)
+    check_score(Q, index, 4, 8, "peaked, D = 64")
+    c = W.config("meank-256k")
+    Q = W.normal((1, 5, c["Mq"], 64), c["seed"], W.T_Q, "bf16", DEV)
+    index = W.index_like(1, 1, c["N"] // 32, 64, c["seed"], DEV, scale=0.25)
+    check_score(Q, index, c["n_sink"], c["n_recent"], "meank-256k extent, D = 64")
 
 
 def test_meank_score_peaked_softmax():

@@ -265,17 +265,18 @@ def test_rule_paged_full_size_equals_dense(name):
     (1, 16, 2, 2500, 32, 5, 2400, 2450),       # G*W = 256 rows: pass 1 with four-wave workgroups
     (1, 20, 4, 1800, 40, 0, 1700, 1800),       # G*W = 200 rows (padded to 224): four waves, a partial one
 ])
-def test_window_score_against_oracle(L, H_q, H_kv, N, Wn, pi, q_s, q_e):
-    """Wn window rows per query head."""
-    K = W.normal((L, H_kv, N, 128), 17, W.T_K, "bf16", DEV)
-    Qw = W.normal((L, H_q, Wn, 128), 17, W.T_Q, "bf16", DEV)
+@pytest.mark.parametrize("D", [128, 64])
+def test_window_score_against_oracle(L, H_q, H_kv, N, Wn, pi, q_s, q_e, D):
+    """Wn window rows per query head, head dimension D."""
+    K = W.normal((L, H_kv, N, D), 17, W.T_K, "bf16", DEV)
+    Qw = W.normal((L, H_q, Wn, D), 17, W.T_Q, "bf16", DEV)
     got = kvs.kvs_window_score(K, Qw, pi, q_s, q_e)
     torch.cuda.synchronize()
     got = got.cpu().numpy()
     want = oracle.window_score(host(K), host(Qw), pi, q_s, q_e)
     F = oracle.forced_mask(N, pi, q_s, q_e)
     assert np.all(got[F] == 0.0)
-    assert_rel(got[~F], want[~F], RULE_RTOL, f"window score W{Wn} N{N}")
+    assert_rel(got[~F], want[~F], RULE_RTOL, f"window score W{Wn} N{N} D{D}")
     assert abs(got.sum(dtype=np.float64) - L * H_q * Wn) <= 1e-4 * L * H_q * Wn
 
 
