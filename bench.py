@@ -319,6 +319,39 @@ def run_calls(calls, steps, warmup):
     return wall, per_call, spread
 
 
+def parse_smi(text):
+    """Socket power (W) and the GFX clocks (MHz, one per XCD) from `amd-smi metric -p -c` text."""
+    import re
+    power = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", text)
+    clocks = [float(m.group(1)) for m in re.finditer(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz", text)]
+    return (float(power.group(1)) if power else None), clocks
+
+
+def power_sample(fn, ms_per_call, seconds=1.5):
+    """Board power and GFX clock while fn runs back to back: ~`seconds` of calls are queued and
+    amd-smi is read once while they run.  None when amd-smi is missing or fails."""
+    import shutil
+    import subprocess
+    if shutil.which("amd-smi") is None:
+        return None
+    fn()
+    torch.cuda.synchronize()
+    for _ in range(max(8, int(seconds * 1e3 / max(ms_per_call, 1e-3)))):
+        fn()
+    time.sleep(min(0.5, seconds / 3))
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True, text=True, timeout=30)
+        text = r.stdout
+    except (OSError, subprocess.SubprocessError):
+        text = ""
+    torch.cuda.synchronize()
+    power, clocks = parse_smi(text)
+    if power is None and not clocks:
+        return None
+    return {"socket_power_w": power, "gfx_clock_mhz_per_xcd": clocks,
+            "gfx_clock_mhz_mean": round(sum(clocks) / len(clocks), 1) if clocks else None}
+
+
 def run_gpu(s, steps, warmup, only=None):
     calls = s.calls()
     if only:
@@ -477,6 +510,9 @@ def main():
                                                           "selected": int(nr.new.numel())}
         next_rows["kvs_window_score"]["window_rows"] = nr.W
         del nr
+    # board power and clock while the dominant call runs back to back (after the timed steps)
+    dom_call = max(per_call, key=lambda k: per_call[k])
+    psample = power_sample(dict(s.calls())[dom_call], per_call[dom_call])
     if a.copy_calibration:
         x = torch.empty(1 << 31, dtype=torch.int16, device=dev)
         y = torch.empty_like(x)
@@ -520,6 +556,7 @@ def main():
                    "tokens_per_step": tokens},
         "roofline": {"call": dom, "kernels": " + ".join(k if isinstance(k, str) else " | ".join(k)
                                                          for k in call_kernels(a.workload).get(dom, [dom])),
+                     "power_sample": psample,
                      "bound": d["bound"],
                      "achieved": d["achieved"], "peak": d["peak"], "unit": d["unit"], "frac": d["frac"],
                      "per_launch": d["per_launch"], "traffic": d["traffic"]},

@@ -1,0 +1,34 @@
+"""bench.py helpers that run without a GPU."""
+
+import bench
+
+SMI = """GPU: 0
+    POWER:
+        SOCKET_POWER: 1332 W
+        GFX_VOLTAGE: N/A
+    CLOCK:
+        GFX_0:
+            CLK: 1910 MHz
+            MIN_CLK: 500 MHz
+            MAX_CLK: 2400 MHz
+        GFX_1:
+            CLK: 1841 MHz
+            MIN_CLK: 500 MHz
+        MEM_0:
+            CLK: 2000 MHz
+"""
+
+
+def test_parse_amd_smi_power_and_gfx_clocks():
+    power, clocks = bench.parse_smi(SMI)
+    assert power == 1332.0
+    assert clocks == [1910.0, 1841.0]            # memory clocks are not GFX clocks
+    assert bench.parse_smi("") == (None, [])
+
+
+def test_call_kernels_follow_the_workload():
+    big = bench.call_kernels("rule-14b+meank-1m")
+    small = bench.call_kernels("rule-8b+meank-256k")
+    assert "topk_mw_pass*4" in big["kvs_topk_select[rule]"]
+    assert small["kvs_topk_select[rule]"] == ["topk_reg_kernel<32>"]
+    assert big["kvs_meank_score"] == small["kvs_meank_score"]
