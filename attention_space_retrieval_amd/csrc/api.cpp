@@ -101,7 +101,7 @@ size_t kvs_rule_score_workspace(int32_t L, int32_t H_q, int32_t H_kv, int64_t N)
 kvs_status kvs_rule_score(const void* K, int32_t k_dtype, const float* M, int32_t L, int32_t H_q,
                           int32_t H_kv, int32_t D, int64_t N, int64_t pi, int64_t q_s, int64_t q_e,
                           float* rule, void* ws, size_t ws_bytes, void* stream) {
-  if (!K || !M || !rule || !a16(K)) return KVS_ERR_ARG;
+  if (!M || (N > 0 && (!K || !rule)) || !a16(K)) return KVS_ERR_ARG;   // K and rule are empty when N = 0
   if (k_dtype != KVS_F32 && k_dtype != KVS_BF16) return KVS_ERR_DTYPE;
   if (L < 1 || H_q < 1 || H_kv < 1 || N < 0 || pi < 0 || q_s < 0 || q_e < q_s) return KVS_ERR_ARG;
   if (H_q % H_kv != 0 || N > kMaxIndex || numel4(L, H_kv, N, D) < 0 ||
@@ -122,7 +122,7 @@ kvs_status kvs_rule_score_paged(const void* K_pool, int32_t k_dtype, const int64
                                 int64_t pool_size, const float* M, int32_t L, int32_t H_q,
                                 int32_t H_kv, int32_t D, int64_t N, int64_t pi, int64_t q_s,
                                 int64_t q_e, float* rule, void* ws, size_t ws_bytes, void* stream) {
-  if (!K_pool || !M || !rule || !a16(K_pool)) return KVS_ERR_ARG;
+  if (!K_pool || !M || (N > 0 && !rule) || !a16(K_pool)) return KVS_ERR_ARG;
   if (k_dtype != KVS_F32 && k_dtype != KVS_BF16) return KVS_ERR_DTYPE;
   if (L < 1 || H_q < 1 || H_kv < 1 || N < 0 || pool_size < 1 || pi < 0 || q_s < 0 || q_e < q_s)
     return KVS_ERR_ARG;
@@ -222,9 +222,10 @@ size_t kvs_meank_score_workspace(int32_t L, int32_t H_q, int32_t H_kv, int64_t M
 kvs_status kvs_meank_score(const void* Q, const void* index, int32_t L, int32_t H_q, int32_t H_kv,
                            int32_t D, int64_t Mq, int64_t nB, int64_t n_sink, int64_t n_recent,
                            float* R, void* ws, size_t ws_bytes, void* stream) {
-  if (!Q || !index || !R || !a16(Q) || !a16(index)) return KVS_ERR_ARG;
   if (L < 1 || H_q < 1 || H_kv < 1 || Mq < 0 || nB < 0 || n_sink < 0 || n_recent < 0)
     return KVS_ERR_ARG;
+  // Q is empty when Mq = 0 (every R_b is then 0), the index and R when nB = 0
+  if ((Mq > 0 && !Q) || (nB > 0 && (!index || !R)) || !a16(Q) || !a16(index)) return KVS_ERR_ARG;
   if (H_q % H_kv != 0 || numel4(L, H_q, Mq, D) < 0 || numel4(L, H_kv, nB, D) < 0 ||
       (int64_t)L * H_kv > 65535 || nB > kMaxIndex)
     return KVS_ERR_SHAPE;
@@ -272,8 +273,8 @@ size_t kvs_window_score_workspace(int32_t L, int32_t H_q, int32_t H_kv, int64_t 
 kvs_status kvs_window_score(const void* K, const void* Qw, int32_t L, int32_t H_q, int32_t H_kv,
                             int32_t D, int64_t N, int64_t W, int64_t pi, int64_t q_s, int64_t q_e,
                             float* score, void* ws, size_t ws_bytes, void* stream) {
-  if (!K || !Qw || !score || !a16(K) || !a16(Qw)) return KVS_ERR_ARG;
   if (L < 1 || H_q < 1 || H_kv < 1 || N < 0 || W < 1 || pi < 0 || q_s < 0 || q_e < q_s) return KVS_ERR_ARG;
+  if (!Qw || (N > 0 && (!K || !score)) || !a16(K) || !a16(Qw)) return KVS_ERR_ARG;   // K, score empty when N = 0
   if (H_q % H_kv != 0 || N > kMaxIndex || numel4(L, H_kv, N, D) < 0 || numel4(L, H_q, W, D) < 0 ||
       (int64_t)L * H_kv > 65535 || (int64_t)(H_q / H_kv) * W > (int64_t)1 << 24 ||
       !grid_ok(cdiv((int64_t)(H_q / H_kv) * W, 256) * L * H_kv) || !grid_ok(cdiv(N, 256) * L * H_kv) ||

@@ -56,6 +56,10 @@ int main(void) {
   CHECK(kvs_rule_score(F, 1, F, 2, 4, 2, 128, 1024, 16, 992, 1024, F, F, ws - 1, NULL), KVS_ERR_WORKSPACE);
   CHECK(kvs_rule_score(F, 1, F, 2, 4, 2, 128, (int64_t)1 << 31, 16, 992, 1024, F, F, ws, NULL), KVS_ERR_SHAPE);
   CHECK(kvs_rule_score(F, 1, F, 2, 4, 2, 128, 0, 16, 992, 1024, F, F, ws, NULL), KVS_OK);   /* nothing launched */
+  CHECK(kvs_rule_score(NULL, 1, F, 2, 4, 2, 128, 0, 16, 992, 1024, NULL, F, ws, NULL), KVS_OK); /* empty K, rule */
+  CHECK(kvs_rule_score(F, 1, NULL, 2, 4, 2, 128, 0, 16, 992, 1024, F, F, ws, NULL), KVS_ERR_ARG); /* M never empty */
+  CHECK(kvs_meank_score(NULL, NULL, 2, 8, 2, 128, 0, 0, 4, 7, NULL, NULL, 0, NULL), KVS_OK);  /* nB = 0 */
+  CHECK(kvs_meank_score(NULL, F, 2, 8, 2, 128, 5, 300, 4, 7, F, F, 1 << 20, NULL), KVS_ERR_ARG);
   CHECK(kvs_rule_score_paged(F, 1, NULL, 2048, F, 2, 4, 2, 128, 1024, 16, 992, 1024, F, F, ws, NULL), KVS_ERR_ARG);
   CHECK(kvs_rule_score_paged(F, 1, F, 0, F, 2, 4, 2, 128, 1024, 16, 992, 1024, F, F, ws, NULL), KVS_ERR_ARG);
   CHECK(kvs_rule_score_paged(F, 1, F, 2048, F, 2, 4, 3, 128, 1024, 16, 992, 1024, F, F, ws, NULL), KVS_ERR_SHAPE);

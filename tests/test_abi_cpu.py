@@ -75,6 +75,8 @@ def test_rule_rejections(lib):
     assert call(wsb=ws - 1) == 5
     assert call(N=1 << 31) == 2
     assert call(N=0) == 0                   # empty input: nothing to do, nothing launched
+    assert call(N=0, K=None, rule=None) == 0   # an empty tensor may come as NULL
+    assert call(K=None) == 1 and call(rule=None) == 1
 
 
 def test_topk_slot_meank_rerope_rejections(lib):

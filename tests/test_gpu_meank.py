@@ -258,6 +258,18 @@ def test_meank_score_shapes(L, H_q, H_kv, Mq, nB, sink, recent, D):
     check_score(Q, index, sink, recent, f"R D{D} L{L} Hq{H_q} Hkv{H_kv} Mq{Mq} nB{nB}")
 
 
+def test_meank_score_without_query_tokens_is_zero():
+    """No query tokens (an empty Q, passed as NULL): every R_b is 0, as the oracle's empty sum."""
+    Q = torch.empty((2, 8, 0, 128), dtype=torch.bfloat16, device=DEV)
+    index = W.index_like(2, 2, 100, 128, 33, DEV)
+    R = torch.full((100,), 7.0, device=DEV)
+    kvs.kvs_meank_score(Q, index, 4, 8, R=R)
+    torch.cuda.synchronize()
+    assert torch.all(R == 0)
+    want = oracle.meank_score(host(Q), host(index), 4, 8)
+    assert np.all(want == 0)
+
+
 def test_meank_score_d64_peaked_and_full_extent():
     """D = 64 with a peaked softmax (index spread 1.0), and one (layer, KV head) at meank-256k's
     per-group extent (2560 query rows x 8124 candidate blocks)."""
