@@ -52,3 +52,60 @@ def test_noalloc_equals_workspace_call_over_consecutive_calls(concentrated):
         assert g_nk == o_nk
         np.testing.assert_array_equal(g_keep, o_keep.astype(np.uint8))
         np.testing.assert_array_equal(g_idx, o_idx)
+
+
+def test_noalloc_on_a_side_stream():
+    """On a stream of its own (not the default one) the entry point finds that stream's device and its
+    copy of the static array; the result equals the workspace call's."""
+    n, f0, f1, C = 92160, (0, 64), (92096, 92160), 8192
+    score = W.scores_with_ties(n, 320, 6).to(DEV)
+    ref = _outputs(n)
+    kvs.kvs_topk_select(score, f0, f1, C, *ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    got = _outputs(n)
+    with torch.cuda.stream(side):
+        kvs.kvs_topk_select_noalloc(score, f0, f1, C, *got)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g_keep, g_idx, g_nk = _host(*got)
+    r_keep, r_idx, r_nk = _host(*ref)
+    assert g_nk == r_nk
+    np.testing.assert_array_equal(g_keep, r_keep)
+    np.testing.assert_array_equal(g_idx, r_idx)
+
+
+def test_noalloc_replays_in_a_graph():
+    """Captured in a HIP graph (the caller it is for) and replayed on fresh scores written into the
+    captured buffer, with eager calls of both entry points between the replays: every replay equals
+    the eager selection bit for bit."""
+    n, f0, f1, C = 92160, (0, 64), (92096, 92160), 8192
+    score = torch.empty(n, dtype=torch.float32, device=DEV)
+    got = _outputs(n)
+    score.copy_(W.scores_with_ties(n, 330, None).to(DEV))
+    side = torch.cuda.Stream()                          # warm up off the capture stream first
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        kvs.kvs_topk_select_noalloc(score, f0, f1, C, *got)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        kvs.kvs_topk_select_noalloc(score, f0, f1, C, *got)
+    torch.cuda.synchronize()
+    for rep, (seed, levels) in enumerate(((331, None), (332, 4), (333, 50))):
+        print(f"[noalloc] graph replay {rep}", flush=True)
+        score.copy_(W.scores_with_ties(n, seed, levels).to(DEV))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        g_keep, g_idx, g_nk = _host(*got)
+        ref = _outputs(n)
+        kvs.kvs_topk_select(score, f0, f1, C, *ref)
+        eager = _outputs(n)
+        kvs.kvs_topk_select_noalloc(score, f0, f1, C, *eager)
+        torch.cuda.synchronize()
+        for keep, idx, nk in (_host(*ref), _host(*eager)):
+            assert g_nk == nk
+            np.testing.assert_array_equal(g_keep, keep)
+            np.testing.assert_array_equal(g_idx, idx)
