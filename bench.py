@@ -475,6 +475,9 @@ def main():
                          "Mean-K append, working-set update)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run one 4 GiB device copy (for HBM counter scaling)")
+    ap.add_argument("--no-power-sample", action="store_true",
+                    help="skip reading board power and clock with amd-smi (it starts a child process: "
+                         "leave it out under a counter-collecting profiler)")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library runs on one device and has no multi-GPU mode "
@@ -512,7 +515,7 @@ def main():
         del nr
     # board power and clock while the dominant call runs back to back (after the timed steps)
     dom_call = max(per_call, key=lambda k: per_call[k])
-    psample = power_sample(dict(s.calls())[dom_call], per_call[dom_call])
+    psample = None if a.no_power_sample else power_sample(dict(s.calls())[dom_call], per_call[dom_call])
     if a.copy_calibration:
         x = torch.empty(1 << 31, dtype=torch.int16, device=dev)
         y = torch.empty_like(x)
