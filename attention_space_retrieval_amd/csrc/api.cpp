@@ -141,6 +141,8 @@ kvs_status kvs_rule_score_paged(const void* K_pool, int32_t k_dtype, const int64
                                     rule, ws, as_stream(stream)));
 }
 
+int64_t kvs_rule_score_wait_limit(int64_t polls) { return kvs_rule_fold_spin(polls); }
+
 size_t kvs_topk_workspace(int64_t n) {
   if (n < 0 || n > kMaxIndex) return 0;
   return kvs_topk_ws_bytes(n);

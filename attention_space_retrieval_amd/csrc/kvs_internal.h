@@ -91,6 +91,9 @@ hipError_t kvs_launch_rule(const void* K, int dtype, const int64_t* slots, int64
                            const float* M, int L, int H_q, int H_kv, int D, int64_t N, int64_t pi,
                            int64_t q_s, int64_t q_e, float* rule, void* ws, hipStream_t st);
 size_t kvs_rule_ws_bytes(int L, int H_q, int H_kv, int64_t N);
+// Sets the fold's bounded wait (polls; < 0: every chunk takes the spill path);
+// returns the previous value.
+int64_t kvs_rule_fold_spin(int64_t polls);
 
 hipError_t kvs_launch_topk(const float* score, int64_t n, int64_t f0b, int64_t f0e, int64_t f1b,
                            int64_t f1e, int64_t n_forced, int64_t c_star, uint8_t* keep_mask,

@@ -30,6 +30,7 @@ _SIGNATURES = [
     ("kvs_rule_score", _I32, [_P, _I32, _P, _I32, _I32, _I32, _I32, _I64, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     ("kvs_rule_score_paged", _I32, [_P, _I32, _P, _I64, _P, _I32, _I32, _I32, _I32, _I64, _I64, _I64,
                                     _I64, _P, _P, _SZ, _P]),
+    ("kvs_rule_score_wait_limit", _I64, [_I64]),
     ("kvs_window_score_workspace", _SZ, [_I32, _I32, _I32, _I64, _I64]),
     ("kvs_window_score", _I32, [_P, _P, _I32, _I32, _I32, _I32, _I64, _I64, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     ("kvs_topk_workspace", _SZ, [_I64]),
@@ -175,6 +176,12 @@ def kvs_rule_score_paged(K_pool, slots, M, pi, q_s, q_e, rule=None, ws=None):
         _ptr(K_pool), _dtype_code(K_pool), _ptr(slots), pool_size, _ptr(M), L, H_q, H_kv, D, N, int(pi),
         int(q_s), int(q_e), _ptr(rule), _ptr(ws), _nbytes(ws), _stream(K_pool)))
     return rule
+
+
+def kvs_rule_score_wait_limit(polls):
+    """Bounded wait of the rule scorer's fold in polls (< 0: every chunk takes the spill path);
+    returns the previous setting.  Process-wide; a diagnostic and test setting."""
+    return int(load().kvs_rule_score_wait_limit(int(polls)))
 
 
 def kvs_window_score_workspace(L, H_q, H_kv, W, N):

@@ -122,6 +122,21 @@ kvs_status kvs_rule_score_paged(const void* K_pool, int32_t k_dtype, const int64
                                 int64_t q_e, float* rule, void* ws, size_t ws_bytes,
                                 void* stream);
 
+/*
+ * Bounded wait of the rule scorer's fold -- a diagnostic and test setting;
+ * the default suits every size.  With bf16 keys and G <= 8 both rule-score
+ * calls run as a work queue: a workgroup keeps a chunk's logits on chip and
+ * folds its G heads into one value per position once every chunk of its
+ * (layer, KV head) group has published its softmax partials.  A chunk whose
+ * group is not complete when its workgroup gets to it is spilled and summed
+ * by the column pass instead, with the same bits as a result.  polls >= 0:
+ * the one blocking wait (at the end, once every chunk is claimed) polls at
+ * most that often before it spills; polls < 0: no chunk is folded.
+ * Process-wide, for calls launched after it returns.  Returns the previous
+ * value.
+ */
+int64_t kvs_rule_score_wait_limit(int64_t polls);
+
 /* Workspace bytes kvs_window_score needs for these sizes. */
 size_t kvs_window_score_workspace(int32_t L, int32_t H_q, int32_t H_kv, int64_t W, int64_t N);
 

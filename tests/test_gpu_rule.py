@@ -176,6 +176,56 @@ def test_rule_all_forced_and_determinism():
     assert torch.equal(a, b)
 
 
+def _spilled_fraction(ws, L, H_q, N):
+    """The workspace starts with the [L*H_q, N] float32 spill; filled with 0xff before a call, the
+    share of it written afterwards is the share of positions whose chunk took the spill path."""
+    spill = ws[: L * H_q * N * 4].view(torch.int32)
+    return float((spill != -1).sum().item()) / (L * H_q * N)
+
+
+@pytest.mark.parametrize("L,H_q,H_kv,D,N,paged", [
+    (2, 32, 8, 128, 5000, False),    # G = 4, ragged tail
+    (3, 40, 8, 128, 4097, False),    # G = 5, one-row tail chunk
+    (1, 16, 2, 128, 777, True),      # G = 8, read through a slot map
+    (2, 16, 4, 64, 3000, True),      # D = 64
+    (1, 8, 2, 128, 131073, False),   # many chunks per group
+])
+def test_rule_fold_equals_spill_path(L, H_q, H_kv, D, N, paged):
+    """The bf16 scorer folds each chunk's G heads on chip once its group's normalisers are out, and
+    spills the chunk when they are not; the column pass finishes a spilled chunk with the fold's
+    own arithmetic.  Every chunk spilled (wait limit < 0), no waiting at all (limit 0) and the
+    default all give the same bits, and the default folds (nothing written to the spill)."""
+    if paged:
+        _, pool, slots, M = _paged_inputs(L, H_q, H_kv, D, N, N + 500, "bf16", 21, dead=(3,))
+        run = lambda ws: kvs.kvs_rule_score_paged(pool, slots, M, 5, N - 70, N - 10, ws=ws)
+    else:
+        K = W.normal((L, H_kv, N, D), 21, W.T_K, "bf16", DEV)
+        M = W.memory_vectors(L, H_q, D, 21, DEV)
+        run = lambda ws: kvs.kvs_rule_score(K, M, 5, N - 70, N - 10, ws=ws)
+    need = kvs.kvs_rule_score_workspace(L, H_q, H_kv, N)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    out = {}
+    prev = kvs.kvs_rule_score_wait_limit(-1)
+    try:
+        for limit in (-1, 0, prev):
+            kvs.kvs_rule_score_wait_limit(limit)
+            ws.fill_(0xFF)
+            out[limit] = run(ws).clone()
+            torch.cuda.synchronize()
+            if limit == -1:
+                assert _spilled_fraction(ws, L, H_q, N) == 1.0
+            if limit == prev and N <= 5000:
+                assert _spilled_fraction(ws, L, H_q, N) == 0.0
+    finally:
+        kvs.kvs_rule_score_wait_limit(prev)
+    for limit in (0, prev):
+        assert torch.equal(out[limit].view(torch.int32), out[-1].view(torch.int32)), f"limit {limit}"
+    if not paged:
+        F = oracle.forced_mask(N, 5, N - 70, N - 10)
+        want = oracle.rule_score(host(K), host(M), 5, N - 70, N - 10)
+        assert_rel(out[prev].cpu().numpy()[~F], want[~F], RULE_RTOL, "fold path")
+
+
 @pytest.mark.parametrize("name", ["rule-8b", "rule-14b"])
 def test_rule_full_size(name):
     """Full configuration in the benchmark's launch shape, every output against the oracle."""
@@ -191,6 +241,14 @@ def test_rule_full_size(name):
     np.testing.assert_allclose(M.cpu().numpy(), Mo, atol=1e-5)
     print(f"[{name}] oracle rule score", flush=True)
     got, want = check_rule(inp["K"], M, c["pi"], c["q_s"], c["q_e"], name, M_oracle=Mo)
+    ws = torch.full((kvs.kvs_rule_score_workspace(c["L"], c["H_q"], c["H_kv"], c["N"]),), 0xFF,
+                    dtype=torch.uint8, device=DEV)
+    again = kvs.kvs_rule_score(inp["K"], M, c["pi"], c["q_s"], c["q_e"], ws=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(again.cpu().numpy().view(np.int32), got.view(np.int32))
+    spilled = _spilled_fraction(ws, c["L"], c["H_q"], c["N"])
+    print(f"[{name}] share of positions spilled: {spilled:.4f}", flush=True)
+    assert spilled < 0.05
     # top-k and slot redirect in the benchmark's launch shape (workspace: the multi-workgroup path
     # above 32768 scores), bit for bit against the oracle's selection of the same float32 scores
     keep, idx, nk = kvs.kvs_topk_select(torch.from_numpy(got).to(DEV), (0, c["pi"]),
@@ -244,14 +302,23 @@ def test_rule_paged_against_oracle(dtype, L, H_q, H_kv, D, N, pool_size, dead):
 
 @pytest.mark.parametrize("name", ["rule-8b", "rule-14b"])
 def test_rule_paged_full_size_equals_dense(name):
-    """At full size, the pool read through a permuted slot map gives the dense scores bit for bit."""
+    """At full size, the pool read through a permuted slot map gives the dense scores.  The two
+    calls score the same keys in chunks of different lengths (the paged chunk is shorter, to keep
+    three workgroups per CU beside its slot array), so the softmax partials merge in a different
+    grouping: the scores agree to float32 summation order, 1e-5 relative -- a wrong row would be
+    off by orders of magnitude -- and the forced positions are exactly 0 in both."""
     c = W.config(name)
     L, H_q, H_kv, D, N = c["L"], c["H_q"], c["H_kv"], c["D"], c["N"]
     K, pool, slots, M = _paged_inputs(L, H_q, H_kv, D, N, N + 4096, "bf16", 16)
     dense = kvs.kvs_rule_score(K, M, c["pi"], c["q_s"], c["q_e"])
     paged = kvs.kvs_rule_score_paged(pool, slots, M, c["pi"], c["q_s"], c["q_e"])
     torch.cuda.synchronize()
-    assert torch.equal(dense, paged)
+    d, p = dense.cpu().numpy().astype(np.float64), paged.cpu().numpy().astype(np.float64)
+    F = oracle.forced_mask(N, c["pi"], c["q_s"], c["q_e"])
+    assert np.all(d[F] == 0) and np.all(p[F] == 0)
+    rel = np.abs(p[~F] - d[~F]) / d[~F]
+    print(f"[{name}] paged vs dense: max relative difference {rel.max():.2e}", flush=True)
+    assert rel.max() <= 1e-5
     del K, pool
 
 
