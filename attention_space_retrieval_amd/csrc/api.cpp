@@ -161,7 +161,26 @@ kvs_status kvs_topk_select(const float* score, int64_t n, int64_t f0_begin, int6
   if (need && ((uintptr_t)ws & 3)) return KVS_ERR_ARG;
   if (!need) ws = nullptr;
   return hip_status(kvs_launch_topk(score, n, f0_begin, f0_end, f1_begin, f1_end, n_forced, c_star,
-                                    keep_mask, keep_idx, n_kept, ws, as_stream(stream)));
+                                    keep_mask, keep_idx, n_kept, ws, as_stream(stream), nullptr, 0, nullptr));
+}
+
+kvs_status kvs_topk_select_redirect(const float* score, int64_t n, int64_t f0_begin, int64_t f0_end,
+                                    int64_t f1_begin, int64_t f1_end, int64_t C, uint8_t* keep_mask,
+                                    int32_t* keep_idx, int64_t* n_kept, const int64_t* slot_in,
+                                    int64_t dead_slot, int64_t* slot_out, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  int64_t n_forced = 0, c_star = 0;
+  const kvs_status a = topk_args(score, n, f0_begin, f0_end, f1_begin, f1_end, C, keep_mask, keep_idx,
+                                 n_kept, &n_forced, &c_star);
+  if (a != KVS_OK) return a;
+  if (n > 0 && (!slot_in || !slot_out)) return KVS_ERR_ARG;
+  const size_t need = kvs_topk_ws_bytes(n);
+  if (need && ws && ws_bytes < need) return KVS_ERR_WORKSPACE;
+  if (need && ((uintptr_t)ws & 3)) return KVS_ERR_ARG;
+  if (!need) ws = nullptr;
+  return hip_status(kvs_launch_topk(score, n, f0_begin, f0_end, f1_begin, f1_end, n_forced, c_star,
+                                    keep_mask, keep_idx, n_kept, ws, as_stream(stream), slot_in, dead_slot,
+                                    n > 0 ? slot_out : nullptr));
 }
 
 int64_t kvs_topk_noalloc_max(void) { return kvs_topk_noalloc_max_n(); }

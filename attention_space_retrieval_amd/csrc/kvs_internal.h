@@ -95,9 +95,11 @@ size_t kvs_rule_ws_bytes(int L, int H_q, int H_kv, int64_t N);
 // returns the previous value.
 int64_t kvs_rule_fold_spin(int64_t polls);
 
+// slot_out != nullptr: the emit also writes slot_out[j] = kept ? slot_in[j] : dead_slot.
 hipError_t kvs_launch_topk(const float* score, int64_t n, int64_t f0b, int64_t f0e, int64_t f1b,
                            int64_t f1e, int64_t n_forced, int64_t c_star, uint8_t* keep_mask,
-                           int32_t* keep_idx, int64_t* n_kept, void* ws, hipStream_t st);
+                           int32_t* keep_idx, int64_t* n_kept, void* ws, hipStream_t st,
+                           const int64_t* slot_in, int64_t dead_slot, int64_t* slot_out);
 size_t kvs_topk_ws_bytes(int64_t n);
 // Same selection with the multi-workgroup state in the library's own static
 // device array (no workspace); n <= kvs_topk_noalloc_max_n().

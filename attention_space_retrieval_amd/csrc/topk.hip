@@ -31,6 +31,19 @@ struct Forced {
   __device__ bool operator()(int j) const { return (j >= f0b && j < f0e) || (j >= f1b && j < f1e); }
 };
 
+// The slot-map redirect of the layout layer, written by the multi-workgroup
+// emit itself when asked for (out != nullptr): out[j] = kept ? in[j] : dead.
+// in and out may be one array (each position is read, then written, by the
+// same thread).
+struct Redirect {
+  const int64_t* in;
+  int64_t dead;
+  int64_t* out;
+  __device__ __forceinline__ void operator()(int64_t j, bool keep) const {
+    if (out) out[j] = keep ? in[j] : dead;
+  }
+};
+
 // Keys held in registers, for n <= 1024 * KPT: thread t owns positions
 // j = 1024u + t (u < KPT), so the scores are read once, with every load of a
 // thread in flight together, and no pass after that touches memory.  The key
@@ -577,10 +590,17 @@ __global__ __launch_bounds__(kMwThreads) void topk_mw_count(MwArgs a) {
 }
 
 __global__ __launch_bounds__(kMwThreads) void topk_mw_emit(MwArgs a, uint8_t* __restrict__ keep_mask,
-                                                           int32_t* __restrict__ keep_idx) {
+                                                           int32_t* __restrict__ keep_idx, Redirect rd) {
   __shared__ uint32_t cnt[2][kMwKeys][kMwWaves];
   __shared__ uint32_t base[2];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int64_t slice0 = (int64_t)blockIdx.x * kMwSlice;
+  // the slots to redirect, fetched before anything waits
+  int64_t sv[kMwKeys];
+  if (rd.out) {
+#pragma unroll
+    for (int u = 0; u < kMwKeys; ++u) sv[u] = rd.in[min(slice0 + u * kMwThreads + t, (int64_t)a.n - 1)];
+  }
   uint32_t kT, k_tie;
   mw_threshold(a, kT, k_tie);
   uint32_t key[kMwKeys];
@@ -616,7 +636,6 @@ __global__ __launch_bounds__(kMwThreads) void topk_mw_emit(MwArgs a, uint8_t* __
       }
   }
   __syncthreads();
-  const int64_t slice0 = (int64_t)blockIdx.x * kMwSlice;
 #pragma unroll
   for (int u = 0; u < kMwKeys; ++u) {
     const int64_t j = slice0 + u * kMwThreads + t;
@@ -625,7 +644,10 @@ __global__ __launch_bounds__(kMwThreads) void topk_mw_emit(MwArgs a, uint8_t* __
     const uint32_t def_before = cnt[0][u][wave], tie_before = cnt[1][u][wave];
     const bool keep = (key[u] > kT) | (tie & (tie_before + rank_below(bt, lane) < k_tie));
     const uint64_t bk = __ballot(keep);
-    if (j < a.n) keep_mask[j] = keep ? 1 : 0;
+    if (j < a.n) {
+      keep_mask[j] = keep ? 1 : 0;
+      if (rd.out) rd.out[j] = keep ? sv[u] : rd.dead;
+    }
     if (keep) keep_idx[def_before + min(tie_before, k_tie) + rank_below(bk, lane)] = (int32_t)j;
   }
 }
@@ -633,9 +655,13 @@ __global__ __launch_bounds__(kMwThreads) void topk_mw_emit(MwArgs a, uint8_t* __
 // C* >= |H|: everything is kept.
 __global__ __launch_bounds__(256) void keep_all_kernel(int n, uint8_t* __restrict__ keep_mask,
                                                        int32_t* __restrict__ keep_idx,
-                                                       int64_t* __restrict__ n_kept) {
+                                                       int64_t* __restrict__ n_kept, Redirect rd) {
   const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j < n) { keep_mask[j] = 1; keep_idx[j] = j; }
+  if (j < n) {
+    keep_mask[j] = 1;
+    keep_idx[j] = j;
+    rd(j, true);
+  }
   if (j == 0) *n_kept = n;
 }
 
@@ -659,23 +685,35 @@ size_t kvs_topk_ws_bytes(int64_t n) {
 
 hipError_t kvs_launch_topk(const float* score, int64_t n, int64_t f0b, int64_t f0e, int64_t f1b,
                            int64_t f1e, int64_t n_forced, int64_t c_star, uint8_t* keep_mask,
-                           int32_t* keep_idx, int64_t* n_kept, void* ws, hipStream_t st) {
+                           int32_t* keep_idx, int64_t* n_kept, void* ws, hipStream_t st,
+                           const int64_t* slot_in, int64_t dead_slot, int64_t* slot_out) {
+  const Redirect rd{slot_in, dead_slot, slot_out};
   if (c_star >= n - n_forced) {   // includes n == 0: still writes n_kept
     const unsigned blocks = n > 0 ? ceil_div(n, 256) : 1u;
     hipLaunchKernelGGL(keep_all_kernel, dim3(blocks), dim3(256), 0, st, (int)n, keep_mask, keep_idx,
-                       n_kept);
+                       n_kept, rd);
     return hipGetLastError();
   }
   Forced f{(int)f0b, (int)f0e, (int)f1b, (int)f1e};
+  // One workgroup selects up to 32768 scores (or more without a workspace); there the slot
+  // loads would queue behind a single workgroup, so the redirect runs as its own kernel after
+  // it.  The multi-workgroup emit writes it itself.
 #define TOPK_REG(KPT)                                                                               \
   hipLaunchKernelGGL(topk_reg_kernel<KPT>, dim3(1), dim3(kThreads), 0, st, score, (int)n, f, (int)c_star, \
                      (int)n_forced, keep_mask, keep_idx, n_kept)
-  if (n <= 8 * kThreads) TOPK_REG(8);
-  else if (n <= 32 * kThreads) TOPK_REG(32);
+  if (n <= 8 * kThreads || n <= 32 * kThreads || ws == nullptr) {
+    if (n <= 8 * kThreads) TOPK_REG(8);
+    else if (n <= 32 * kThreads) TOPK_REG(32);
+    else
+      hipLaunchKernelGGL(topk_stream_kernel, dim3(1), dim3(kThreads), 0, st, score, (int)n, f,
+                         (int)c_star, (int)n_forced, keep_mask, keep_idx, n_kept);
+    if (slot_out != nullptr) {
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      return kvs_launch_slotmap(slot_in, keep_mask, n, dead_slot, slot_out, st);
+    }
+  }
 #undef TOPK_REG
-  else if (ws == nullptr)
-    hipLaunchKernelGGL(topk_stream_kernel, dim3(1), dim3(kThreads), 0, st, score, (int)n, f,
-                       (int)c_star, (int)n_forced, keep_mask, keep_idx, n_kept);
   else {
     MwArgs a{score, (int)n, f, (int)c_star, static_cast<uint32_t*>(ws)};
     const dim3 grid((unsigned)((n + kMwSlice - 1) / kMwSlice)), block(kMwThreads);
@@ -685,7 +723,7 @@ hipError_t kvs_launch_topk(const float* score, int64_t n, int64_t f0b, int64_t f
       for (int p = 0; p < 4; ++p) hipLaunchKernelGGL(topk_mw_pass, grid, block, 0, st, a, p);
     }
     hipLaunchKernelGGL(topk_mw_count, grid, block, 0, st, a);
-    hipLaunchKernelGGL(topk_mw_emit, grid, block, 0, st, a, keep_mask, keep_idx);
+    hipLaunchKernelGGL(topk_mw_emit, grid, block, 0, st, a, keep_mask, keep_idx, rd);
   }
   return hipGetLastError();
 }
@@ -755,7 +793,8 @@ hipError_t kvs_launch_topk_noalloc(const float* score, int64_t n, int64_t f0b, i
     const hipError_t e = scratch_for(st, &ws);
     if (e != hipSuccess) return e;
   }
-  return kvs_launch_topk(score, n, f0b, f0e, f1b, f1e, n_forced, c_star, keep_mask, keep_idx, n_kept, ws, st);
+  return kvs_launch_topk(score, n, f0b, f0e, f1b, f1e, n_forced, c_star, keep_mask, keep_idx, n_kept, ws, st,
+                         nullptr, 0, nullptr);
 }
 
 hipError_t kvs_launch_slotmap(const int64_t* in, const uint8_t* mask, int64_t N, int64_t dead,

@@ -35,6 +35,8 @@ _SIGNATURES = [
     ("kvs_window_score", _I32, [_P, _P, _I32, _I32, _I32, _I32, _I64, _I64, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     ("kvs_topk_workspace", _SZ, [_I64]),
     ("kvs_topk_select", _I32, [_P, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
+    ("kvs_topk_select_redirect", _I32, [_P, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _I64, _P, _P,
+                                        _SZ, _P]),
     ("kvs_topk_noalloc_max", _I64, []),
     ("kvs_topk_select_noalloc", _I32, [_P, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P]),
     ("kvs_slotmap_redirect", _I32, [_P, _P, _I64, _I64, _P, _P]),
@@ -238,6 +240,38 @@ def kvs_topk_select(score, f0, f1, C, keep_mask=None, keep_idx=None, n_kept=None
         _ptr(score), n, f0[0], f0[1], f1[0], f1[1], C, _ptr(keep_mask), _ptr(keep_idx),
         _ptr(n_kept), _ptr(ws), _nbytes(ws), _stream(score)))
     return keep_mask, keep_idx, n_kept
+
+
+def kvs_topk_select_redirect(score, f0, f1, C, slot_in, dead_slot, keep_mask=None, keep_idx=None, n_kept=None,
+                             slot_out=None, ws=None, single_workgroup=False):
+    """kvs_topk_select with the slot-map redirect written by the same launch: returns
+    (keep_mask, keep_idx, n_kept, slot_out), slot_out[j] = slot_in[j] if kept else dead_slot
+    (slot_out may be slot_in itself).  single_workgroup as in kvs_topk_select."""
+    _dev(score, slot_in, keep_mask, keep_idx, n_kept, slot_out, ws)
+    if score.dtype != torch.float32:
+        raise TypeError("score must be float32")
+    if slot_in.dtype != torch.int64:
+        raise TypeError("slot_in must be int64")
+    n = score.numel()
+    dev = score.device
+    keep_mask = torch.empty(n, dtype=torch.uint8, device=dev) if keep_mask is None else keep_mask
+    keep_idx = torch.empty(n, dtype=torch.int32, device=dev) if keep_idx is None else keep_idx
+    n_kept = torch.empty(1, dtype=torch.int64, device=dev) if n_kept is None else n_kept
+    slot_out = torch.empty_like(slot_in) if slot_out is None else slot_out
+    _need(keep_mask.dtype == torch.uint8 and keep_mask.numel() == n, "keep_mask must be uint8 [n]")
+    _need(keep_idx.dtype == torch.int32 and keep_idx.numel() >= n, "keep_idx must be int32 [n]")
+    _need(n_kept.dtype == torch.int64 and n_kept.numel() >= 1, "n_kept must be int64 [1]")
+    _need(slot_in.numel() == n and slot_out.numel() == n and slot_out.dtype == torch.int64,
+          "slot_in and slot_out must be int64 [n]")
+    need = kvs_topk_workspace(n)
+    if single_workgroup:
+        ws = None
+    elif need:
+        ws = _workspace(need, dev, ws)
+    _check("kvs_topk_select_redirect", load().kvs_topk_select_redirect(
+        _ptr(score), n, f0[0], f0[1], f1[0], f1[1], C, _ptr(keep_mask), _ptr(keep_idx), _ptr(n_kept),
+        _ptr(slot_in), int(dead_slot), _ptr(slot_out), _ptr(ws), _nbytes(ws), _stream(score)))
+    return keep_mask, keep_idx, n_kept, slot_out
 
 
 def kvs_topk_noalloc_max():

@@ -57,16 +57,18 @@ WORKLOADS = {"rule-8b+meank-256k": ("rule-8b", "meank-256k"),
 TOPK_MW = ["topk_mw_init", "topk_mw_minmax", "topk_mw_pass*4", "topk_mw_count", "topk_mw_emit"]
 CALL_KERNELS = {
     "kvs_qmem_update": ["qmem_kernel<128, true>"],
-    "kvs_rule_score": ["rule_logits_mfma<128, 1, false>", "rule_lse_merge", "rule_colsum"],
-    "kvs_topk_select[rule]": ["topk_reg_kernel<32>"],
+    # bf16 keys, G <= 8: the work-queue fold; the last template argument is the workgroups per CU
+    # its LDS allows (3 at G = 4, 2 at G = 5), the third the chunk length
+    "kvs_rule_score": ["rule_fold_reset", "rule_fold_queue<128, false, 1024, 3>", "rule_fold_colsum"],
+    # the redirect runs inside the multi-workgroup emit, and as its own kernel after a one-workgroup
+    # selection
+    "kvs_topk_select_redirect[rule]": ["topk_reg_kernel<32>", "slotmap_kernel"],
     "kvs_topk_select[meank]": ["topk_reg_kernel<8>"],
-    "kvs_slotmap_redirect": ["slotmap_kernel"],
     "kvs_meank_build": ["meank_build_raw<128>"],
     "kvs_meank_score": ["meank_pass<true, false, 4, 128>", "meank_pass<false, false, 4, 128>", "meank_reduce<false>"],
     "kvs_rerope_scatter": ["rerope_scatter_kernel<128>", "v_scatter_kernel<128>"],
-    # rows beyond the step (timed after it): the paged rule score's merge and column sum are the
-    # dense call's kernels on the same sizes
-    "kvs_rule_score_paged": ["rule_logits_mfma<128, 1, true>", "rule_lse_merge", "rule_colsum"],
+    # rows beyond the step (timed after it): the paged rule score takes 768-position chunks
+    "kvs_rule_score_paged": ["rule_fold_reset", "rule_fold_queue<128, true, 768, 3>", "rule_fold_colsum"],
     "kvs_window_score": [("meank_pass<true, true, 2, 128>", "meank_pass<true, true, 4, 128>"), "meank_lse_merge",
                          "meank_pass<false, true, 2, 128>",
                          "meank_reduce<true>"],
@@ -79,7 +81,8 @@ def call_kernels(workload):
     """CALL_KERNELS with the top-k kernels the workload's sizes select."""
     ck = dict(CALL_KERNELS)
     if workload == "rule-14b+meank-1m":
-        ck["kvs_topk_select[rule]"] = TOPK_MW                       # n = 92160
+        ck["kvs_rule_score"] = ["rule_fold_reset", "rule_fold_queue<128, false, 1024, 2>", "rule_fold_colsum"]
+        ck["kvs_topk_select_redirect[rule]"] = TOPK_MW              # n = 92160
         ck["kvs_topk_select[meank]"] = ["topk_reg_kernel<32>"]      # n = 32768 blocks
         # the 1M workspace keeps no V beside raw K (the scatter reads the packed staging buffers), so
         # the working-set update there moves K only
@@ -152,11 +155,9 @@ class Setup:
             ("kvs_qmem_update", lambda: kvs.kvs_qmem_update(self.spans[-1], c["lam"], self.M, False)),
             ("kvs_rule_score", lambda: kvs.kvs_rule_score(self.K, self.M, c["pi"], c["q_s"], c["q_e"],
                                                           rule=self.rule, ws=self.ws_rule)),
-            ("kvs_topk_select[rule]", lambda: kvs.kvs_topk_select(
-                self.rule, (0, c["pi"]), (c["q_s"], c["q_e"]), c["C"], self.keep_r, self.idx_r, self.nk_r,
-                ws=self.ws_topk_r)),
-            ("kvs_slotmap_redirect", lambda: kvs.kvs_slotmap_redirect(self.slots, self.keep_r, c["dead_slot"],
-                                                                      self.slots_out)),
+            ("kvs_topk_select_redirect[rule]", lambda: kvs.kvs_topk_select_redirect(
+                self.rule, (0, c["pi"]), (c["q_s"], c["q_e"]), c["C"], self.slots, c["dead_slot"], self.keep_r,
+                self.idx_r, self.nk_r, self.slots_out, ws=self.ws_topk_r)),
             ("kvs_meank_build", lambda: kvs.kvs_meank_build(self.Kraw, index=self.index)),
             ("kvs_meank_score", lambda: kvs.kvs_meank_score(self.Q, self.index, m["n_sink"], m["n_recent"],
                                                             R=self.R, ws=self.ws_mk)),
@@ -178,8 +179,7 @@ class Setup:
         return {
             "kvs_qmem_update": ("hbm", c["L"] * c["H_q"] * c["span"] * c["D"] * 2 + 2 * c["L"] * c["H_q"] * c["D"] * 4),
             "kvs_rule_score": ("hbm", LG_r * N * c["D"] * 2 + c["L"] * c["H_q"] * c["D"] * 4 + 4 * N),
-            "kvs_topk_select[rule]": ("hbm", 4 * N + N + 4 * c["C"]),
-            "kvs_slotmap_redirect": ("hbm", 17 * N),
+            "kvs_topk_select_redirect[rule]": ("hbm", 4 * N + N + 4 * c["C"] + 16 * N),
             "kvs_meank_build": ("hbm", m["L"] * m["H_kv"] * m["N"] * m["D"] * 2 + m["L"] * m["H_kv"] * nB * m["D"] * 2),
             "kvs_meank_score": ("mfma", 2.0 * m["Mq"] * m["H_q"] * m["L"] * cand * m["D"]),
             "kvs_topk_select[meank]": ("hbm", 4 * nB + nB + 4 * m["budget"]),
@@ -542,10 +542,9 @@ def main():
         r["traffic"] = None if t is None else round(t)
     dom = max(rows, key=lambda k: rows[k]["ms"])
     d = rows[dom]
-    rule_ms = sum(per_call[k] for k in ("kvs_qmem_update", "kvs_rule_score", "kvs_topk_select[rule]",
-                                         "kvs_slotmap_redirect"))
-    rule_bytes = sum(work[k][1] for k in ("kvs_qmem_update", "kvs_rule_score", "kvs_topk_select[rule]",
-                                          "kvs_slotmap_redirect"))
+    turn = ("kvs_qmem_update", "kvs_rule_score", "kvs_topk_select_redirect[rule]")
+    rule_ms = sum(per_call[k] for k in turn)
+    rule_bytes = sum(work[k][1] for k in turn)
     out = {
         "metric": METRIC,
         "value": tokens / (ms_per_step * 1e-3),

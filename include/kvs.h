@@ -189,6 +189,25 @@ kvs_status kvs_topk_select(const float* score, int64_t n, int64_t f0_begin, int6
                            void* stream);
 
 /*
+ * Top-k and slot-map redirect in one launch -- IntentKV Sec. 3.1, Eq. (1),
+ * and the layout layer's slot map S_r (abstract; Sec. 1): the selection of
+ * kvs_topk_select, bit for bit, whose emit also writes
+ *   slot_out[j] = keep_mask[j] ? slot_in[j] : dead_slot
+ * as kvs_slotmap_redirect would from the mask.  One eviction step of the
+ * rule mode is then this call after kvs_rule_score.  Above 32768 scores
+ * (with a workspace) the selection's own emit writes the slot map; a
+ * one-workgroup selection is followed by the redirect kernel instead.
+ *   slot_in, slot_out  [n] int64, device (may be the same array).
+ * Other arguments, workspace and errors as kvs_topk_select (KVS_ERR_ARG also
+ * for a null slot array when n > 0).
+ */
+kvs_status kvs_topk_select_redirect(const float* score, int64_t n, int64_t f0_begin, int64_t f0_end,
+                                    int64_t f1_begin, int64_t f1_end, int64_t C, uint8_t* keep_mask,
+                                    int32_t* keep_idx, int64_t* n_kept, const int64_t* slot_in,
+                                    int64_t dead_slot, int64_t* slot_out, void* ws, size_t ws_bytes,
+                                    void* stream);
+
+/*
  * Budgeted top-k that allocates nothing -- for callers that cannot allocate:
  * code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation.  The same selection as kvs_topk_select, bit for bit, with the

@@ -1,13 +1,13 @@
 /*
  * A plain C consumer of the library: device memory from hipMalloc, no PyTorch, every step through
  * the C ABI of kvs.h.  It runs an IntentKV rule turn (QueryMemory over three turns, rule score,
- * top-k with the forced set, slot redirect) and a KVMEM Mean-K step (index build, R_b, sink/recent
+ * top-k with the forced set, slot redirect, both also fused in one call) and a KVMEM Mean-K step (index build, R_b, sink/recent
  * + budget selection, re-RoPE scatter through a page table) on seeded synthetic inputs and checks
  * what holds exactly: unit-norm memory rows, sum(rule) = L*H_q, zeros on the forced sets, the
  * selection sizes, ascending valid top-C* selections of the scores returned, the slot map, the
  * index of a block against its mean, sum(R) = Mq, V pages copied bit for bit, K pair norms kept by
- * the rotation, the no-allocation top-k equal to the workspace one, and identical bits on a second
- * run.  Exit status = number of failed checks.
+ * the rotation, the no-allocation and the fused top-k equal to the workspace one, and identical
+ * bits on a second run.  Exit status = number of failed checks.
  */
 #include <hip/hip_runtime_api.h>
 #include <math.h>
@@ -132,6 +132,12 @@ static void rule_turn(int run, uint32_t* rule_bits_out) {
   int64_t* dslot2 = dalloc(N * 8);
   up(dslot, hslot, N * 8);
   KVS(kvs_slotmap_redirect(dslot, dkeep, N, -1, dslot2, st));
+  /* the selection and the redirect in one launch, into other buffers */
+  uint8_t* dkeep3 = dalloc(N);
+  int32_t* didx3 = dalloc(N * 4);
+  int64_t* dnk3 = dalloc(8);
+  int64_t* dslot3 = dalloc(N * 8);
+  KVS(kvs_topk_select_redirect(drule, N, 0, pi, q_s, q_e, C, dkeep3, didx3, dnk3, dslot, -1, dslot3, tws, tws_b, st));
   /* the no-allocation top-k on the same scores */
   uint8_t* dkeep2 = dalloc(N);
   int32_t* didx2 = dalloc(N * 4);
@@ -169,6 +175,21 @@ static void rule_turn(int run, uint32_t* rule_bits_out) {
   check_selection(hrule, N, 0, pi, q_s, q_e, C, hkeep, hidx, hnk, "rule top-k");
   CHECK(hnk2 == hnk && memcmp(hkeep2, hkeep, N) == 0 && memcmp(hidx2, hidx, hnk * 4) == 0,
         "no-allocation top-k differs from the workspace one");
+  {
+    uint8_t* k3 = malloc(N);
+    int32_t* i3 = malloc(N * 4);
+    int64_t n3, *s3 = malloc(N * 8);
+    down(k3, dkeep3, N);
+    down(i3, didx3, N * 4);
+    down(&n3, dnk3, 8);
+    down(s3, dslot3, N * 8);
+    CHECK(n3 == hnk && memcmp(k3, hkeep, N) == 0 && memcmp(i3, hidx, hnk * 4) == 0 &&
+              memcmp(s3, hslot2, N * 8) == 0,
+          "top-k with the redirect fused differs from the two calls");
+    free(k3);
+    free(i3);
+    free(s3);
+  }
   for (int64_t j = 0; j < N; ++j)
     CHECK(hslot2[j] == (hkeep[j] ? hslot[j] : -1), "slot %lld: %lld", (long long)j, (long long)hslot2[j]);
   memcpy(rule_bits_out, hrule, N * 4);
@@ -179,6 +200,7 @@ static void rule_turn(int run, uint32_t* rule_bits_out) {
   HIP(hipFree(dK)); HIP(hipFree(dQ)); HIP(hipFree(dM)); HIP(hipFree(ws)); HIP(hipFree(drule));
   HIP(hipFree(dkeep)); HIP(hipFree(didx)); HIP(hipFree(dnk)); HIP(hipFree(tws)); HIP(hipFree(dslot));
   HIP(hipFree(dslot2)); HIP(hipFree(dkeep2)); HIP(hipFree(didx2)); HIP(hipFree(dnk2));
+  HIP(hipFree(dkeep3)); HIP(hipFree(didx3)); HIP(hipFree(dnk3)); HIP(hipFree(dslot3));
   HIP(hipStreamDestroy(st));
 }
 

@@ -27,7 +27,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = header_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(kvs.ENTRY_POINTS) == names
@@ -90,6 +90,13 @@ def test_topk_slot_meank_rerope_rejections(lib):
     assert need >= 4 * (256 + 2 * 45)
     assert lib.kvs_topk_select(FAKE, 92160, 0, 64, 92096, 92160, 8192, FAKE, FAKE, FAKE, FAKE, need - 1,
                                None) == 5
+    # the fused redirect: the same checks, and both slot arrays when n > 0
+    R = lib.kvs_topk_select_redirect
+    assert R(None, 10, 0, 1, 5, 6, 3, FAKE, FAKE, FAKE, FAKE, -1, FAKE, None, 0, None) == 1
+    assert R(FAKE, 10, 0, 1, 5, 6, 3, FAKE, FAKE, FAKE, None, -1, FAKE, None, 0, None) == 1
+    assert R(FAKE, 10, 0, 1, 5, 6, 3, FAKE, FAKE, FAKE, FAKE, -1, None, None, 0, None) == 1
+    assert R(FAKE, 1 << 31, 0, 1, 5, 6, 3, FAKE, FAKE, FAKE, FAKE, -1, FAKE, None, 0, None) == 2
+    assert R(FAKE, 92160, 0, 64, 92096, 92160, 8192, FAKE, FAKE, FAKE, FAKE, -1, FAKE, FAKE, need - 1, None) == 5
     # the no-allocation variant: same checks, and a fixed size limit instead of a workspace
     nmax = lib.kvs_topk_noalloc_max()
     assert nmax == 1 << 24

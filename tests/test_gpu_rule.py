@@ -486,6 +486,34 @@ def test_slotmap_bit_exact():
     np.testing.assert_array_equal(slots.cpu().numpy(), np.where(want == -1, 123456789, want))
 
 
+@pytest.mark.parametrize("n,C,f0,f1,single,in_place", [
+    (5000, 700, (0, 16), (4900, 4964), False, False),        # one workgroup, keys in registers (8 per thread)
+    (30000, 4096, (0, 64), (29936, 30000), False, True),     # 32 per thread, slots redirected in place
+    (92160, 8192, (0, 64), (92096, 92160), False, False),    # several workgroups
+    (92160, 8192, (0, 64), (92096, 92160), True, True),      # one workgroup streaming from L2
+    (3000, 5000, (0, 10), (2990, 3000), False, False),       # C >= n: everything kept
+    (3000, 20, (0, 10), (2980, 3000), False, False),         # C < |F|: the forced set only
+    (1, 1, (0, 0), (0, 0), False, False),
+])
+def test_topk_select_redirect_equals_the_two_calls(n, C, f0, f1, single, in_place):
+    """The fused selection + redirect writes the same mask, indices, count and slot map, bit for bit,
+    as kvs_topk_select followed by kvs_slotmap_redirect, on every top-k path."""
+    score = W.scores_with_ties(n, n + 3, 64).to(DEV)                      # many ties at the threshold
+    slots = torch.from_numpy(np.random.default_rng(n).permutation(4 * n)[:n].copy()).to(DEV)
+    keep, idx, nk = kvs.kvs_topk_select(score, f0, f1, C, single_workgroup=single)
+    want_slots = kvs.kvs_slotmap_redirect(slots, keep, -7)
+    s_in = slots.clone()
+    k2, i2, n2, s_out = kvs.kvs_topk_select_redirect(score, f0, f1, C, s_in, -7,
+                                                     slot_out=s_in if in_place else None, single_workgroup=single)
+    torch.cuda.synchronize()
+    m = int(nk.item())
+    assert int(n2.item()) == m
+    assert torch.equal(keep, k2) and torch.equal(idx[:m], i2[:m])
+    assert torch.equal(s_out, want_slots)
+    if in_place:
+        assert s_out.data_ptr() == s_in.data_ptr()
+
+
 def test_rule_turn_end_to_end_tiny():
     """qmem x 3 turns -> rule -> top-k -> slot map on rule-tiny, against the oracle chain."""
     c = W.config("rule-tiny")
