@@ -448,7 +448,7 @@ struct FoldArgs {
   uint32_t* lse;           // [L*H_kv][kLine]: the G normaliser bits of a group at the start of its
                            // line, kLseUnset until a workgroup has merged them
   float* fold;             // [L*H_kv][N]
-  uint32_t* spilled;       // [L*H_kv][n_chunks]: 1 = the chunk went to the spill
+  uint32_t* spilled;       // [n_chunks][L*H_kv]: 1 = the chunk went to the spill
   uint32_t* count;         // [L*H_kv][kLine]: chunks published per group (word 0 of each line)
   uint32_t* queue;         // [kQueues][kLine]: claims handed out per queue (word 0 of each line)
 };
@@ -636,7 +636,7 @@ __global__ __launch_bounds__(kFoldThreads, WPS) void rule_fold_queue(FoldArgs a)
         float* out = a.spill + ((size_t)head0 + h) * N + r0;
         for (int p = threadIdx.x; p < nrow; p += kFoldThreads) out[p] = hb[h * HS + p];
       }
-      if (threadIdx.x == 0) a.spilled[(size_t)lg * nc + c] = 1u;
+      if (threadIdx.x == 0) a.spilled[(size_t)c * a.LHkv + lg] = 1u;
     }
   };
 
@@ -798,40 +798,60 @@ __global__ __launch_bounds__(256) void rule_fold_reset(uint64_t* __restrict__ pa
 // rule_j = sum over the L*H_kv groups, in a fixed order, of the folded value,
 // or, for a chunk that went to the spill, of the same sum of the G heads'
 // terms computed here from the spilled logits.  64 positions per workgroup,
-// all in one chunk (the chunk length is a multiple of 64).
+// all in one chunk (the chunk length is a multiple of 64).  Wave w takes the
+// groups w, w+4, ...: their spill flags arrive 64 at a time in one load, and
+// the folded values 8 rows at a time, before any of them is needed.
 __global__ __launch_bounds__(256) void rule_fold_colsum(const float* __restrict__ fold,
                                                         const float* __restrict__ spill,
                                                         const uint64_t* __restrict__ partials,
                                                         const uint32_t* __restrict__ lse,
                                                         const uint32_t* __restrict__ spilled, int LHkv, int G,
                                                         int n_chunks, int CP, int64_t N, float* __restrict__ rule) {
+  constexpr int RB = 8;                 // rows per batch of loads
   __shared__ float part[4][kColTile];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t j0 = (int64_t)blockIdx.x * kColTile;
   const int64_t j = j0 + lane;
+  const int64_t jc = j < N ? j : N - 1;   // a lane past N reads a valid address and drops the value
   const int c = (int)(j0 / CP);
+  const uint32_t* flags = spilled + (size_t)c * LHkv;
+  const int rows = (LHkv - wave + 3) / 4;   // this wave's groups: wave + 4k, k < rows
   float acc = 0.f;
-  for (int lg = wave; lg < LHkv; lg += 4) {
-    float v = 0.f;
-    if (__builtin_amdgcn_readfirstlane(spilled[(size_t)lg * n_chunks + c])) {
-      const int head0 = lg * G;
-      float L[8];
-      bool have = true;
+  for (int k0 = 0; k0 < rows; k0 += 64) {
+    const int kk = k0 + lane;
+    const uint32_t fl = kk < rows ? flags[wave + 4 * kk] : 0u;   // lane i: the flag of the wave's row k0 + i
+    const int nb = min(64, rows - k0);
+    for (int b0 = 0; b0 < nb; b0 += RB) {
+      float fv[RB];
 #pragma unroll
-      for (int hl = 0; hl < 8; ++hl) {
-        const uint32_t b = hl < G ? __builtin_amdgcn_readfirstlane(lse[(size_t)lg * kLine + hl]) : 0u;
-        L[hl] = __uint_as_float(b);
-        have &= hl >= G || b != kLseUnset;
+      for (int t = 0; t < RB; ++t) {
+        const int lg = wave + 4 * (k0 + min(b0 + t, nb - 1));
+        fv[t] = fold[(size_t)lg * N + jc];
       }
-      // Normalisers never published: no chunk of this group was folded, so
-      // computing them here is consistent (and gives the same bits anyway).
-      if (!have) group_lse<8>(partials + (size_t)head0 * n_chunks, n_chunks, 0, 1, G, lane, L);
-      if (j < N)
-        for (int h = 0; h < G; ++h) v += __builtin_amdgcn_exp2f(spill[((size_t)head0 + h) * N + j] - L[h]);
-    } else if (j < N) {
-      v = fold[(size_t)lg * N + j];
+#pragma unroll
+      for (int t = 0; t < RB; ++t) {
+        if (b0 + t >= nb) break;
+        const int lg = wave + 4 * (k0 + b0 + t);
+        float v = fv[t];
+        if (__builtin_amdgcn_readlane(fl, b0 + t)) {
+          const int head0 = lg * G;
+          float L[8];
+          bool have = true;
+#pragma unroll
+          for (int hl = 0; hl < 8; ++hl) {
+            const uint32_t bits = hl < G ? __builtin_amdgcn_readfirstlane(lse[(size_t)lg * kLine + hl]) : 0u;
+            L[hl] = __uint_as_float(bits);
+            have &= hl >= G || bits != kLseUnset;
+          }
+          // Normalisers never published: no chunk of this group was folded, so
+          // computing them here is consistent (and gives the same bits anyway).
+          if (!have) group_lse<8>(partials + (size_t)head0 * n_chunks, n_chunks, 0, 1, G, lane, L);
+          v = 0.f;
+          for (int h = 0; h < G; ++h) v += __builtin_amdgcn_exp2f(spill[((size_t)head0 + h) * N + jc] - L[h]);
+        }
+        acc += v;
+      }
     }
-    acc += v;
   }
   part[wave][lane] = acc;
   __syncthreads();
