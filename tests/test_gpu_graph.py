@@ -152,3 +152,47 @@ def test_rule_turn_and_meank_step_on_concurrent_streams():
     got = t.outputs()
     for name in want:
         assert torch.equal(got[name], want[name]), f"{name} differs between concurrent and sequential calls"
+
+
+def test_rule_scores_on_concurrent_streams_share_the_device():
+    """Two rule scores with their own workspaces, on two streams at once, next to a Mean-K score
+    on a third: each equals its call alone, bit for bit.  The rule score's persistent workgroups
+    claim chunks from queues in their own workspace and never rely on how many of them are
+    resident, so sharing the CUs with other kernels changes only the timing."""
+    shapes = [(2, 32, 8, 128, 131073), (3, 40, 8, 128, 50000)]     # G = 4 and G = 5
+    jobs = []
+    for i, (L, H_q, H_kv, D, N) in enumerate(shapes):
+        K = W.normal((L, H_kv, N, D), 300 + i, W.T_K, "bf16", DEV)
+        M = W.memory_vectors(L, H_q, D, 300 + i, DEV)
+        ws = torch.empty(kvs.kvs_rule_score_workspace(L, H_q, H_kv, N), dtype=torch.uint8, device=DEV)
+        out = torch.empty(N, dtype=torch.float32, device=DEV)
+        jobs.append((K, M, ws, out, N))
+    mk_Q = W.normal((4, 32, 512, 128), 310, W.T_Q, "bf16", DEV)
+    mk_index = W.normal((4, 8, 8192, 128), 310, W.T_K, "bf16", DEV)
+    mk_R = torch.empty(8192, dtype=torch.float32, device=DEV)
+    mk_ws = torch.empty(kvs.kvs_meank_score_workspace(4, 32, 8, 512, 8192), dtype=torch.uint8, device=DEV)
+    alone = []
+    for K, M, ws, out, N in jobs:
+        kvs.kvs_rule_score(K, M, 5, N - 64, N, rule=out, ws=ws)
+        torch.cuda.synchronize()
+        alone.append(out.clone())
+    kvs.kvs_meank_score(mk_Q, mk_index, 4, 64, R=mk_R, ws=mk_ws)
+    torch.cuda.synchronize()
+    mk_alone = mk_R.clone()
+    for rep in range(3):
+        for _, _, _, out, _ in jobs:
+            out.fill_(float("nan"))
+        streams = [torch.cuda.Stream() for _ in range(3)]
+        for s in streams:
+            s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(streams[2]):
+            kvs.kvs_meank_score(mk_Q, mk_index, 4, 64, R=mk_R, ws=mk_ws)
+        for s, (K, M, ws, out, N) in zip(streams[:2], jobs):
+            with torch.cuda.stream(s):
+                kvs.kvs_rule_score(K, M, 5, N - 64, N, rule=out, ws=ws)
+        for s in streams:
+            torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        for (_, _, _, out, _), want in zip(jobs, alone):
+            assert torch.equal(out.view(torch.int32), want.view(torch.int32)), f"round {rep}"
+        assert torch.equal(mk_R.view(torch.int32), mk_alone.view(torch.int32))
