@@ -333,7 +333,7 @@ kvs_status kvs_working_set_update(const void* k_src, const void* v_src, int64_t 
   if (src_tokens % block != 0 || numel4(L, H_kv, src_tokens, D) < 0 ||
       numel4(L, H_kv, pool_pages, (int64_t)block * D) < 0 || pool_pages > kMaxIndex ||
       n_new > pool_pages || n_prev > pool_pages || !grid_ok(n_new) ||
-      !grid_ok(n_new * cdiv((int64_t)L * H_kv, kvs::kWorksetSlices)))
+      !grid_ok(n_new * cdiv((int64_t)L * H_kv, kvs::kWorksetChunk)))
     return KVS_ERR_SHAPE;
   const size_t need = kvs_workset_ws_bytes(pool_pages);
   if (need > 0 && (!ws || ws_bytes < need || !a16(ws))) return KVS_ERR_WORKSPACE;

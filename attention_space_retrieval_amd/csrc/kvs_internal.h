@@ -16,11 +16,13 @@ constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 // (layer, KV head) slices per workgroup, one wave per slice: the re-RoPE
 // scatter launches n_sel * ceil(L*H_kv / kScatterSlices) workgroups of
-// kScatterThreads, the working-set update n_new * ceil(L*H_kv / kWorksetSlices)
-// workgroups of 64 * kWorksetSlices threads
+// kScatterThreads; the working-set update n_new * ceil(L*H_kv / kWorksetChunk)
+// workgroups of 64 * kWorksetSlices threads, each wave taking every
+// kWorksetSlices-th slice of the workgroup's chunk
 constexpr int kScatterSlices = 16;
 constexpr int kScatterThreads = 64 * kScatterSlices;
 constexpr int kWorksetSlices = 8;
+constexpr int kWorksetChunk = 8;
 
 // bf16 is the top half of a binary32: widening is a shift.
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }

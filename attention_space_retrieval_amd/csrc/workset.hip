@@ -152,7 +152,10 @@ __global__ __launch_bounds__(kThreads) void workset_diff(
 // Same-process A/B at meank-256k: 5.09 ms against 5.12 ms with two slices per
 // wave of 256 threads.  The scatter's 16-slice, 1024-thread shape was 4% slower
 // here: most workgroups belong to blocks retained in place, which exit at
-// once, and large workgroups cost more to launch and retire.
+// once, and large workgroups cost more to launch and retire.  At meank-1m
+// (512 slices, half the selected blocks moved, half incoming) that shape is
+// 4% faster (6.43 against 6.70 ms), and 32- or 64-slice chunks over 8 waves
+// 2-3%; the 8-slice shape stays for the sizes where blocks stay in place.
 template <int D, bool WITH_V>
 __global__ __launch_bounds__(64 * kWorksetSlices, 2) void workset_apply(
     const uint16_t* __restrict__ k_src, const uint16_t* __restrict__ v_src, int64_t src_tokens,
@@ -161,7 +164,7 @@ __global__ __launch_bounds__(64 * kWorksetSlices, 2) void workset_apply(
     uint16_t* __restrict__ k_pool, uint16_t* __restrict__ v_pool, int64_t pool_pages) {
   constexpr int LPR = D / 8, RPL = 64 / LPR, LOADS = kBlk / RPL;
   __shared__ float2 tab[kBlk][D / 2];
-  const int nch = (LG + kWorksetSlices - 1) / kWorksetSlices;
+  const int nch = (LG + kWorksetChunk - 1) / kWorksetChunk;
   const int r = blockIdx.x / nch, chunk = blockIdx.x % nch;
   const int32_t rank = old_rank[r];
   const int64_t page = pages[r];
@@ -178,8 +181,8 @@ __global__ __launch_bounds__(64 * kWorksetSlices, 2) void workset_apply(
   constexpr int kBlkBytes = kBlk * D * 2, kGroupBytes = RPL * D * 2;
   const int lane_off = (rr * D + cl * 8) * 2;
   const int64_t pool_tokens = pool_pages * kBlk;
-  const int lg_end = min(LG, (chunk + 1) * kWorksetSlices);
-  for (int lg = chunk * kWorksetSlices + wave; lg < lg_end; lg += kWorksetSlices) {
+  const int lg_end = min(LG, (chunk + 1) * kWorksetChunk);
+  for (int lg = chunk * kWorksetChunk + wave; lg < lg_end; lg += kWorksetSlices) {
     const size_t d0 = ((size_t)lg * pool_tokens + (size_t)page * kBlk) * D;
     const size_t s0 = ((size_t)lg * src_tokens + (size_t)sb * kBlk) * D;
     const auto kin = buf_rsrc(k_src + s0, kBlkBytes);
@@ -236,7 +239,7 @@ hipError_t kvs_launch_workset(const void* k_src, const void* v_src, int64_t src_
   const uint16_t* vs = static_cast<const uint16_t*>(v_src);
   uint16_t* kp = static_cast<uint16_t*>(k_pool);
   uint16_t* vp = static_cast<uint16_t*>(v_pool);
-  const dim3 grid((unsigned)(n_new * ceil_div(LG, kWorksetSlices))), block(64 * kWorksetSlices);
+  const dim3 grid((unsigned)(n_new * ceil_div(LG, kWorksetChunk))), block(64 * kWorksetSlices);
 #define KVS_APPLY(DD, WV)                                                                          \
   hipLaunchKernelGGL((workset_apply<DD, WV>), grid, block, 0, st, ks, vs, src_tokens, new_blocks, \
                      pages_out, old_rank_out, LG, pos_base, l2t, kp, vp, pool_pages)
