@@ -366,7 +366,8 @@ __global__ __launch_bounds__(256) void rule_colsum(const float* __restrict__ spi
 
 constexpr int kQueues = 2;                       // claim counters, each shared by half the workgroups
 constexpr int kLine = 64;                        // words between counters (one 256-byte line each)
-constexpr int kFoldThreads = 256;
+constexpr int kFoldWaves = 4;                    // waves per workgroup
+constexpr int kFoldThreads = 64 * kFoldWaves;
 constexpr uint32_t kLseUnset = 0x7fbadbadu;      // a NaN payload no arithmetic here produces
 constexpr uint32_t kNanBits = 0x7fc00000u;       // the canonical quiet NaN
 // A chunk partial is the bit pair (max, sum); a sum is never negative, so
@@ -478,26 +479,28 @@ __device__ __forceinline__ uint32_t queue_items(const FoldArgs& a, int qi) {
 // its workgroup before that one can reach this wait.  It is bounded besides;
 // past the bound the chunk is spilled.
 //
-// WPS: workgroups per CU that the LDS footprint allows (2 or 3), which is
-// also the waves per SIMD the register budget is cut for.  With fewer waves,
+// WPS: workgroups per CU that the LDS footprint allows (2 or 3); the register
+// budget is cut for the waves per SIMD that makes.  With fewer waves per SIMD,
 // each keeps more 16-row tiles of K in flight (4 instead of 2).
 template <int D, bool PAGED, int CP, int WPS>
-__global__ __launch_bounds__(kFoldThreads, WPS) void rule_fold_queue(FoldArgs a) {
+__global__ __launch_bounds__(kFoldThreads, WPS * kFoldWaves / 4) void rule_fold_queue(FoldArgs a) {
   constexpr int LAG = kFoldLag;
   constexpr int KS = D / 32;            // MFMA k-steps per row
   constexpr int QW = D / 4;             // dims owned by one 16-lane group
   constexpr int HS = CP + 4;            // held-logit row stride
-  constexpr int NT = CP / 64;           // 16-row tiles per wave per chunk
+  constexpr int NT = CP / (16 * kFoldWaves);   // 16-row tiles per wave per chunk
+  static_assert(CP % (16 * kFoldWaves) == 0, "a chunk is whole rounds of the waves' tiles");
+  constexpr int HPW = 8 / kFoldWaves;   // heads per wave when the waves merge a group's normalisers
   constexpr int kRow = D * 2 + 16;
   constexpr int RPI = 64 / (D / 8);     // rows per load instruction
   constexpr int NLD = 16 / RPI;         // load instructions per 16-row tile
   static_assert(NT >= 2, "the fetches ride on the second-last tile");
   extern __shared__ float held[];
-  __shared__ __attribute__((aligned(16))) char stage[4][16 * kRow];
-  __shared__ float2 red[4][8];
+  __shared__ __attribute__((aligned(16))) char stage[kFoldWaves][16 * kRow];
+  __shared__ float2 red[kFoldWaves][8];
   __shared__ float s_lse[8];
   __shared__ int s_lg, s_c, s_pub, s_cmp;
-  __shared__ int s_miss[2][4];
+  __shared__ int s_miss[2][kFoldWaves];
   __shared__ int32_t sslot[PAGED ? CP : 1];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
@@ -596,23 +599,28 @@ __global__ __launch_bounds__(kFoldThreads, WPS) void rule_fold_queue(FoldArgs a)
       const uint64_t* part = a.partials + (size_t)lg * G * nc;
       for (int64_t it = 0;; ++it) {
         float lse[8];
-        const bool mine = group_lse<2>(part, nc, wave, 4, G, lane, lse);
+        const bool mine = group_lse<HPW>(part, nc, wave, kFoldWaves, G, lane, lse);
         if (lane == 0) {
-          if (wave < G) s_lse[wave] = lse[wave];
-          if (wave + 4 < G) s_lse[wave + 4] = lse[wave + 4];
+#pragma unroll
+          for (int j = 0; j < HPW; ++j)
+            if (wave + j * kFoldWaves < G) s_lse[wave + j * kFoldWaves] = lse[wave + j * kFoldWaves];
           s_miss[it & 1][wave] = !mine;
         }
         __syncthreads();
-        ok = !(s_miss[it & 1][0] | s_miss[it & 1][1] | s_miss[it & 1][2] | s_miss[it & 1][3]);
+        int miss = 0;
+#pragma unroll
+        for (int w = 0; w < kFoldWaves; ++w) miss |= s_miss[it & 1][w];
+        ok = !miss;
         if (ok) {
           // publish for the other workgroups of the group (the same bits whoever merges)
           if (lane == 0) {
-            if (wave < G)
-              __hip_atomic_store(a.lse + (size_t)lg * kLine + wave, __float_as_uint(lse[wave]), __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-            if (wave + 4 < G)
-              __hip_atomic_store(a.lse + (size_t)lg * kLine + wave + 4, __float_as_uint(lse[wave + 4]),
-                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int j = 0; j < HPW; ++j) {
+              const int h = wave + j * kFoldWaves;
+              if (h < G)
+                __hip_atomic_store(a.lse + (size_t)lg * kLine + h, __float_as_uint(lse[h]), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
           }
           break;
         }
@@ -647,13 +655,13 @@ __global__ __launch_bounds__(kFoldThreads, WPS) void rule_fold_queue(FoldArgs a)
   __syncthreads();
   int lg = __builtin_amdgcn_readfirstlane(s_lg), c = __builtin_amdgcn_readfirstlane(s_c);
   if (lg < 0) return;
-  constexpr int RING = WPS <= 2 ? 4 : 2;
+  constexpr int RING = WPS * kFoldWaves / 4 <= 2 ? 4 : 2;   // more tiles in flight when fewer waves share a SIMD
   constexpr int PF = RING < NT ? RING : NT;
   u32x4 W[PF][NLD];
   bf16x8 B[KS];
   auto first_loads = [&]() {
 #pragma unroll
-    for (int i = 0; i + 1 < PF; ++i) load_tile(row0 + wave * 16 + 64 * i, W[i]);
+    for (int i = 0; i + 1 < PF; ++i) load_tile(row0 + wave * 16 + 16 * kFoldWaves * i, W[i]);
   };
   read_slots(c);
   stage_slots();
@@ -675,8 +683,8 @@ __global__ __launch_bounds__(kFoldThreads, WPS) void rule_fold_queue(FoldArgs a)
                                         // of the held chunk's group
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-      const int64_t t0 = row0 + wave * 16 + 64 * i;
-      if (i + PF - 1 < NT) load_tile(t0 + 64 * (PF - 1), W[(i + PF - 1) % PF]);
+      const int64_t t0 = row0 + wave * 16 + 16 * kFoldWaves * i;
+      if (i + PF - 1 < NT) load_tile(t0 + 16 * kFoldWaves * (PF - 1), W[(i + PF - 1) % PF]);
       if (i == NT - 2) {
         if (threadIdx.x == 0) take();
         if (wave == 0 && old_lg >= 0 && (lane < G || lane == 63))
@@ -725,7 +733,7 @@ __global__ __launch_bounds__(kFoldThreads, WPS) void rule_fold_queue(FoldArgs a)
       if (lane < G) {
         float m = -INFINITY, s = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) lse_merge(m, s, red[w][lane].x, red[w][lane].y);
+        for (int w = 0; w < kFoldWaves; ++w) lse_merge(m, s, red[w][lane].x, red[w][lane].y);
         __hip_atomic_store(a.partials + ((size_t)lg * G + lane) * nc + c, part_bits(m, s), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
       }
@@ -867,11 +875,11 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // gathered rows want the occupancy more).  The transpose stage is counted at
 // its D = 128 size.
 inline int fold_chunk(int G, bool paged) {
-  for (int cp : {1024, 768, 512, 256, 128}) {
+  for (int cp : {1024, 768, 512, 256}) {
     const size_t held = (size_t)(kFoldLag + 1) * G * (cp + 4) * 4;
     if (!paged ? held <= 43008 : held + 4 * 16 * 272 + (size_t)cp * 4 + 512 <= 160 * 1024 / 3) return cp;
   }
-  return 128;
+  return 256;
 }
 // Chunks per group the workspace is sized for: the shorter of the two chunk lengths.
 inline int64_t fold_chunks_max(int G, int64_t N) {
@@ -982,7 +990,7 @@ hipError_t kvs_launch_rule(const void* K, int dtype, const int64_t* slots, int64
     const int64_t items = (int64_t)LHkv * nc_fold;
     const size_t lds = (size_t)(kFoldLag + 1) * G * (CP + 4) * 4;
     // the kernel's own LDS: the transpose stage, the slots of a paged chunk, a few words
-    const size_t lds_static = (size_t)4 * 16 * (2 * D + 16) + (paged ? (size_t)CP * 4 : 0) + 512;
+    const size_t lds_static = (size_t)kFoldWaves * 16 * (2 * D + 16) + (paged ? (size_t)CP * 4 : 0) + 512;
     const int wps = (int)((160 * 1024) / (lds + lds_static));
     // one resident wave of persistent workgroups (a multiple of kQueues)
     const int64_t resident = (int64_t)device_cus() * std::min(std::max(wps, 1), 3) / kQueues * kQueues;
@@ -997,8 +1005,7 @@ hipError_t kvs_launch_rule(const void* K, int dtype, const int64_t* slots, int64
     case 1024: FOLD_LAUNCH(DD, PG, 1024); break;                                          \
     case 768: FOLD_LAUNCH(DD, PG, 768); break;                                            \
     case 512: FOLD_LAUNCH(DD, PG, 512); break;                                            \
-    case 256: FOLD_LAUNCH(DD, PG, 256); break;                                            \
-    default: FOLD_LAUNCH(DD, PG, 128); break;                                             \
+    default: FOLD_LAUNCH(DD, PG, 256); break;                                             \
   }
     if (D == 128) { if (paged) { FOLD_LAUNCH_C(128, true) } else { FOLD_LAUNCH_C(128, false) } }
     else { if (paged) { FOLD_LAUNCH_C(64, true) } else { FOLD_LAUNCH_C(64, false) } }
