@@ -331,6 +331,7 @@ def test_rule_paged_full_size_equals_dense(name):
     (1, 4, 4, 300, 1, 299, 0, 0),              # one candidate
     (1, 16, 2, 2500, 32, 5, 2400, 2450),       # G*W = 256 rows: pass 1 with four-wave workgroups
     (1, 20, 4, 1800, 40, 0, 1700, 1800),       # G*W = 200 rows (padded to 224): four waves, a partial one
+    (1, 40, 4, 1500, 32, 3, 1400, 1450),       # G*W = 320 rows: pass 1 with a second, partial 256-row tile
 ])
 @pytest.mark.parametrize("D", [128, 64])
 def test_window_score_against_oracle(L, H_q, H_kv, N, Wn, pi, q_s, q_e, D):
