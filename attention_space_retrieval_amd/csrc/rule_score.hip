@@ -35,6 +35,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 using namespace kvs;
 
@@ -805,10 +806,13 @@ __global__ __launch_bounds__(256) void rule_fold_reset(uint64_t* __restrict__ pa
 
 // rule_j = sum over the L*H_kv groups, in a fixed order, of the folded value,
 // or, for a chunk that went to the spill, of the same sum of the G heads'
-// terms computed here from the spilled logits.  64 positions per workgroup,
-// all in one chunk (the chunk length is a multiple of 64).  Wave w takes the
-// groups w, w+4, ...: their spill flags arrive 64 at a time in one load, and
-// the folded values 8 rows at a time, before any of them is needed.
+// terms computed here from the spilled logits.  VEC * 64 positions per
+// workgroup, all in one chunk (the chunk length is a multiple of that), VEC
+// consecutive positions per lane (VEC = 4 when N is a multiple of 4, so each
+// load instruction reads 1 KB of a row).  Wave w takes the groups w, w+4, ...:
+// their spill flags arrive 64 at a time in one load, and the folded values 8
+// rows at a time, before any of them is needed.
+template <int VEC>
 __global__ __launch_bounds__(256) void rule_fold_colsum(const float* __restrict__ fold,
                                                         const float* __restrict__ spill,
                                                         const uint64_t* __restrict__ partials,
@@ -816,31 +820,45 @@ __global__ __launch_bounds__(256) void rule_fold_colsum(const float* __restrict_
                                                         const uint32_t* __restrict__ spilled, int LHkv, int G,
                                                         int n_chunks, int CP, int64_t N, float* __restrict__ rule) {
   constexpr int RB = 8;                 // rows per batch of loads
-  __shared__ float part[4][kColTile];
+  using VT = std::conditional_t<VEC == 4, u32x4, uint32_t>;
+  __shared__ float part[4][64 * VEC];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int64_t j0 = (int64_t)blockIdx.x * kColTile;
-  const int64_t j = j0 + lane;
-  const int64_t jc = j < N ? j : N - 1;   // a lane past N reads a valid address and drops the value
+  const int64_t j0 = (int64_t)blockIdx.x * (64 * VEC);
+  const int64_t j = j0 + (int64_t)lane * VEC;   // the lane's first position; past N a row reads as zero
   const int c = (int)(j0 / CP);
   const uint32_t* flags = spilled + (size_t)c * LHkv;
   const int rows = (LHkv - wave + 3) / 4;   // this wave's groups: wave + 4k, k < rows
-  float acc = 0.f;
+  // one row of N floats as a buffer resource; offsets past it read zero
+  auto load_row = [&](const float* row) -> VT {
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(row, (int)(N * 4));
+    if constexpr (VEC == 4) return __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(j * 4), 0, 0);
+    else return __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(j * 4), 0, 0);
+  };
+  float acc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
   for (int k0 = 0; k0 < rows; k0 += 64) {
     const int kk = k0 + lane;
     const uint32_t fl = kk < rows ? flags[wave + 4 * kk] : 0u;   // lane i: the flag of the wave's row k0 + i
     const int nb = min(64, rows - k0);
     for (int b0 = 0; b0 < nb; b0 += RB) {
-      float fv[RB];
+      VT fv[RB];
 #pragma unroll
       for (int t = 0; t < RB; ++t) {
         const int lg = wave + 4 * (k0 + min(b0 + t, nb - 1));
-        fv[t] = fold[(size_t)lg * N + jc];
+        fv[t] = load_row(fold + (size_t)lg * N);
       }
 #pragma unroll
       for (int t = 0; t < RB; ++t) {
         if (b0 + t >= nb) break;
         const int lg = wave + 4 * (k0 + b0 + t);
-        float v = fv[t];
+        float v[VEC];
+        if constexpr (VEC == 4) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(fv[t][e]);
+        } else {
+          v[0] = __uint_as_float(fv[t]);
+        }
         if (__builtin_amdgcn_readlane(fl, b0 + t)) {
           const int head0 = lg * G;
           float L[8];
@@ -854,16 +872,30 @@ __global__ __launch_bounds__(256) void rule_fold_colsum(const float* __restrict_
           // Normalisers never published: no chunk of this group was folded, so
           // computing them here is consistent (and gives the same bits anyway).
           if (!have) group_lse<8>(partials + (size_t)head0 * n_chunks, n_chunks, 0, 1, G, lane, L);
-          v = 0.f;
-          for (int h = 0; h < G; ++h) v += __builtin_amdgcn_exp2f(spill[((size_t)head0 + h) * N + jc] - L[h]);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) v[e] = 0.f;
+          for (int h = 0; h < G; ++h) {
+            const VT x = load_row(spill + ((size_t)head0 + h) * N);
+            if constexpr (VEC == 4) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] += __builtin_amdgcn_exp2f(__uint_as_float(x[e]) - L[h]);
+            } else {
+              v[0] += __builtin_amdgcn_exp2f(__uint_as_float(x) - L[h]);
+            }
+          }
         }
-        acc += v;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] += v[e];
       }
     }
   }
-  part[wave][lane] = acc;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) part[wave][lane * VEC + e] = acc[e];
   __syncthreads();
-  if (wave == 0 && j < N) rule[j] = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+  for (int i = threadIdx.x; i < 64 * VEC; i += 256) {
+    const int64_t jj = j0 + i;
+    if (jj < N) rule[jj] = ((part[0][i] + part[1][i]) + part[2][i]) + part[3][i];
+  }
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1012,8 +1044,12 @@ hipError_t kvs_launch_rule(const void* K, int dtype, const int64_t* slots, int64
 #undef FOLD_LAUNCH_C
 #undef FOLD_LAUNCH
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(rule_fold_colsum, dim3(ceil_div(N, kColTile)), dim3(256), 0, st, w.fold, w.spill, partials,
-                       lse, w.spilled, LHkv, G, (int)nc_fold, CP, N, rule);
+    if (N % 4 == 0)
+      hipLaunchKernelGGL(rule_fold_colsum<4>, dim3(ceil_div(N, 4 * 64)), dim3(256), 0, st, w.fold, w.spill, partials,
+                         lse, w.spilled, LHkv, G, (int)nc_fold, CP, N, rule);
+    else
+      hipLaunchKernelGGL(rule_fold_colsum<1>, dim3(ceil_div(N, 64)), dim3(256), 0, st, w.fold, w.spill, partials,
+                         lse, w.spilled, LHkv, G, (int)nc_fold, CP, N, rule);
     return hipGetLastError();
   }
 
