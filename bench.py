@@ -59,7 +59,7 @@ CALL_KERNELS = {
     "kvs_qmem_update": ["qmem_kernel<128, true>"],
     # bf16 keys, G <= 8: the work-queue fold; the last template argument is the workgroups per CU
     # its LDS allows (3 at G = 4, 2 at G = 5), the third the chunk length
-    "kvs_rule_score": ["rule_fold_reset", "rule_fold_queue<128, false, 1024, 3>", "rule_fold_colsum"],
+    "kvs_rule_score": ["rule_fold_reset", "rule_fold_queue<128, false, 1024, 3>", "rule_fold_colsum<4>"],
     # the redirect runs inside the multi-workgroup emit, and as its own kernel after a one-workgroup
     # selection
     "kvs_topk_select_redirect[rule]": ["topk_reg_kernel<32>", "slotmap_kernel"],
@@ -68,7 +68,7 @@ CALL_KERNELS = {
     "kvs_meank_score": ["meank_pass<true, false, 4, 128>", "meank_pass<false, false, 4, 128>", "meank_reduce<false>"],
     "kvs_rerope_scatter": ["rerope_scatter_kernel<128>", "v_scatter_kernel<128>"],
     # rows beyond the step (timed after it): the paged rule score takes 768-position chunks
-    "kvs_rule_score_paged": ["rule_fold_reset", "rule_fold_queue<128, true, 768, 3>", "rule_fold_colsum"],
+    "kvs_rule_score_paged": ["rule_fold_reset", "rule_fold_queue<128, true, 768, 3>", "rule_fold_colsum<4>"],
     "kvs_window_score": [("meank_pass<true, true, 2, 128>", "meank_pass<true, true, 4, 128>"), "meank_lse_merge",
                          "meank_pass<false, true, 2, 128>",
                          "meank_reduce<true>"],
@@ -81,7 +81,7 @@ def call_kernels(workload):
     """CALL_KERNELS with the top-k kernels the workload's sizes select."""
     ck = dict(CALL_KERNELS)
     if workload == "rule-14b+meank-1m":
-        ck["kvs_rule_score"] = ["rule_fold_reset", "rule_fold_queue<128, false, 1024, 2>", "rule_fold_colsum"]
+        ck["kvs_rule_score"] = ["rule_fold_reset", "rule_fold_queue<128, false, 1024, 2>", "rule_fold_colsum<4>"]
         ck["kvs_topk_select_redirect[rule]"] = TOPK_MW              # n = 92160
         ck["kvs_topk_select[meank]"] = ["topk_reg_kernel<32>"]      # n = 32768 blocks
         # the 1M workspace keeps no V beside raw K (the scatter reads the packed staging buffers), so

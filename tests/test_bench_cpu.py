@@ -34,3 +34,18 @@ def test_call_kernels_follow_the_workload():
     # the fold's workgroups per CU follow G: 3 at rule-8b (G = 4), 2 at rule-14b (G = 5)
     assert small["kvs_rule_score"][1].endswith("1024, 3>") and big["kvs_rule_score"][1].endswith("1024, 2>")
     assert big["kvs_meank_score"] == small["kvs_meank_score"]
+
+
+def test_every_listed_kernel_has_profiled_traffic():
+    """Each kernel bench.py attributes to a call appears, under that exact short name, in the
+    committed HBM-traffic profile of the workload, so no call's traffic silently reads as null."""
+    import json
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for wl in bench.WORKLOADS:
+        with open(os.path.join(root, "profiles", f"hbm_traffic_all-kernels_{wl}.json")) as f:
+            profiled = json.load(f)["kernels"]
+        for call, kernels in bench.call_kernels(wl).items():
+            for k in kernels:
+                alts = [a.split("*")[0] for a in (k if isinstance(k, tuple) else (k,))]
+                assert any(a in profiled for a in alts), (wl, call, alts)
