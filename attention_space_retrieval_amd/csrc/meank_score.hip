@@ -256,39 +256,7 @@ __global__ __launch_bounds__(64 * NW, 2) void meank_pass(const uint16_t* __restr
   const uint16_t* Ig = index + (size_t)lg * nB * D;
   const float* Lg = lse2 + (size_t)lg * rows_pad;
 
-  // persistent operand: pass 1 = query rows, pass 2 = index rows (block columns).
-  // The workgroup's 256 rows are read whole and coalesced (16 loads of 16 bytes
-  // per thread at D = 128; rows past the end read as zero), staged in LDS, and each wave
-  // takes its 64 rows in the operand layout from there.  Loaded straight in
-  // that layout, every load instruction would touch 64 rows 16 bytes at a
-  // time, which starves the passes that stream few tiles per workgroup.
-  const int64_t p0 = (int64_t)tile * PER_WG + wave * kPerWave;
-  bf16x8 B0[KS], B1[KS];
-  {
-    const int64_t pbase = (PASS1 ? 0 : c0) + (int64_t)tile * PER_WG;
-    const int64_t plim = PASS1 ? rows : c1;
-    const int pcount = (int)(plim <= pbase ? 0 : (plim - pbase > PER_WG ? PER_WG : plim - pbase));
-    const uint16_t* pg = (PASS1 ? Qg : Ig) + (pcount > 0 ? (size_t)pbase * D : 0);
-    const __amdgpu_buffer_rsrc_t prs = buf_rsrc(pg, pcount * kRowBytes);
-    constexpr int kLoads = PER_WG * kRowBytes / 16 / NT;
-    u32x4 v[kLoads];
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i)
-      v[i] = __builtin_amdgcn_raw_buffer_load_b128(prs, (threadIdx.x + NT * i) * 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int idx = threadIdx.x + NT * i;
-      *reinterpret_cast<u32x4*>(smem + (idx / Dm::kChunks) * kLdsRow + (idx % Dm::kChunks) * 16) = v[i];
-    }
-    __syncthreads();
-    const char* r0 = smem + (wave * kPerWave + n) * kLdsRow + h * (kRowBytes / 2);
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      B0[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(r0 + 16 * k));
-      B1[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(r0 + 32 * kLdsRow + 16 * k));
-    }
-    __syncthreads();
-  }
+  const int64_t p0 = (int64_t)tile * PER_WG + wave * kPerWave;   // the wave's first persistent row
   // streamed operand: pass 1 = index tiles over this split of [c0, c1), pass 2 = query tiles over [0, rows)
   const uint16_t* sbase = PASS1 ? Ig : Qg;
   int64_t s_begin = PASS1 ? c0 : 0, s_end = PASS1 ? c1 : rows;
@@ -317,11 +285,47 @@ __global__ __launch_bounds__(64 * NW, 2) void meank_pass(const uint16_t* __restr
   // streamed rows [s_begin, s_end) and, in pass 2, their lse2 (tile k = rows 32k..)
   const __amdgpu_buffer_rsrc_t srows = buf_rsrc(sbase + (size_t)s_begin * D, (int)((s_end - s_begin) * kRowBytes));
   const __amdgpu_buffer_rsrc_t slse = buf_rsrc(Lg, PASS1 ? 0 : (int)(rows_pad * 4));
+  // The first two streamed tiles' loads go out before the persistent rows':
+  // a workgroup that streams few tiles (the window score's pass 2 streams
+  // four or five) would otherwise wait for them one after the other once
+  // its persistent rows are in.
   Stage<D, NT> st[PF];
   stage_load<!PASS1>(st[0], srows, 0, slse);
+  stage_load<!PASS1>(st[1], srows, 1, slse);
+  // persistent operand: pass 1 = query rows, pass 2 = index rows (block columns).
+  // The workgroup's 256 rows are read whole and coalesced (16 loads of 16 bytes
+  // per thread at D = 128; rows past the end read as zero), staged in LDS, and each wave
+  // takes its 64 rows in the operand layout from there.  Loaded straight in
+  // that layout, every load instruction would touch 64 rows 16 bytes at a
+  // time, which starves the passes that stream few tiles per workgroup.
+  bf16x8 B0[KS], B1[KS];
+  {
+    const int64_t pbase = (PASS1 ? 0 : c0) + (int64_t)tile * PER_WG;
+    const int64_t plim = PASS1 ? rows : c1;
+    const int pcount = (int)(plim <= pbase ? 0 : (plim - pbase > PER_WG ? PER_WG : plim - pbase));
+    const uint16_t* pg = (PASS1 ? Qg : Ig) + (pcount > 0 ? (size_t)pbase * D : 0);
+    const __amdgpu_buffer_rsrc_t prs = buf_rsrc(pg, pcount * kRowBytes);
+    constexpr int kLoads = PER_WG * kRowBytes / 16 / NT;
+    u32x4 v[kLoads];
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i)
+      v[i] = __builtin_amdgcn_raw_buffer_load_b128(prs, (threadIdx.x + NT * i) * 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int idx = threadIdx.x + NT * i;
+      *reinterpret_cast<u32x4*>(smem + (idx / Dm::kChunks) * kLdsRow + (idx % Dm::kChunks) * 16) = v[i];
+    }
+    __syncthreads();
+    const char* r0 = smem + (wave * kPerWave + n) * kLdsRow + h * (kRowBytes / 2);
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      B0[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(r0 + 16 * k));
+      B1[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(r0 + 32 * kLdsRow + 16 * k));
+    }
+    __syncthreads();
+  }
   stage_store<!PASS1>(st[0], tiles[0], lses[0]);
-  stage_load<!PASS1>(st[0], srows, 1, slse);
-  stage_store<!PASS1>(st[0], tiles[1], lses[1]);
+  stage_store<!PASS1>(st[1], tiles[1], lses[1]);
 #pragma unroll
   for (int k = 2; k <= PF; ++k) stage_load<!PASS1>(st[k % PF], srows, k, slse);
   __syncthreads();
