@@ -148,3 +148,52 @@ def test_meank_step_random_shapes(seed):
     ko, vo = oracle.rerope_scatter(host(Kp), host(Vp), o_sel, pt.cpu().numpy(), pos_base, theta, k0, v0)
     assert_within_ulp(bits(k_pool), ko, f"re-RoPE'd K, case {seed}", atol=1e-6)
     np.testing.assert_array_equal(bits(v_pool), vo)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_rule_paged_random_shapes(seed):
+    """The rule score read in place from a token-major pool through a seeded slot map, some slots dead
+    (-1 or past the pool): against the oracle's paged score."""
+    rng = np.random.default_rng([80, seed])
+    L, H_kv, G = int(rng.integers(1, 3)), int(rng.integers(1, 5)), int(rng.integers(1, 9))
+    H_q, D, N = G * H_kv, int(rng.choice([64, 128])), _size(rng, 4000)
+    dtype = "bf16" if rng.random() < 0.75 else "f32"
+    pool_size = N + int(rng.integers(0, 300))
+    pi, q_s, q_e = _forced(rng, N)
+    print(f"[sweep paged {seed}] L{L} Hq{H_q} Hkv{H_kv} D{D} N{N} pool{pool_size} {dtype} pi{pi} "
+          f"span[{q_s},{q_e})", flush=True)
+    pool = W.normal((L, pool_size, H_kv, D), 9300 + seed, W.T_K, dtype, DEV)
+    slots = rng.permutation(pool_size)[:N].astype(np.int64)
+    n_dead = int(rng.integers(0, min(N, 40) + 1))
+    dead_at = rng.choice(N, n_dead, replace=False) if n_dead else np.array([], dtype=np.int64)
+    slots[dead_at] = np.where(rng.random(n_dead) < 0.5, -1, pool_size + 7)
+    M = W.memory_vectors(L, H_q, D, 9300 + seed, DEV)
+    got = kvs.kvs_rule_score_paged(pool, torch.from_numpy(slots).to(DEV), M, pi, q_s, q_e)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    want = oracle.rule_score_paged(host(pool), slots, host(M), pi, q_s, q_e)
+    out = oracle.forced_mask(N, pi, q_s, q_e) | (slots < 0) | (slots >= pool_size)
+    np.testing.assert_array_equal(got[out], 0.0)
+    if (~out).any():
+        assert_rel(got[~out], want[~out], RTOL, f"paged rule score, case {seed}")
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_working_set_random_sets(seed):
+    """Differential working-set update between two seeded selections (retained blocks that keep or
+    change rank, incoming and outgoing ones): pages, ranks, released pages, the pool (K within 1 ulp,
+    V bit for bit) and every page it must not touch, against the oracle."""
+    from tests.test_gpu_meank import _workset_case
+    rng = np.random.default_rng([81, seed])
+    L, H_kv, D = int(rng.integers(1, 3)), int(rng.integers(1, 6)), int(rng.choice([64, 128]))
+    S = _size(rng, 64)
+    prev = sorted(rng.choice(S, int(rng.integers(0, S + 1)), replace=False).tolist())
+    keep_some = [b for b in prev if rng.random() < 0.6]
+    fresh = rng.choice(S, int(rng.integers(0, S + 1)), replace=False).tolist()
+    new = sorted(set(keep_some) | set(fresh))
+    pool_pages = max(len(prev), len(new), 1) + int(rng.integers(0, 8))
+    prev_pages = rng.permutation(pool_pages)[:len(prev)].tolist()
+    pos_base, with_v = int(rng.integers(0, 1 << 20)), bool(rng.random() < 0.7)
+    print(f"[sweep workset {seed}] L{L} Hkv{H_kv} D{D} blocks{S} pages{pool_pages} prev{len(prev)} "
+          f"new{len(new)} v{int(with_v)}", flush=True)
+    _workset_case(L, H_kv, D, S, pool_pages, prev, prev_pages, new, pos_base, with_v, 9400 + seed)
