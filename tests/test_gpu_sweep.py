@@ -197,3 +197,32 @@ def test_working_set_random_sets(seed):
     print(f"[sweep workset {seed}] L{L} Hkv{H_kv} D{D} blocks{S} pages{pool_pages} prev{len(prev)} "
           f"new{len(new)} v{int(with_v)}", flush=True)
     _workset_case(L, H_kv, D, S, pool_pages, prev, prev_pages, new, pos_base, with_v, 9400 + seed)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_rule_score_large_random_shapes(seed):
+    """Long caches (10k-100k positions, up to 4 layers and 8 KV heads), where the work-queue fold runs
+    thousands of chunks over every resident workgroup: the scores against the oracle, the selection
+    on them bit for bit."""
+    rng = np.random.default_rng([82, seed])
+    L, H_kv, G = int(rng.integers(1, 5)), int(rng.integers(1, 9)), int(rng.integers(1, 9))
+    H_q, D = G * H_kv, int(rng.choice([64, 128]))
+    N = int(np.exp(rng.uniform(np.log(10000), np.log(100000))))
+    pi, q_s, q_e = _forced(rng, N)
+    print(f"[sweep rule-large {seed}] L{L} Hq{H_q} Hkv{H_kv} D{D} N{N} pi{pi} span[{q_s},{q_e})", flush=True)
+    K = W.normal((L, H_kv, N, D), 9500 + seed, W.T_K, "bf16", DEV)
+    M = W.memory_vectors(L, H_q, D, 9500 + seed, DEV)
+    rule = kvs.kvs_rule_score(K, M, pi, q_s, q_e)
+    torch.cuda.synchronize()
+    got = rule.cpu().numpy()
+    want = oracle.rule_score(host(K), host(M), pi, q_s, q_e)
+    F = oracle.forced_mask(N, pi, q_s, q_e)
+    assert np.all(got[F] == 0.0)
+    assert_rel(got[~F], want[~F], RTOL, f"rule score, large case {seed}")
+    assert abs(got.sum(dtype=np.float64) - L * H_q) <= 1e-4 * L * H_q
+    C = int(rng.integers(0, N))
+    keep, idx, nk = kvs.kvs_topk_select(rule, (0, pi), (q_s, q_e), C)
+    torch.cuda.synchronize()
+    o_keep, o_idx, o_nk = oracle.topk_select(got, (0, pi), (q_s, q_e), C)
+    assert int(nk.item()) == o_nk
+    np.testing.assert_array_equal(idx[:o_nk].cpu().numpy(), o_idx)
