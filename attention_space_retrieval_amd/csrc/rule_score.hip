@@ -390,9 +390,8 @@ __device__ __forceinline__ uint64_t part_bits(float m, float s) {
 // lse[h] takes lane 0's value.  The loads of a batch of 64*KB chunks of all
 // the heads go out together.  False if a partial is still unpublished (the
 // results are then meaningless).  part: [G][n_chunks] words of the group.
-template <int HM>
+template <int HM, int KB = 4>
 __device__ bool group_lse(const uint64_t* part, int n_chunks, int h0, int hs, int G, int lane, float* lse) {
-  constexpr int KB = 4;
   float m[HM], s[HM];
 #pragma unroll
   for (int j = 0; j < HM; ++j) { m[j] = -INFINITY; s[j] = 0.f; }
@@ -811,11 +810,18 @@ __global__ __launch_bounds__(256) void rule_fold_reset(uint64_t* __restrict__ pa
 // terms computed here from the spilled logits.  VEC * 64 positions per
 // workgroup, all in one chunk (the chunk length is a multiple of that), VEC
 // consecutive positions per lane (VEC = 4 when N is a multiple of 4, so each
-// load instruction reads 1 KB of a row).  Wave w takes the groups w, w+4, ...:
-// their spill flags arrive 64 at a time in one load, and the folded values 8
-// rows at a time, before any of them is needed.
+// load instruction reads 1 KB of a row).  Sixteen waves split the groups of a
+// workgroup's positions, so each wave's chain of dependent load rounds is a
+// sixteenth of the rows long: wave w takes the groups w, w+16, ..., their
+// spill flags arriving 64 at a time in one load and the folded values 8 rows
+// at a time, before any of them is needed; the wave sums are then added in
+// wave order.  (Four waves, each walking a quarter of the rows, took 39 us
+// instead of 27 at L*H_kv = 384, N = 92160.)  The rare spill branch merges a
+// group's normalisers one head at a time, which keeps the kernel at 92
+// registers, so sixteen waves fit without spilling.
+constexpr int kColWaves = 16;                   // waves per column-sum workgroup
 template <int VEC>
-__global__ __launch_bounds__(256) void rule_fold_colsum(const float* __restrict__ fold,
+__global__ __launch_bounds__(64 * kColWaves) void rule_fold_colsum(const float* __restrict__ fold,
                                                         const float* __restrict__ spill,
                                                         const uint64_t* __restrict__ partials,
                                                         const uint32_t* __restrict__ lse,
@@ -823,13 +829,13 @@ __global__ __launch_bounds__(256) void rule_fold_colsum(const float* __restrict_
                                                         int n_chunks, int CP, int64_t N, float* __restrict__ rule) {
   constexpr int RB = 8;                 // rows per batch of loads
   using VT = std::conditional_t<VEC == 4, u32x4, uint32_t>;
-  __shared__ float part[4][64 * VEC];
+  __shared__ float part[kColWaves][64 * VEC];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t j0 = (int64_t)blockIdx.x * (64 * VEC);
   const int64_t j = j0 + (int64_t)lane * VEC;   // the lane's first position; past N a row reads as zero
   const int c = (int)(j0 / CP);
   const uint32_t* flags = spilled + (size_t)c * LHkv;
-  const int rows = (LHkv - wave + 3) / 4;   // this wave's groups: wave + 4k, k < rows
+  const int rows = (LHkv - wave + kColWaves - 1) / kColWaves;   // this wave's groups: wave + kColWaves*k, k < rows
   // one row of N floats as a buffer resource; offsets past it read zero
   auto load_row = [&](const float* row) -> VT {
     const __amdgpu_buffer_rsrc_t rs = buf_rsrc(row, (int)(N * 4));
@@ -841,19 +847,19 @@ __global__ __launch_bounds__(256) void rule_fold_colsum(const float* __restrict_
   for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
   for (int k0 = 0; k0 < rows; k0 += 64) {
     const int kk = k0 + lane;
-    const uint32_t fl = kk < rows ? flags[wave + 4 * kk] : 0u;   // lane i: the flag of the wave's row k0 + i
+    const uint32_t fl = kk < rows ? flags[wave + kColWaves * kk] : 0u;   // lane i: the flag of the wave's row k0 + i
     const int nb = min(64, rows - k0);
     for (int b0 = 0; b0 < nb; b0 += RB) {
       VT fv[RB];
 #pragma unroll
       for (int t = 0; t < RB; ++t) {
-        const int lg = wave + 4 * (k0 + min(b0 + t, nb - 1));
+        const int lg = wave + kColWaves * (k0 + min(b0 + t, nb - 1));
         fv[t] = load_row(fold + (size_t)lg * N);
       }
 #pragma unroll
       for (int t = 0; t < RB; ++t) {
         if (b0 + t >= nb) break;
-        const int lg = wave + 4 * (k0 + b0 + t);
+        const int lg = wave + kColWaves * (k0 + b0 + t);
         float v[VEC];
         if constexpr (VEC == 4) {
 #pragma unroll
@@ -873,7 +879,12 @@ __global__ __launch_bounds__(256) void rule_fold_colsum(const float* __restrict_
           }
           // Normalisers never published: no chunk of this group was folded, so
           // computing them here is consistent (and gives the same bits anyway).
-          if (!have) group_lse<8>(partials + (size_t)head0 * n_chunks, n_chunks, 0, 1, G, lane, L);
+          // one head at a time (the merge order, and so the bits, do not depend on the batching)
+          if (!have) {
+#pragma unroll
+            for (int hl = 0; hl < 8; ++hl)
+              if (hl < G) group_lse<1, 1>(partials + (size_t)head0 * n_chunks, n_chunks, hl, 1, G, lane, L);
+          }
 #pragma unroll
           for (int e = 0; e < VEC; ++e) v[e] = 0.f;
           for (int h = 0; h < G; ++h) {
@@ -894,9 +905,12 @@ __global__ __launch_bounds__(256) void rule_fold_colsum(const float* __restrict_
 #pragma unroll
   for (int e = 0; e < VEC; ++e) part[wave][lane * VEC + e] = acc[e];
   __syncthreads();
-  for (int i = threadIdx.x; i < 64 * VEC; i += 256) {
+  for (int i = threadIdx.x; i < 64 * VEC; i += 64 * kColWaves) {
     const int64_t jj = j0 + i;
-    if (jj < N) rule[jj] = ((part[0][i] + part[1][i]) + part[2][i]) + part[3][i];
+    float r = part[0][i];
+#pragma unroll
+    for (int w = 1; w < kColWaves; ++w) r += part[w][i];
+    if (jj < N) rule[jj] = r;
   }
 }
 
@@ -1047,10 +1061,10 @@ hipError_t kvs_launch_rule(const void* K, int dtype, const int64_t* slots, int64
 #undef FOLD_LAUNCH
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (N % 4 == 0)
-      hipLaunchKernelGGL(rule_fold_colsum<4>, dim3(ceil_div(N, 4 * 64)), dim3(256), 0, st, w.fold, w.spill, partials,
+      hipLaunchKernelGGL(rule_fold_colsum<4>, dim3(ceil_div(N, 4 * 64)), dim3(64 * kColWaves), 0, st, w.fold, w.spill, partials,
                          lse, w.spilled, LHkv, G, (int)nc_fold, CP, N, rule);
     else
-      hipLaunchKernelGGL(rule_fold_colsum<1>, dim3(ceil_div(N, 64)), dim3(256), 0, st, w.fold, w.spill, partials,
+      hipLaunchKernelGGL(rule_fold_colsum<1>, dim3(ceil_div(N, 64)), dim3(64 * kColWaves), 0, st, w.fold, w.spill, partials,
                          lse, w.spilled, LHkv, G, (int)nc_fold, CP, N, rule);
     return hipGetLastError();
   }
