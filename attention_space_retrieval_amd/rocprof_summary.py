@@ -32,7 +32,7 @@ KERNEL_SOURCES = {
     "rule_logits_mfma": "rule_score.hip", "rule_logits_f32": "rule_score.hip",
     "rule_lse_merge": "rule_score.hip", "rule_colsum": "rule_score.hip",
     "rule_fold_reset": "rule_score.hip", "rule_fold_queue": "rule_score.hip", "rule_fold_colsum": "rule_score.hip",
-    "topk_reg_kernel": "topk.hip", "topk_stream_kernel": "topk.hip", "topk_mw_init": "topk.hip",
+    "topk_wg_kernel": "topk.hip", "topk_stream_kernel": "topk.hip", "topk_mw_init": "topk.hip",
     "topk_mw_minmax": "topk.hip", "topk_mw_pass": "topk.hip", "topk_mw_count": "topk.hip",
     "topk_mw_emit": "topk.hip", "keep_all_kernel": "topk.hip",
     "slotmap_kernel": "topk.hip",

@@ -62,8 +62,8 @@ CALL_KERNELS = {
     "kvs_rule_score": ["rule_fold_reset", "rule_fold_queue<128, false, 1024, 3>", "rule_fold_colsum<4>"],
     # the redirect runs inside the multi-workgroup emit, and as its own kernel after a one-workgroup
     # selection
-    "kvs_topk_select_redirect[rule]": ["topk_reg_kernel<32>", "slotmap_kernel"],
-    "kvs_topk_select[meank]": ["topk_reg_kernel<8>"],
+    "kvs_topk_select_redirect[rule]": ["topk_wg_kernel<8>", "slotmap_kernel"],
+    "kvs_topk_select[meank]": ["topk_wg_kernel<2>"],
     "kvs_meank_build": ["meank_build_raw<128>"],
     "kvs_meank_score": ["meank_pass<true, false, 4, 128>", "meank_pass<false, false, 4, 128>", "meank_reduce<false>"],
     "kvs_rerope_scatter": ["rerope_scatter_kernel<128>", "v_scatter_kernel<128>"],
@@ -83,7 +83,7 @@ def call_kernels(workload):
     if workload == "rule-14b+meank-1m":
         ck["kvs_rule_score"] = ["rule_fold_reset", "rule_fold_queue<128, false, 1024, 2>", "rule_fold_colsum<4>"]
         ck["kvs_topk_select_redirect[rule]"] = TOPK_MW              # n = 92160
-        ck["kvs_topk_select[meank]"] = ["topk_reg_kernel<32>"]      # n = 32768 blocks
+        ck["kvs_topk_select[meank]"] = ["topk_wg_kernel<8>"]       # n = 32768 blocks
         # the 1M workspace keeps no V beside raw K (the scatter reads the packed staging buffers), so
         # the working-set update there moves K only
         ck["kvs_working_set_update"] = ["workset_diff", "workset_apply<128, false>"]

@@ -30,7 +30,7 @@ def test_call_kernels_follow_the_workload():
     big = bench.call_kernels("rule-14b+meank-1m")
     small = bench.call_kernels("rule-8b+meank-256k")
     assert "topk_mw_pass*4" in big["kvs_topk_select_redirect[rule]"]
-    assert small["kvs_topk_select_redirect[rule]"] == ["topk_reg_kernel<32>", "slotmap_kernel"]
+    assert small["kvs_topk_select_redirect[rule]"] == ["topk_wg_kernel<8>", "slotmap_kernel"]
     # the fold's workgroups per CU follow G: 3 at rule-8b (G = 4), 2 at rule-14b (G = 5)
     assert small["kvs_rule_score"][1].endswith("1024, 3>") and big["kvs_rule_score"][1].endswith("1024, 2>")
     assert big["kvs_meank_score"] == small["kvs_meank_score"]

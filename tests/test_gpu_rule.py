@@ -457,6 +457,20 @@ def test_topk_concentrated_scores(n, C):
         check_topk(score, (0, 64), (n - 64, n), C, single_workgroup=True)
 
 
+@pytest.mark.parametrize("n,C,spread", [(32768, 8192, 1e-6), (8192, 3000, 1e-5), (32768, 20000, 0.0),
+                                         (92160, 8192, 1e-6)])
+def test_topk_cluster_with_outliers(n, C, spread):
+    """A dense cluster and a few far outliers: the first 11-bit digit of the candidates' key range
+    puts the whole cluster into one bin, far more keys than the one-workgroup kernel ranks directly,
+    so its 8-bit passes over the keys in registers find the threshold (spread 0: every cluster key
+    ties)."""
+    g = np.random.default_rng([n, 17])
+    x = 1.0 + spread * g.standard_normal(n)
+    x[g.choice(n, 16, replace=False)] = 1e3 * (1.0 + g.random(16))
+    score = torch.from_numpy(x.astype(np.float32)).to(DEV)
+    check_topk(score, (0, 4), (n - 64, n), C)
+
+
 def test_topk_special_values():
     s = torch.tensor([float("nan"), -float("inf"), 0.0, -0.0, 1.0, float("inf"), -1e-30, 1e-30,
                       float("nan"), 0.0], device=DEV)
@@ -488,7 +502,7 @@ def test_slotmap_bit_exact():
 
 
 @pytest.mark.parametrize("n,C,f0,f1,single,in_place", [
-    (5000, 700, (0, 16), (4900, 4964), False, False),        # one workgroup, keys in registers (8 per thread)
+    (5000, 700, (0, 16), (4900, 4964), False, False),        # one workgroup, keys in registers (8 per thread, two 16-byte loads)
     (30000, 4096, (0, 64), (29936, 30000), False, True),     # 32 per thread, slots redirected in place
     (92160, 8192, (0, 64), (92096, 92160), False, False),    # several workgroups
     (92160, 8192, (0, 64), (92096, 92160), True, True),      # one workgroup streaming from L2
