@@ -5,7 +5,8 @@
 // reads 64/(D/8) rows of the span, and a batch of such loads is in flight at
 // once (one wave per head leaves latency, not bandwidth, as the limit).  The
 // per-lane partial sums are combined over the row groups with a fixed
-// butterfly, the squared norm over the lanes of a row the same way.
+// butterfly, the squared norm over the lanes of a row the same way.  The
+// previous M row is read first, so its load overlaps the span's.
 #include "kvs_internal.h"
 
 using namespace kvs;
@@ -24,6 +25,12 @@ __global__ __launch_bounds__(256) void qmem_kernel(const void* __restrict__ q, i
   const int lh = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (lh >= LH) return;
   const int cl = lane % LPR, rr = lane / LPR;
+  // the previous M goes out first, so its load overlaps the span's instead of following the sums
+  float* m = M + (size_t)lh * D + (size_t)cl * 8;
+  float mprev[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) mprev[e] = m[e];   // (read on the first turn too, and not used)
+  __builtin_amdgcn_sched_barrier(0);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   // Rows go through a buffer resource over each batch of NB * RPL rows, so the
   // loads of a batch issue together with no branch and rows past S read as
@@ -57,13 +64,12 @@ __global__ __launch_bounds__(256) void qmem_kernel(const void* __restrict__ q, i
   for (int o = LPR; o < 64; o <<= 1)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o, kWave);
-  float* m = M + (size_t)lh * D + (size_t)cl * 8;
   float v[8];
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float enc = acc[e] / (float)S;
-    v[e] = first_turn ? enc : fmaf(decay, m[e], enc);
+    v[e] = first_turn ? enc : fmaf(decay, mprev[e], enc);
     ss = fmaf(v[e], v[e], ss);
   }
 #pragma unroll
