@@ -90,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void topk_wg_kernel(
     uint8_t* __restrict__ keep_mask, int32_t* __restrict__ keep_idx, int64_t* __restrict__ n_kept) {
   // the first-digit histograms; the 8-bit passes use the same words as one
   // 256-bin histogram per wave
-  __shared__ uint32_t hist[kWgHists * kWgBins + 64];   // + one discard word per lane
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kWgHists * kWgBins + 64];   // + one discard word per lane
   __shared__ uint32_t lst[kList];
   __shared__ uint32_t wred[kWaves][2];
   __shared__ uint32_t wsum[kWaves];

@@ -545,6 +545,11 @@ def main():
     turn = ("kvs_qmem_update", "kvs_rule_score", "kvs_topk_select_redirect[rule]")
     rule_ms = sum(per_call[k] for k in turn)
     rule_bytes = sum(work[k][1] for k in turn)
+    # the eviction step alone (rule score, then top-k with the slot redirect), without the QueryMemory
+    # update that precedes it in a turn
+    select = ("kvs_rule_score", "kvs_topk_select_redirect[rule]")
+    sel_ms = sum(per_call[k] for k in select)
+    sel_bytes = sum(work[k][1] for k in select)
     out = {
         "metric": METRIC,
         "value": tokens / (ms_per_step * 1e-3),
@@ -565,6 +570,8 @@ def main():
         "rule_turn": {"ms": round(rule_ms, 4), "tokens_per_s": c["N"] / (rule_ms * 1e-3),
                       "hbm_gbps": rule_bytes / (rule_ms * 1e-3) / 1e9,
                       "frac_hbm_peak": rule_bytes / (rule_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "rule_select": {"ms": round(sel_ms, 4), "hbm_gbps": sel_bytes / (sel_ms * 1e-3) / 1e9,
+                        "frac_hbm_peak": sel_bytes / (sel_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "meank_score_tflops": rows["kvs_meank_score"]["achieved"],
         # the exact R_b runs two passes over the same tiles (row normalisers, then column sums), so
         # it executes twice the algorithmic flops; the mix ceiling is the rate a register-only loop
