@@ -24,7 +24,9 @@
 // and use immediate offsets) and software-pipelines each wave: each MFMA of
 // tile t+1 is followed by a slice of tile t's exp2 epilogue, so the matrix and
 // vector units overlap.  The same engine serves the window score (the SnapKV
-// window of query rows over the cache's keys; see the end of this file).
+// window of query rows over the cache's keys; see the end of this file).  R_b
+// at D = 128 runs meank_pass_dma, the same pipeline with the streamed tiles
+// brought into LDS by load-to-LDS DMA (below).
 // Workgroups are mapped XCD-aware: the tiles of one (l, g) land on the same
 // XCD and share its L2 copy of the streamed operand.
 // Operand k-slots: lane half h = lane/32 carries k-slots 8h..8h+7 of every
@@ -472,6 +474,228 @@ __global__ __launch_bounds__(64 * NW, 2) void meank_pass(const uint16_t* __restr
   }
 }
 
+// R_b's passes with the streamed tiles fed to LDS by load-to-LDS DMA
+// (`buffer_load_dwordx4 ... lds`, gfx950) instead of through a ring of
+// register stages and LDS stores.  Each lane's 16 bytes land at the
+// instruction's LDS base + 16 * lane, from any global offset the lane names,
+// so a tile is laid out unpadded (32 rows of 256 bytes) with chunk c of row r
+// at chunk position c ^ (r & 15): the operand reads of 16 consecutive rows
+// then still hit 16 distinct bank groups.  kDmaBufs tiles are in flight;
+// tile k is issued kDmaBufs - 1 tiles ahead of its use, each wave waits for
+// its own part of the next tile with an explicit vmcnt (nothing else in the
+// loop touches vector memory), and a bare s_barrier (no fence, which would
+// wait for every outstanding DMA) publishes it.  A row past the end of the
+// streamed rows reads as zero.  The persistent operand is loaded straight in
+// operand layout: it is read once per workgroup, against hundreds of
+// streamed tiles.  D = 128 only.  Same-process A/B against meank_pass, same
+// bits: meank-256k 5.00 -> 4.86 ms, meank-1m 39.4 -> 38.2 ms (a ring of six
+// tiles measured level with four).
+constexpr int kDmaBufs = 4;
+
+// One load-to-LDS DMA of 16 bytes a lane: lane l's bytes go to lds + 16 * l.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
+template <bool PASS1>
+__global__ __launch_bounds__(256, 2) void meank_pass_dma(const uint16_t* __restrict__ Q,
+                                                         const uint16_t* __restrict__ index, int LG,
+                                                         int64_t rows, int64_t rows_pad, int64_t nB,
+                                                         int64_t c0, int64_t c1, int T, float scale,
+                                                         float* __restrict__ lse2, float* __restrict__ colpart) {
+  constexpr int D = 128;
+  using Dm = Dims<D>;
+  constexpr int KS = Dm::KS, kRowBytes = Dm::kRowBytes, kChunks = Dm::kChunks;
+  constexpr int NT = 256, PER_WG = 4 * kPerWave;
+  // DMA instructions a wave issues per tile: its two 1 KB quarters of the tile, and in pass 2
+  // its 32-byte quarter of the tile's lse2 (two lanes)
+  constexpr int kPerTile = PASS1 ? 2 : 3;
+  __shared__ __attribute__((aligned(16))) char tb0[kTile * kRowBytes];
+  __shared__ __attribute__((aligned(16))) char tb1[kTile * kRowBytes];
+  __shared__ __attribute__((aligned(16))) char tb2[kTile * kRowBytes];
+  __shared__ __attribute__((aligned(16))) char tb3[kTile * kRowBytes];
+  __shared__ __attribute__((aligned(16))) float lb0[kTile];
+  __shared__ __attribute__((aligned(16))) float lb1[kTile];
+  __shared__ __attribute__((aligned(16))) float lb2[kTile];
+  __shared__ __attribute__((aligned(16))) float lb3[kTile];
+  int lg, tile;
+  xcd_map(T, LG, lg, tile);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n = lane & 31, h = lane >> 5;
+  const uint16_t* Qg = Q + (size_t)lg * rows * D;
+  const uint16_t* Ig = index + (size_t)lg * nB * D;
+  const float* Lg = lse2 + (size_t)lg * rows_pad;
+  const int64_t p0 = (int64_t)tile * PER_WG + wave * kPerWave;   // the wave's first persistent row
+
+  const uint16_t* sbase = PASS1 ? Ig : Qg;
+  const int64_t s_begin = PASS1 ? c0 : 0, s_end = PASS1 ? c1 : rows;
+  const int nt = (int)((s_end - s_begin + kTile - 1) / kTile);
+  const __amdgpu_buffer_rsrc_t srows = buf_rsrc(sbase + (size_t)s_begin * D, (int)((s_end - s_begin) * kRowBytes));
+  const __amdgpu_buffer_rsrc_t slse = buf_rsrc(Lg, PASS1 ? 0 : (int)(rows_pad * 4));
+  // this lane's global byte offsets within a tile for its two DMA quarters (rows 4q .. 4q+3 of
+  // quarter q = 2 * wave + i, chunk position lane & 15 holding chunk (lane & 15) ^ (row & 15))
+  int goff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 4 * (2 * wave + i) + (lane >> 4);
+    goff[i] = r * kRowBytes + (((lane & 15) ^ (r & 15)) * 16);
+  }
+  auto issue = [&](int k, char* tb, float* lb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(srows, tb + (2 * wave + i) * 1024, k * (kTile * kRowBytes) + goff[i]);
+    if (!PASS1) {
+      if (lane < 2) dma16(slse, lb + 8 * wave, (k * kTile + 8 * wave) * 4 + 16 * lane);
+    }
+  };
+  // the operand read of a tile: lane (n, h) takes row n's chunks 8h .. 8h+7, swizzled
+  auto read_tile = [&](const char* tb, bf16x8* A) __attribute__((always_inline)) {
+    const char* row = tb + n * kRowBytes;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      A[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + (((8 * h + s) ^ (n & 15)) * 16)));
+  };
+  // s_waitcnt with vmcnt <= kPerTile, expcnt and lgkmcnt left alone (gfx9 encoding)
+  constexpr int kWaitNext = (kPerTile & 15) | (7 << 4) | (15 << 8) | ((kPerTile >> 4) << 14);
+
+  issue(0, tb0, lb0);
+  issue(1, tb1, lb1);
+  issue(2, tb2, lb2);
+  // persistent operand straight from global memory in operand layout (rows past the end read zero)
+  bf16x8 B0[KS], B1[KS];
+  {
+    const int64_t pbase = (PASS1 ? 0 : c0) + (int64_t)tile * PER_WG;
+    const int64_t plim = PASS1 ? rows : c1;
+    const int pcount = (int)(plim <= pbase ? 0 : (plim - pbase > PER_WG ? PER_WG : plim - pbase));
+    const uint16_t* pg = (PASS1 ? Qg : Ig) + (pcount > 0 ? (size_t)pbase * D : 0);
+    const __amdgpu_buffer_rsrc_t prs = buf_rsrc(pg, pcount * kRowBytes);
+    const int r0 = (wave * kPerWave + n) * kRowBytes + h * (kRowBytes / 2);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      B0[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(prs, r0 + 16 * s, 0, 0));
+      B1[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(prs, r0 + 32 * kRowBytes + 16 * s, 0, 0));
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_barrier();
+
+  const bool live = p0 < (PASS1 ? rows : c1 - c0);   // wave-uniform
+  bf16x8 A[KS];
+  f32x16 cA0 = {}, cA1 = {}, cB0 = {}, cB1 = {};
+  float lA[16], lB[16];
+  read_tile(tb0, A);
+  if (!PASS1) read_lse16(lb0, h, lA);
+  if (live) mma2<D>(A, B0, B1, cA0, cA1);
+
+  float m0, m1, s0 = 0.f, s1 = 0.f;
+  if (PASS1) {
+    f32x16 x0 = cA0, x1 = cA1;
+    if (nt == 1) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (s_begin + c_row(v, h) >= s_end) { x0[v] = -INFINITY; x1[v] = -INFINITY; }
+    }
+    m0 = fmaxf(tile_max(x0) * scale, -3.0e38f);
+    m1 = fmaxf(tile_max(x1) * scale, -3.0e38f);
+    m0 = fmaxf(m0, __shfl_xor(m0, 32, kWave));
+    m1 = fmaxf(m1, __shfl_xor(m1, 32, kWave));
+  }
+
+  // body t: issue tile t+3 into the buffer tile t-1 used, read tile t+1, MFMAs of t+1 with the
+  // epilogue of t, then wait for this wave's part of tile t+2 and meet the others
+  auto body = [&](int t, char* tb_issue, float* lb_issue, const char* tb_read, const float* lb_read,
+                  f32x16& cc0, f32x16& cc1, float* lc, f32x16& cn0, f32x16& cn1, float* ln) __attribute__((always_inline)) {
+    issue(t + 3, tb_issue, lb_issue);
+    read_tile(tb_read, A);
+    if (!PASS1) read_lse16(lb_read, h, ln);
+    float a0 = 0.f, a1 = 0.f;
+    if (live) step_mma_epi<PASS1, D>(A, B0, B1, cn0, cn1, cc0, cc1, scale, lc, m0, m1, a0, a1);
+    if (PASS1) {
+      if (__builtin_expect(__ballot(!(a0 <= kRebase) || !(a1 <= kRebase)) != 0, 0)) {
+        lse_fold<false>(cc0, scale, m0, s0, a0, 0, h, c1, 0, 0);
+        lse_fold<false>(cc1, scale, m1, s1, a1, 0, h, c1, 0, 0);
+      } else {
+        s0 += a0;
+        s1 += a1;
+      }
+    } else {
+      s0 += a0;
+      s1 += a1;
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitNext);
+    __builtin_amdgcn_s_barrier();
+  };
+  // t % 4 fixes the buffers (issue into (t+3)%4, read (t+1)%4) and t % 2 the accumulators
+  auto body_k = [&](int t, auto kc) __attribute__((always_inline)) {
+    constexpr int k = decltype(kc)::value;
+    char* tbs[4] = {tb0, tb1, tb2, tb3};
+    float* lbs[4] = {lb0, lb1, lb2, lb3};
+    if constexpr ((k & 1) != 0)
+      body(t, tbs[(k + 3) & 3], lbs[(k + 3) & 3], tbs[(k + 1) & 3], lbs[(k + 1) & 3], cB0, cB1, lB, cA0, cA1, lA);
+    else
+      body(t, tbs[(k + 3) & 3], lbs[(k + 3) & 3], tbs[(k + 1) & 3], lbs[(k + 1) & 3], cA0, cA1, lA, cB0, cB1, lB);
+  };
+  using K0 = std::integral_constant<int, 0>;
+  using K1 = std::integral_constant<int, 1>;
+  using K2 = std::integral_constant<int, 2>;
+  using K3 = std::integral_constant<int, 3>;
+  int t = 0;
+  for (; t + 4 < nt; t += 4) {
+    body_k(t, K0{});
+    body_k(t + 1, K1{});
+    body_k(t + 2, K2{});
+    body_k(t + 3, K3{});
+  }
+  if (t + 1 < nt) {
+    body_k(t, K0{});
+    if (t + 2 < nt) {
+      body_k(t + 1, K1{});
+      if (t + 3 < nt) body_k(t + 2, K2{});
+    }
+  }
+  // the last tile, nt - 1, was computed by body nt - 2 (B if that is even), or by the prologue
+  const bool last_b = nt >= 2 && (nt & 1) == 0;
+  f32x16* last0 = last_b ? &cB0 : &cA0;
+  f32x16* last1 = last_b ? &cB1 : &cA1;
+  float* llast = last_b ? lB : lA;
+  if (PASS1) {
+    const int64_t b0 = s_begin + (int64_t)(nt - 1) * kTile;
+    lse_fold<true>(*last0, scale, m0, s0, 0.f, b0, h, s_end, 0, 0);
+    lse_fold<true>(*last1, scale, m1, s1, 0.f, b0, h, s_end, 0, 0);
+  } else {
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      a0 += __builtin_amdgcn_exp2f(fmaf((*last0)[v], scale, -llast[v]));
+      a1 += __builtin_amdgcn_exp2f(fmaf((*last1)[v], scale, -llast[v]));
+    }
+    s0 += a0;
+    s1 += a1;
+  }
+  // the DMAs issued for tiles past the end must land before the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(0);
+
+  if (PASS1) {
+    float mm = __shfl_xor(m0, 32, kWave), ss = __shfl_xor(s0, 32, kWave);
+    lse_merge(m0, s0, mm, ss);
+    mm = __shfl_xor(m1, 32, kWave);
+    ss = __shfl_xor(s1, 32, kWave);
+    lse_merge(m1, s1, mm, ss);
+    if (h == 0) {
+      const int64_t r0 = p0 + n, r1 = p0 + 32 + n;
+      if (r0 < rows_pad) lse2[(size_t)lg * rows_pad + r0] = (r0 < rows && s0 > 0.f) ? m0 + log2f(s0) : INFINITY;
+      if (r1 < rows_pad) lse2[(size_t)lg * rows_pad + r1] = (r1 < rows && s1 > 0.f) ? m1 + log2f(s1) : INFINITY;
+    }
+  } else {
+    s0 += __shfl_xor(s0, 32, kWave);
+    s1 += __shfl_xor(s1, 32, kWave);
+    if (h == 0) {
+      const int64_t b0 = c0 + p0 + n, b1 = c0 + p0 + 32 + n;
+      if (b0 < c1) colpart[(size_t)lg * nB + b0] = s0;
+      if (b1 < c1) colpart[(size_t)lg * nB + b1] = s1;
+    }
+  }
+}
+
 // Row lse from the pass-1 split partials, merged in split order.
 __global__ __launch_bounds__(256) void meank_lse_merge(const float2* __restrict__ part1, int64_t n_rows,
                                                        int64_t rows, int64_t rows_pad, int n_split,
@@ -534,15 +758,26 @@ hipError_t launch_meank_score(const uint16_t* Qb, const uint16_t* Ib, int L, int
   const float scale = (float)(1.4426950408889634 / __builtin_sqrt((double)D));
   if (c1 > c0 && rows > 0) {
     const int T1 = (int)ceil_div(rows_pad, kPerWG);
-    hipLaunchKernelGGL((meank_pass<true, false, 4, D>), dim3((unsigned)T1 * LG), dim3(256), 0, st, Qb, Ib, LG, rows,
-                       rows_pad, nB, c0, c1, (int64_t)0, (int64_t)0, T1, scale, 1, lse2, nullptr, colpart);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     const int T2 = (int)ceil_div(c1 - c0, kPerWG);
-    hipLaunchKernelGGL((meank_pass<false, false, 4, D>), dim3((unsigned)T2 * LG), dim3(256), 0, st, Qb, Ib, LG, rows,
-                       rows_pad, nB, c0, c1, (int64_t)0, (int64_t)0, T2, scale, 1, lse2, nullptr, colpart);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if constexpr (D == 128) {
+      hipLaunchKernelGGL((meank_pass_dma<true>), dim3((unsigned)T1 * LG), dim3(256), 0, st, Qb, Ib, LG, rows,
+                         rows_pad, nB, c0, c1, T1, scale, lse2, colpart);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((meank_pass_dma<false>), dim3((unsigned)T2 * LG), dim3(256), 0, st, Qb, Ib, LG, rows,
+                         rows_pad, nB, c0, c1, T2, scale, lse2, colpart);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    } else {
+      hipLaunchKernelGGL((meank_pass<true, false, 4, D>), dim3((unsigned)T1 * LG), dim3(256), 0, st, Qb, Ib, LG, rows,
+                         rows_pad, nB, c0, c1, (int64_t)0, (int64_t)0, T1, scale, 1, lse2, nullptr, colpart);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((meank_pass<false, false, 4, D>), dim3((unsigned)T2 * LG), dim3(256), 0, st, Qb, Ib, LG, rows,
+                         rows_pad, nB, c0, c1, (int64_t)0, (int64_t)0, T2, scale, 1, lse2, nullptr, colpart);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   } else {
     c1 = c0;   // no candidates (or no queries): every R_b is 0
   }

@@ -38,7 +38,8 @@ KERNEL_SOURCES = {
     "slotmap_kernel": "topk.hip",
     "meank_build_raw": "meank_build.hip", "meank_build_derope": "meank_build.hip",
     "meank_append_kernel": "meank_build.hip",
-    "meank_pass": "meank_score.hip", "meank_reduce": "meank_score.hip", "meank_lse_merge": "meank_score.hip",
+    "meank_pass": "meank_score.hip", "meank_pass_dma": "meank_score.hip", "meank_reduce": "meank_score.hip",
+    "meank_lse_merge": "meank_score.hip",
     "rerope_scatter_kernel": "rerope_scatter.hip", "v_scatter_kernel": "rerope_scatter.hip",
     "workset_diff": "workset.hip", "workset_apply": "workset.hip",
 }

@@ -65,7 +65,7 @@ CALL_KERNELS = {
     "kvs_topk_select_redirect[rule]": ["topk_wg_kernel<8>", "slotmap_kernel"],
     "kvs_topk_select[meank]": ["topk_wg_kernel<2>"],
     "kvs_meank_build": ["meank_build_raw<128>"],
-    "kvs_meank_score": ["meank_pass<true, false, 4, 128>", "meank_pass<false, false, 4, 128>", "meank_reduce<false>"],
+    "kvs_meank_score": ["meank_pass_dma<true>", "meank_pass_dma<false>", "meank_reduce<false>"],
     "kvs_rerope_scatter": ["rerope_scatter_kernel<128>", "v_scatter_kernel<128>"],
     # rows beyond the step (timed after it): the paged rule score takes 768-position chunks
     "kvs_rule_score_paged": ["rule_fold_reset", "rule_fold_queue<128, true, 768, 3>", "rule_fold_colsum<4>"],
