@@ -489,12 +489,15 @@ __global__ __launch_bounds__(64 * NW, 2) void meank_pass(const uint16_t* __restr
 // operand layout: it is read once per workgroup, against hundreds of
 // streamed tiles.  D = 128 only.  Same-process A/B against meank_pass, same
 // bits: meank-256k 5.00 -> 4.86 ms, meank-1m 39.4 -> 38.2 ms (a ring of six
-// tiles measured level with four).
+// tiles measured level with four); with the lane's operand offsets computed
+// once (each buffer's base in the read's immediate offset) and the tile's
+// offset in the DMA's scalar offset, a further 1-1.4%.
 constexpr int kDmaBufs = 4;
 
-// One load-to-LDS DMA of 16 bytes a lane: lane l's bytes go to lds + 16 * l.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+// One load-to-LDS DMA of 16 bytes a lane: lane l's bytes go to lds + 16 * l, from the lane's
+// offset voff plus the wave-uniform offset soff.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
 
 template <bool PASS1>
@@ -542,17 +545,23 @@ __global__ __launch_bounds__(256, 2) void meank_pass_dma(const uint16_t* __restr
   }
   auto issue = [&](int k, char* tb, float* lb) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(srows, tb + (2 * wave + i) * 1024, k * (kTile * kRowBytes) + goff[i]);
+    for (int i = 0; i < 2; ++i) dma16(srows, tb + (2 * wave + i) * 1024, goff[i], k * (kTile * kRowBytes));
     if (!PASS1) {
-      if (lane < 2) dma16(slse, lb + 8 * wave, (k * kTile + 8 * wave) * 4 + 16 * lane);
+      if (lane < 2) dma16(slse, lb + 8 * wave, 32 * wave + 16 * lane, k * kTile * 4);
     }
   };
-  // the operand read of a tile: lane (n, h) takes row n's chunks 8h .. 8h+7, swizzled
-  auto read_tile = [&](const char* tb, bf16x8* A) __attribute__((always_inline)) {
-    const char* row = tb + n * kRowBytes;
+  // the operand read of a tile: lane (n, h) takes row n's chunks 8h .. 8h+7, swizzled.  The
+  // lane's eight byte offsets within a tile are computed once (and kept opaque, so they are not
+  // re-derived per tile); each buffer's base then goes into the read's immediate offset.
+  int roff[KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-      A[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(row + (((8 * h + s) ^ (n & 15)) * 16)));
+  for (int s = 0; s < KS; ++s) {
+    roff[s] = n * kRowBytes + (((8 * h + s) ^ (n & 15)) * 16);
+    asm volatile("" : "+v"(roff[s]));
+  }
+  auto read_tile = [&](const char* tb, bf16x8* A) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) A[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tb + roff[s]));
   };
   // s_waitcnt with vmcnt <= kPerTile, expcnt and lgkmcnt left alone (gfx9 encoding)
   constexpr int kWaitNext = (kPerTile & 15) | (7 << 4) | (15 << 8) | ((kPerTile >> 4) << 14);
