@@ -4,6 +4,11 @@
         -> Markdown table of per-kernel durations (stdout)
     python -m attention_space_retrieval_amd.rocprof_summary traffic FETCH_CSV WRITE_CSV --command CMD
         -> JSON with HBM bytes per dispatch for every library kernel (stdout)
+    python -m attention_space_retrieval_amd.rocprof_summary counters COUNTER_CSV --kernel NAME ... --command CMD
+        -> Markdown table of MFMA, VALU, exp2, clock and wait figures per named kernel, the mean over
+           its dispatches, from one --pmc run of SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_INSTS_MFMA
+           SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32 SQ_WAIT_INST_ANY SQ_WAVE_CYCLES
+           SQ_VALU_MFMA_COEXEC_CYCLES GRBM_GUI_ACTIVE (stdout)
 
 The traffic summary scales the counters by what they read for the runtime's
 own device copy of known size (bench.py --copy-calibration copies 4 GiB):
@@ -134,6 +139,50 @@ def traffic_json(fetch_csv, write_csv, command):
             "kernels": kernels}
 
 
+def counters_markdown(path, kernels, command, n_simd=1024, n_xcd=8):
+    """Per-kernel means over the dispatches whose short name starts with one of `kernels`."""
+    per = collections.defaultdict(dict)
+    meta = {}
+    for r in csv.DictReader(open(path)):
+        name = short_name(r["Kernel_Name"])
+        if not any(name.startswith(k) for k in kernels):
+            continue
+        d = int(r["Dispatch_Id"])
+        per[d][r["Counter_Name"]] = float(r["Counter_Value"])
+        meta[d] = (name, int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+    cols = collections.OrderedDict()
+    for d in sorted(per):
+        name, t0, t1 = meta[d]
+        c, dur = per[d], (t1 - t0) * 1e-9
+        cyc = c["GRBM_GUI_ACTIVE"] / n_xcd
+        rows = cols.setdefault(name, collections.defaultdict(list))
+        rows["dur"].append(dur * 1e3)
+        rows["mfma"].append(c["SQ_INSTS_MFMA"])
+        rows["trans"].append(c["SQ_INSTS_VALU_TRANS_F32"] * 64)
+        rows["valu"].append(c["SQ_INSTS_VALU"] / c["SQ_INSTS_MFMA"])
+        rows["clk"].append(cyc / dur / 1e9)
+        rows["busy"].append(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (n_simd * cyc))
+        rows["coexec"].append(c["SQ_VALU_MFMA_COEXEC_CYCLES"] / c["SQ_VALU_MFMA_BUSY_CYCLES"])
+        rows["wait"].append(c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"])
+    mean = lambda v: sum(v) / len(v)
+    names = list(cols)
+    lines = ["Command (repository root, one MI355X):", "", f"    {command}", "",
+             "| per dispatch (mean over " + ", ".join(f"{len(cols[n]['dur'])}" for n in names) + " dispatches) | "
+             + " | ".join(f"`{n}`" for n in names) + " |", "|---" * (len(names) + 1) + "|"]
+    def row(label, f):
+        lines.append(f"| {label} | " + " | ".join(f(cols[n]) for n in names) + " |")
+    row("duration (dispatch timestamps)", lambda c: f"{mean(c['dur']):.2f} ms ({min(c['dur']):.2f}-{max(c['dur']):.2f})")
+    row("SQ_INSTS_MFMA", lambda c: f"{int(mean(c['mfma'])):,}")
+    row("executed MFMA flops (32x32x16: 32768 each)", lambda c: f"{mean(c['mfma']) * 32768:.4e}")
+    row("SQ_INSTS_VALU_TRANS_F32 x 64 lanes", lambda c: f"{mean(c['trans']):.4e}")
+    row("SQ_INSTS_VALU per MFMA (the MFMA itself counted)", lambda c: f"{mean(c['valu']):.2f}")
+    row("clock = GRBM_GUI_ACTIVE / XCDs / duration", lambda c: f"{mean(c['clk']):.2f} GHz ({min(c['clk']):.2f}-{max(c['clk']):.2f})")
+    row("matrix cores busy = MFMA busy / (SIMDs x cycles)", lambda c: f"{100 * mean(c['busy']):.0f}%")
+    row("VALU co-executing with the matrix cores", lambda c: f"{100 * mean(c['coexec']):.0f}%")
+    row("SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES", lambda c: f"{100 * mean(c['wait']):.0f}%")
+    return "\n".join(lines) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -144,8 +193,14 @@ def main(argv=None):
     t.add_argument("fetch_csv")
     t.add_argument("write_csv")
     t.add_argument("--command", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("csv")
+    c.add_argument("--kernel", action="append", required=True)
+    c.add_argument("--command", required=True)
     a = ap.parse_args(argv)
-    if a.what == "stats":
+    if a.what == "counters":
+        sys.stdout.write(counters_markdown(a.csv, a.kernel, a.command))
+    elif a.what == "stats":
         sys.stdout.write(stats_markdown(a.csv, a.command))
     else:
         json.dump(traffic_json(a.fetch_csv, a.write_csv, a.command), sys.stdout, indent=1)
