@@ -394,6 +394,35 @@ def check_topk(score, f0, f1, C, single_workgroup=False):
     np.testing.assert_array_equal(idx[:nk].cpu().numpy(), oidx)
 
 
+@pytest.mark.parametrize("n,single", [(5, False), (77, False), (1025, False), (4097, False), (4098, False),
+                                      (4099, False), (8191, False), (8193, False), (32767, False),
+                                      (32769, False), (92161, False), (40001, True)])
+@pytest.mark.parametrize("offset", [0, 1])
+def test_topk_ragged_tail_candidates(n, single, offset):
+    """No forced range, and the largest scores at the last three positions: a selection whose last
+    16-byte load of scores is only partly inside n must still see them.  offset = 1 views the
+    scores, the mask and the indices one element into their allocations (4, 1 and 4 bytes past
+    a 16-byte boundary)."""
+    base = W.scores_with_ties(n + offset, 900 + n, None).clone()
+    for i, v in enumerate((100.0, 99.0, 98.0)):
+        if n - 1 - i >= 0:
+            base[offset + n - 1 - i] = v
+    score = base.to(DEV)[offset:]
+    for C in (1, 3, n // 2 + 1):
+        print(f"[topk tail] n={n} offset={offset} single={single} C={C}", flush=True)
+        keep = torch.full((n + offset,), 7, dtype=torch.uint8, device=DEV)[offset:]
+        idx = torch.full((n + offset,), -5, dtype=torch.int32, device=DEV)[offset:]
+        keep, idx, nk = kvs.kvs_topk_select(score, (0, 0), (0, 0), C, keep_mask=keep, keep_idx=idx,
+                                            single_workgroup=single)
+        torch.cuda.synchronize()
+        ok, oidx, onk = oracle.topk_select(score.cpu().numpy(), (0, 0), (0, 0), C)
+        nk = int(nk.item())
+        assert nk == onk == min(C, n)
+        np.testing.assert_array_equal(keep.cpu().numpy().astype(bool), ok)
+        np.testing.assert_array_equal(idx[:nk].cpu().numpy(), oidx)
+        assert set(range(max(0, n - min(C, 3)), n)) <= set(oidx.tolist())
+
+
 @pytest.mark.parametrize("n,levels,f0,f1,C", [
     (1024, None, (0, 16), (992, 1024), 256),
     (1024, 7, (0, 16), (992, 1024), 256),          # heavy ties at the threshold
