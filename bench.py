@@ -47,6 +47,10 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 # interleaved) in a register-only loop over all 256 CUs at 4-16 waves per SIMD: 1.51-1.57 PFLOP/s,
 # against ~1.96 PFLOP/s for the MFMAs alone (the clock does not hold 2.4 GHz under either load).
 MIX_CEILING_TFLOPS = 1570.0
+# The same mix at the engine's two waves per SIMD with random bf16 operands (N(0, 1/4)) in the
+# registers instead of constant ones: the switching of the operand bits holds the chip at its power
+# cap, and the loop runs at 1.28-1.30 PFLOP/s (1.63 on zero operands, 1.70 without the exp2).
+MIX_CEILING_RANDOM_TFLOPS = 1290.0
 WORKLOADS = {"rule-8b+meank-256k": ("rule-8b", "meank-256k"),
              "rule-14b+meank-1m": ("rule-14b", "meank-1m")}
 # kernels each call launches (rocprofv3 short names); a tuple lists alternatives of which the
@@ -580,7 +584,10 @@ def main():
             "tflop_per_call": 2 * work["kvs_meank_score"][1] / 1e12,
             "tflops": round(2 * rows["kvs_meank_score"]["achieved"], 2),
             "mix_ceiling_tflops": MIX_CEILING_TFLOPS,
-            "frac_of_mix_ceiling": round(2 * rows["kvs_meank_score"]["achieved"] / MIX_CEILING_TFLOPS, 4)},
+            "frac_of_mix_ceiling": round(2 * rows["kvs_meank_score"]["achieved"] / MIX_CEILING_TFLOPS, 4),
+            "random_operand_ceiling_tflops": MIX_CEILING_RANDOM_TFLOPS,
+            "frac_of_random_operand_ceiling": round(2 * rows["kvs_meank_score"]["achieved"]
+                                                    / MIX_CEILING_RANDOM_TFLOPS, 4)},
         "calls": rows,
         "next_rows": next_rows,
     }
